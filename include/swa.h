@@ -1,0 +1,184 @@
+/*
+ * swa.h -- C ABI of the MI355X (gfx950) masked causal attention library.
+ *
+ * The operation (Learn: Sparse & Sliding-Window Attention, §3 equation):
+ *
+ *     A = softmax(Q K^T * scale + log M) V,   log M_ij in {0, -inf}
+ *
+ * with the mask M_ij = 1 iff  0 <= j <= i < N  and either
+ *   (window)  i - window + 1 <= j            -- swa_mask(n, window) of
+ *             "Attention Variants Compared"; exactly `window` keys per row
+ *             once i >= window - 1, and window >= N gives full causal;
+ *   (stride)  stride > 0 and j mod stride == 0  -- strided_mask(n, window,
+ *             stride) of the same page, anchored at key 0.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, row-major and contiguous:
+ *        Q, O        [B, Hq,  N, d]     (O: [B, Hq, N, dv] for diff_attn_fwd)
+ *        K           [B, Hkv, N, d]
+ *        V           [B, Hkv, N, dv]    (dv = d except in diff_attn_fwd)
+ *     Query head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *     attention in contiguous groups).
+ *   - The library never allocates, frees or synchronizes.  Every call that
+ *     launches work is asynchronous on `stream` (0 = the null stream).
+ *   - Every argument is checked on the host BEFORE any HIP call; a rejected
+ *     call launches nothing and returns a negative swa_status_t.  Launch
+ *     failures return SWA_ERR_HIP.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - No global mutable state: calls on different streams may overlap as
+ *     long as their output buffers do not.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if !defined(HIP_INCLUDE_HIP_HIP_RUNTIME_API_H)
+typedef struct ihipStream_t *hipStream_t;
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, inconsistent mask */
+    SWA_ERR_UNSUPPORTED = -2, /* valid request this library does not implement      */
+    SWA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small               */
+    SWA_ERR_HIP = -4          /* a HIP launch reported an error                       */
+} swa_status_t;
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
+
+/* Largest sequence length any entry point accepts (keeps every index and
+ * cell count of one (batch, head) inside int32). */
+#define SWA_MAX_N (1 << 22)
+
+/*
+ * Block mask: for each query tile of `bm` rows, the key tiles of `bn` keys
+ * that hold at least one attended cell ("Attention Variants Compared":
+ * create_block_mask builds the per-block keep/skip map once, blocks with no
+ * attended cell are skipped; it is then handed to the attention call).
+ * Stored as a CSR over query tiles; within a query tile the key tiles are
+ * ascending.  The mask depends only on (N, window, stride, bm, bn) and is
+ * shared by every batch and head.
+ *
+ *   row_ptr[num_q_tiles + 1]   list of query tile q is [row_ptr[q], row_ptr[q+1])
+ *   kv_tile[nnz]               key tile index
+ *   kind[nnz]                  0 FULL: every in-range cell attends
+ *                              1 PARTIAL: some cells attend (mask applied per cell)
+ *                              2 STRIDE_ONLY: no cell lies in the window part;
+ *                                only stride keys attend, and they attend
+ *                                from every row of the query tile
+ *   cells[nnz]                 attended cells of the tile (rows, keys < N)
+ *   stride_keys[num_q_tiles]   stride keys inside the STRIDE_ONLY tiles of q;
+ *                              they are keys 0, stride, 2*stride, ... in order
+ *   band_begin[num_q_tiles]    index of the first non-STRIDE_ONLY entry of q
+ *                              (STRIDE_ONLY entries come first)
+ *
+ * The caller allocates the five device arrays with the sizes that
+ * swa_block_mask_query returns and fills the scalar fields.
+ */
+typedef struct {
+    int32_t N, window, stride, bm, bn;
+    int32_t num_q_tiles, nnz;
+    int32_t *row_ptr;
+    int32_t *kv_tile;
+    uint8_t *kind;
+    int32_t *cells;
+    int32_t *stride_keys;
+    int32_t *band_begin;
+} swa_block_mask_t;
+
+/* Tile shape (rows bm, keys bn) the attention kernels walk for this dtype
+ * and head sizes; a block mask built with other sizes is rejected.
+ * Host only, no HIP call.  d, dv in {32, 64, 128}. */
+int swa_tile_config(swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn);
+
+/* Number of query tiles and list entries of the block mask of
+ * (N, window, stride, bm, bn).  Host only, no HIP call.
+ * N in [1, SWA_MAX_N], window >= 1, stride >= 0 (0 = no stride pattern),
+ * bm, bn in {16, 32, 64, 128, 256}. */
+int swa_block_mask_query(int N, int window, int stride, int bm, int bn,
+                         int32_t *num_q_tiles, int32_t *nnz);
+
+/* Fill the device arrays of *mask on `stream` from its scalar fields, which
+ * must equal what swa_block_mask_query reports.  Integer work only; the
+ * result is bit-exact. */
+int swa_block_mask_build(const swa_block_mask_t *mask, hipStream_t stream);
+
+/* Debug export of the dense mask: out[i*N + j] = 1 if query i attends key j,
+ * else 0, for N <= 16384 (device array of N*N bytes). */
+int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream);
+
+/*
+ * Masked attention forward (prefill) -- the §3 equation above over the block
+ * mask, with an fp32 online softmax ("Attention Variants Compared": the
+ * Flash-style tiled softmax) so the N x N score matrix never exists.
+ *   q, k, v, out   layouts above, dtype dt, dv = d
+ *   lse            nullable; fp32 [B, Hq, N] natural-log sum of
+ *                  exp(score * scale) over the attended keys
+ *   d in {32, 64, 128} for SWA_BF16 and SWA_F32
+ *   mask           built for (N, window, stride) and swa_tile_config's tiles
+ * Arithmetic: bf16 inputs, fp32 accumulation, output rounded to bf16
+ * (SWA_BF16) or kept fp32 (SWA_F32).
+ */
+int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                 swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                 float scale, const swa_block_mask_t *mask, hipStream_t stream);
+
+/* Bytes of device workspace swa_attn_decode needs for these sizes. */
+size_t swa_attn_decode_workspace_bytes(int B, int Hq, int d, int window);
+
+/*
+ * One decode step over a rolling KV window (Learn: Sparse & Sliding-Window
+ * Attention, §4 and §6: keep only the last `window` tokens' keys and values
+ * in a fixed-size rolling buffer).
+ *   q          [B, Hq, d]            the current token's queries
+ *   k_ring     [B, Hkv, window, d]   position p of a sequence lives in slot
+ *   v_ring     [B, Hkv, window, d]   p mod window; the caller has already
+ *                                    written the current token
+ *   out        [B, Hq, d]
+ *   seq_len    device int32 [B]: tokens so far, the current one included
+ *              (the attended positions are max(0, L-window) .. L-1), or NULL
+ *              for every sequence at length N.  A sequence with L <= 0
+ *              attends nothing and gets zeros.
+ *   workspace  device scratch of swa_attn_decode_workspace_bytes bytes,
+ *              owned by the caller; contents on entry do not matter.
+ *   stride     must be 0: stride keys older than the window are not in the
+ *              ring (SWA_ERR_UNSUPPORTED otherwise).
+ */
+int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
+                    const int32_t *seq_len, void *workspace, size_t workspace_bytes,
+                    swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                    float scale, hipStream_t stream);
+
+/*
+ * Differential attention ("Attention Variants — Sliding Window, Sparse,
+ * Differential": two attention maps from separate query/key projections,
+ * one subtracted from the other; "Attention Variants Compared": the two maps
+ * read the same value cache):
+ *
+ *   out = (softmax(Q1 K1^T * scale + log M) - lambda * softmax(Q2 K2^T * scale + log M)) V
+ *
+ *   q1, q2     [B, Hq, N, d]      k1, k2  [B, Hkv, N, d]
+ *   v          [B, Hkv, N, dv]    out     [B, Hq, N, dv]
+ *   d in {32, 64, 128}, dv in {32, 64, 128}; no normalisation follows the
+ *   subtraction.
+ */
+int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2,
+                  const void *v, void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N,
+                  int d, int dv, int window, int stride, float scale, float lambda,
+                  const swa_block_mask_t *mask, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *swa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

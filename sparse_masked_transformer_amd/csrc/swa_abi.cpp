@@ -1,0 +1,300 @@
+// C-ABI front end: host-side argument checks, block-mask sizing and kernel
+// dispatch.  Every check runs before the first HIP call, so a rejected call
+// touches no device state (and every error path can be exercised without a
+// GPU).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "swa_internal.h"
+
+using swa::kBM;
+using swa::kBN;
+
+namespace {
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool tile_ok(int t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 256; }
+
+// List length of one query tile: the window tiles form one contiguous range
+// [t_lo, t_hi] covering keys max(0, r0 - window + 1) .. r1 (r0, r1 = first
+// and last row of the tile); every stride key left of that range is attended
+// by every row of the tile, and the tiles holding one are listed first.
+void q_tile_counts(int64_t q, int64_t N, int64_t window, int64_t stride, int64_t bm, int64_t bn,
+                   int64_t *n_band, int64_t *n_stride_only) {
+    int64_t r0 = q * bm;
+    int64_t r1 = (r0 + bm < N ? r0 + bm : N) - 1;
+    int64_t lo = r0 - window + 1 > 0 ? r0 - window + 1 : 0;
+    int64_t t_lo = lo / bn, t_hi = r1 / bn;
+    *n_band = t_hi - t_lo + 1;
+    if (stride <= 0 || t_lo == 0)
+        *n_stride_only = 0;
+    else if (stride <= bn)
+        *n_stride_only = t_lo;  // every tile of bn >= stride keys holds a multiple
+    else
+        *n_stride_only = (t_lo * bn + stride - 1) / stride;  // one multiple per tile
+}
+
+int mask_query(int N, int window, int stride, int bm, int bn, int32_t *nq_out, int32_t *nnz_out) {
+    if (N < 1 || N > SWA_MAX_N || window < 1 || stride < 0 || !tile_ok(bm) || !tile_ok(bn))
+        return SWA_ERR_INVALID_ARG;
+    int64_t nq = (static_cast<int64_t>(N) + bm - 1) / bm, nnz = 0;
+    for (int64_t q = 0; q < nq; ++q) {
+        int64_t nb, ns;
+        q_tile_counts(q, N, window, stride, bm, bn, &nb, &ns);
+        nnz += nb + ns;
+    }
+    if (nnz > INT32_MAX)
+        return SWA_ERR_UNSUPPORTED;
+    if (nq_out)
+        *nq_out = static_cast<int32_t>(nq);
+    if (nnz_out)
+        *nnz_out = static_cast<int32_t>(nnz);
+    return SWA_OK;
+}
+
+// The mask must describe exactly this problem and the kernels' tiling.
+int check_mask(const swa_block_mask_t *m, int N, int window, int stride) {
+    if (m == nullptr)
+        return SWA_ERR_INVALID_ARG;
+    if (m->N != N || m->window != window || m->stride != stride || m->bm != kBM || m->bn != kBN)
+        return SWA_ERR_INVALID_ARG;
+    int32_t nq = 0, nnz = 0;
+    int st = mask_query(N, window, stride, kBM, kBN, &nq, &nnz);
+    if (st != SWA_OK)
+        return st;
+    if (m->num_q_tiles != nq || m->nnz != nnz)
+        return SWA_ERR_INVALID_ARG;
+    if (!m->row_ptr || !m->kv_tile || !m->kind || !m->cells || !m->stride_keys || !m->band_begin)
+        return SWA_ERR_INVALID_ARG;
+    return SWA_OK;
+}
+
+int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || N > SWA_MAX_N || window < 1 ||
+        stride < 0)
+        return SWA_ERR_INVALID_ARG;
+    // every flat row index (b*Hq + h)*N + i fits in int32
+    if (static_cast<int64_t>(B) * Hq * N > INT32_MAX)
+        return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
+
+swa::MaskView view_of(const swa_block_mask_t *m) {
+    return swa::MaskView{m->row_ptr, m->kv_tile, m->kind, m->stride_keys, m->band_begin,
+                         m->num_q_tiles};
+}
+
+}  // namespace
+
+namespace swa {
+int decode_splits(int window) {
+    // Each split covers at least 256 ring slots; at most 16 splits.
+    int s = window / 256;
+    if (s < 1)
+        s = 1;
+    if (s > 16)
+        s = 16;
+    return s;
+}
+}  // namespace swa
+
+extern "C" {
+
+int swa_tile_config(swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn) {
+    if ((dt != SWA_F32 && dt != SWA_BF16) || !head_dim_ok(d) || !head_dim_ok(dv) || !bm || !bn)
+        return SWA_ERR_INVALID_ARG;
+    *bm = kBM;
+    *bn = kBN;
+    return SWA_OK;
+}
+
+int swa_block_mask_query(int N, int window, int stride, int bm, int bn, int32_t *num_q_tiles,
+                         int32_t *nnz) {
+    if (!num_q_tiles || !nnz)
+        return SWA_ERR_INVALID_ARG;
+    return mask_query(N, window, stride, bm, bn, num_q_tiles, nnz);
+}
+
+int swa_block_mask_build(const swa_block_mask_t *mask, hipStream_t stream) {
+    if (!mask)
+        return SWA_ERR_INVALID_ARG;
+    int32_t nq = 0, nnz = 0;
+    int st = mask_query(mask->N, mask->window, mask->stride, mask->bm, mask->bn, &nq, &nnz);
+    if (st != SWA_OK)
+        return st;
+    if (mask->num_q_tiles != nq || mask->nnz != nnz)
+        return SWA_ERR_INVALID_ARG;
+    if (!mask->row_ptr || !mask->kv_tile || !mask->kind || !mask->cells || !mask->stride_keys ||
+        !mask->band_begin)
+        return SWA_ERR_INVALID_ARG;
+    return hip_status(swa::launch_block_mask_build(*mask, stream));
+}
+
+int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream) {
+    if (N < 1 || N > 16384 || window < 1 || stride < 0 || out == nullptr)
+        return SWA_ERR_INVALID_ARG;
+    return hip_status(swa::launch_mask_dense(N, window, stride, out, stream));
+}
+
+int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                 swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                 float scale, const swa_block_mask_t *mask, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return SWA_ERR_INVALID_ARG;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return SWA_ERR_INVALID_ARG;
+    if (dt != SWA_F32 && dt != SWA_BF16)
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return SWA_ERR_INVALID_ARG;
+    int st = check_sizes(B, Hq, Hkv, N, window, stride);
+    if (st != SWA_OK)
+        return st;
+    if (!head_dim_ok(d))
+        return SWA_ERR_UNSUPPORTED;
+    st = check_mask(mask, N, window, stride);
+    if (st != SWA_OK)
+        return st;
+    swa::FwdArgs a{};
+    a.q[0] = q;
+    a.k[0] = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.dv = d;
+    a.window = window;
+    a.stride = stride;
+    a.scale = scale;
+    a.lambda = 0.f;
+    a.nmaps = 1;
+    a.mask = view_of(mask);
+    return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
+}
+
+size_t swa_attn_decode_workspace_bytes(int B, int Hq, int d, int window) {
+    if (B < 1 || Hq < 1 || !head_dim_ok(d) || window < 1)
+        return 0;
+    // per (sequence, query head, split): running max and sum (section padded
+    // to 16 bytes), then d partial sums; all fp32
+    size_t parts = static_cast<size_t>(B) * Hq * swa::decode_splits(window);
+    return (((parts * 2 + 3) / 4) * 4 + parts * d) * sizeof(float);
+}
+
+int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
+                    const int32_t *seq_len, void *workspace, size_t workspace_bytes,
+                    swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                    float scale, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out))
+        return SWA_ERR_INVALID_ARG;
+    if (seq_len != nullptr && (reinterpret_cast<uintptr_t>(seq_len) & 3u) != 0)
+        return SWA_ERR_INVALID_ARG;
+    if (dt != SWA_F32 && dt != SWA_BF16)
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return SWA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || window < 1 || window > SWA_MAX_N ||
+        stride < 0 || (seq_len == nullptr && N < 0))
+        return SWA_ERR_INVALID_ARG;
+    if (dt == SWA_BF16 && Hq / Hkv > 16)
+        return SWA_ERR_UNSUPPORTED;  // the query heads of a group share one 16-column tile
+    if (static_cast<int64_t>(B) * Hkv * window > INT32_MAX)
+        return SWA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d))
+        return SWA_ERR_UNSUPPORTED;
+    if (stride != 0)
+        return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
+    if (workspace == nullptr || !aligned16(workspace) ||
+        workspace_bytes < swa_attn_decode_workspace_bytes(B, Hq, d, window))
+        return SWA_ERR_WORKSPACE;
+    swa::DecodeArgs a{};
+    a.q = q;
+    a.k_ring = k_ring;
+    a.v_ring = v_ring;
+    a.out = out;
+    a.seq_len = seq_len;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.window = window;
+    a.scale = scale;
+    return hip_status(dt == SWA_BF16 ? swa::launch_decode_bf16(a, stream)
+                                     : swa::launch_decode_f32(a, stream));
+}
+
+int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
+                  void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int dv,
+                  int window, int stride, float scale, float lambda,
+                  const swa_block_mask_t *mask, hipStream_t stream) {
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) ||
+        !aligned16(out))
+        return SWA_ERR_INVALID_ARG;
+    if (dt != SWA_F32 && dt != SWA_BF16)
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(lambda))
+        return SWA_ERR_INVALID_ARG;
+    int st = check_sizes(B, Hq, Hkv, N, window, stride);
+    if (st != SWA_OK)
+        return st;
+    if (!head_dim_ok(d) || !head_dim_ok(dv))
+        return SWA_ERR_UNSUPPORTED;
+    // bf16: two K tiles and one V tile of 64 keys, double-buffered, in 64 KiB of LDS
+    if (dt == SWA_BF16 && 2 * d + dv > 256)
+        return SWA_ERR_UNSUPPORTED;
+    st = check_mask(mask, N, window, stride);
+    if (st != SWA_OK)
+        return st;
+    swa::FwdArgs a{};
+    a.q[0] = q1;
+    a.k[0] = k1;
+    a.q[1] = q2;
+    a.k[1] = k2;
+    a.v = v;
+    a.out = out;
+    a.lse = nullptr;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.dv = dv;
+    a.window = window;
+    a.stride = stride;
+    a.scale = scale;
+    a.lambda = lambda;
+    a.nmaps = 2;
+    a.mask = view_of(mask);
+    return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
+}
+
+const char *swa_strerror(int status) {
+    switch (status) {
+    case SWA_OK:
+        return "success";
+    case SWA_ERR_INVALID_ARG:
+        return "invalid argument";
+    case SWA_ERR_UNSUPPORTED:
+        return "unsupported configuration";
+    case SWA_ERR_WORKSPACE:
+        return "decode workspace missing or too small";
+    case SWA_ERR_HIP:
+        return "HIP launch error";
+    default:
+        return "unknown status";
+    }
+}
+
+}  // extern "C"

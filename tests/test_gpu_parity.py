@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Integer outputs (block mask, dense mask) must match bit for bit.  Attention
+outputs must match within max-abs 2e-2 for bf16 inputs (fp32 accumulation,
+bf16 output) and 1e-5 for fp32 inputs -- the tolerances the method's
+target states.  Small cases span several tiles and a ragged tail; the
+full-size workloads are checked on sampled rows, in the launch configuration
+the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def swa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_masked_transformer_amd as m
+    return m
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    return t.cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def max_err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# --------------------------------------------------------------------------
+# block mask and dense mask: bit-exact
+# --------------------------------------------------------------------------
+
+MASK_CASES = [(1, 1, 0), (5, 3, 0), (130, 7, 0), (300, 64, 5), (300, 1000, 0), (511, 129, 64),
+              (1000, 50, 130), (777, 200, 1), (4096, 1024, 0), (8192, 1024, 0),
+              (16384, 256, 128), (2048, 33, 3), (640, 600, 700)]
+
+
+@pytest.mark.parametrize("N,W,s", MASK_CASES)
+def test_block_mask_bit_exact(swa, N, W, s):
+    banner(f"block mask N={N} W={W} s={s}")
+    m = swa.swa_block_mask_build(N, W, s)
+    got = m.host()
+    want = oracle.tile_list(N, W, s, m.bm, m.bn)
+    assert got["nnz"] == want["nnz"] and got["num_q_tiles"] == want["num_q_tiles"]
+    for key in ("row_ptr", "kv_tile", "kind", "cells", "stride_keys", "band_begin"):
+        np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+
+
+@pytest.mark.parametrize("N,W,s", [(1, 1, 0), (64, 5, 0), (257, 17, 7), (1024, 100, 64), (3000, 3000, 0)])
+def test_dense_mask_bit_exact(swa, N, W, s):
+    banner(f"dense mask N={N} W={W} s={s}")
+    got = swa.swa_mask_dense(N, W, s).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.mask_dense(N, W, s))
+
+
+# --------------------------------------------------------------------------
+# prefill
+# --------------------------------------------------------------------------
+
+def run_prefill(swa, cfg, q, k, v, with_lse=False):
+    dt = cfg["dtype"]
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"],
+                                    dtype=torch.bfloat16 if dt == "bf16" else torch.float32, d=cfg["d"])
+    qd, kd, vd = dev(q, dt), dev(k, dt), dev(v, dt)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda") if with_lse else None
+    out = swa.swa_attn_fwd(qd, kd, vd, cfg["window"], cfg["stride"], cfg["scale"], mask, lse=lse)
+    torch.cuda.synchronize()
+    return (host(out), lse.cpu().numpy()) if with_lse else host(out)
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, N, d, W, stride
+    (1, 2, 2, 64, 64, 16, 0),
+    (1, 4, 2, 300, 64, 17, 0),
+    (2, 4, 1, 333, 128, 100, 0),
+    (1, 8, 2, 517, 128, 64, 0),
+    (1, 2, 2, 300, 128, 300, 0),
+    (1, 2, 2, 300, 64, 1000, 0),
+    (1, 2, 1, 200, 32, 1, 0),
+    (1, 2, 2, 450, 64, 40, 7),
+    (1, 2, 2, 700, 64, 64, 128),
+    (2, 2, 2, 390, 128, 33, 100),
+    (1, 4, 4, 300, 32, 20, 1),
+    (1, 2, 2, 1000, 64, 128, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,W,s", PREFILL_CASES)
+def test_prefill_parity_small(swa, dtype, B, Hq, Hkv, N, d, W, s):
+    banner(f"prefill {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} W={W} s={s}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dv=d, window=W, stride=s,
+               scale=1.0 / math.sqrt(d), seed=N + d + W + s)
+    q, k, v = synth.prefill_inputs(cfg)
+    got, lse = run_prefill(swa, cfg, q, k, v, with_lse=True)
+    want, want_lse = oracle.attn_full(q, k, v, W, s, cfg["scale"], with_lse=True)
+    assert max_err(got, want) <= TOL[dtype]
+    assert max_err(lse, want_lse) <= (1e-3 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_peaky_scores(swa, dtype):
+    # query scaled by 8: near one-hot softmax rows, large score range
+    banner(f"prefill peaky {dtype}")
+    cfg = dict(dtype=dtype, B=1, Hq=4, Hkv=2, N=400, d=64, dv=64, window=90, stride=33,
+               scale=1.0 / 8, seed=77)
+    q, k, v = synth.prefill_inputs(cfg, q_scale=8.0)
+    got = run_prefill(swa, cfg, q, k, v)
+    want = oracle.attn_full(q, k, v, 90, 33, cfg["scale"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+def test_tiny_fp32_workload_full(swa):
+    cfg = synth.workload("tiny_swa_f32")
+    banner("workload tiny_swa_f32 (all rows)")
+    q, k, v = synth.prefill_inputs(cfg)
+    got = run_prefill(swa, cfg, q, k, v)
+    want = oracle.attn_full(q, k, v, cfg["window"], cfg["stride"], cfg["scale"])
+    assert max_err(got, want) <= TOL["f32"]
+
+
+def boundary_rows(B, H, N, step, extra):
+    must = []
+    for b in range(B):
+        for h in range(H):
+            for i in (0, 1, 63, 64, 127, 128, N // 2, N - 2, N - 1):
+                must.append((b * H + h) * N + i)
+    return synth.sample_rows(B * H * N, extra, seed=step, must=must)
+
+
+@pytest.mark.parametrize("name", ["swa_prefill_bf16", "local_strided_bf16"])
+def test_prefill_workload_sampled(swa, name):
+    cfg = synth.workload(name)
+    banner(f"workload {name} (sampled rows)")
+    q, k, v = synth.prefill_inputs(cfg)
+    got = run_prefill(swa, cfg, q, k, v).reshape(-1, cfg["dv"])
+    rows = boundary_rows(cfg["B"], cfg["Hq"], cfg["N"], 3, 768)
+    want = oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], rows)
+    assert max_err(got[rows], want) <= TOL["bf16"]
+    assert np.all(np.isfinite(got))
+
+
+def test_prefill_deterministic(swa):
+    cfg = dict(dtype="bf16", B=1, Hq=8, Hkv=2, N=1500, d=128, dv=128, window=300, stride=0,
+               scale=1.0 / math.sqrt(128), seed=5)
+    banner("prefill determinism")
+    q, k, v = synth.prefill_inputs(cfg)
+    a = run_prefill(swa, cfg, q, k, v)
+    b = run_prefill(swa, cfg, q, k, v)
+    np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# differential attention
+# --------------------------------------------------------------------------
+
+def run_diff(swa, cfg, q1, k1, q2, k2, v):
+    dt = cfg["dtype"]
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"],
+                                    dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                                    d=cfg["d"], dv=cfg["dv"])
+    out = swa.diff_attn_fwd(dev(q1, dt), dev(k1, dt), dev(q2, dt), dev(k2, dt), dev(v, dt),
+                            cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], mask)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+DIFF_CASES = [(1, 2, 2, 300, 64, 128, 70, 0), (1, 4, 2, 257, 64, 64, 300, 0),
+              (2, 2, 2, 200, 32, 128, 50, 9), (1, 2, 1, 130, 32, 32, 1, 0)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dv,W,s", DIFF_CASES)
+def test_diff_parity_small(swa, dtype, B, Hq, Hkv, N, d, dv, W, s):
+    banner(f"diff {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} dv={dv} W={W} s={s}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dv=dv, window=W, stride=s,
+               scale=1.0 / 8, lam=0.5, seed=N + W)
+    ins = synth.diff_inputs(cfg)
+    got = run_diff(swa, cfg, *ins)
+    want = oracle.diff_full(*ins, W, s, cfg["scale"], cfg["lam"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+def test_diff_workload_sampled(swa):
+    cfg = synth.workload("diff_bf16")
+    banner("workload diff_bf16 (sampled rows)")
+    ins = synth.diff_inputs(cfg)
+    got = run_diff(swa, cfg, *ins).reshape(-1, cfg["dv"])
+    rows = boundary_rows(cfg["B"], cfg["Hq"], cfg["N"], 4, 768)
+    want = oracle.diff_rows(*ins, cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], rows)
+    assert max_err(got[rows], want) <= TOL["bf16"]
+
+
+# --------------------------------------------------------------------------
+# decode over a rolling window
+# --------------------------------------------------------------------------
+
+def run_decode(swa, cfg, ins, pass_len=True):
+    dt = cfg["dtype"]
+    sl = torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda() if pass_len else None
+    out = swa.swa_attn_decode(dev(ins["q"], dt), dev(ins["k_ring"], dt), dev(ins["v_ring"], dt), sl,
+                              cfg["scale"], N=int(ins["seq_len"][0]))
+    torch.cuda.synchronize()
+    return host(out)
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, W, d, lengths
+    (3, 4, 1, 64, 64, [1, 30, 64]),
+    (2, 8, 2, 300, 128, [299, 1000]),
+    (4, 4, 4, 1000, 32, [0, 5, 999, 1001]),
+    (2, 16, 1, 512, 128, [513, 4096]),
+    (1, 2, 2, 33, 64, [100]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,W,d,lens", DECODE_CASES)
+def test_decode_parity(swa, dtype, B, Hq, Hkv, W, d, lens):
+    banner(f"decode {dtype} B={B} Hq={Hq} Hkv={Hkv} W={W} d={d} lens={lens}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, window=W, d=d, dv=d, position=0, n_sink=0,
+               scale=1.0 / math.sqrt(d), seed=W + d)
+    ins = synth.decode_inputs(cfg, seq_len=lens)
+    got = run_decode(swa, cfg, ins)
+    want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+def test_decode_default_length(swa):
+    cfg = dict(dtype="bf16", B=2, Hq=4, Hkv=1, window=128, d=64, dv=64, position=500, n_sink=0,
+               scale=0.125, seed=3)
+    banner("decode seq_len=NULL")
+    ins = synth.decode_inputs(cfg)
+    got = run_decode(swa, cfg, ins, pass_len=False)
+    want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"])
+    assert max_err(got, want) <= TOL["bf16"]
+
+
+def test_decode_workload(swa):
+    cfg = synth.workload("window_decode_bf16")
+    banner("workload window_decode_bf16 (sequences 0, 17, 63)")
+    ins = synth.decode_inputs(cfg)
+    got = run_decode(swa, cfg, ins)
+    pick = [0, 17, 63]
+    want = oracle.decode(ins["q"][pick], ins["k_ring"][pick], ins["v_ring"][pick],
+                         ins["seq_len"][pick], cfg["scale"])
+    assert max_err(got[pick], want) <= TOL["bf16"]
+    assert np.all(np.isfinite(got))
