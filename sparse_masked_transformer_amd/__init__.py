@@ -145,12 +145,18 @@ class BlockMask:
 
 
 def swa_block_mask_build(N, window, stride=0, bm=None, bn=None, device="cuda",
-                         dtype=torch.bfloat16, d=128, dv=None):
-    """Allocate and build the block mask on the GPU (asynchronous on the
-    current stream).  bm/bn default to the kernels' tile shape."""
+                         dtype=torch.bfloat16, d=128, dv=None, into=None):
+    """Build the block mask on the GPU (asynchronous on the current stream),
+    into a new BlockMask or into `into` (same sizes, arrays reused).  bm/bn
+    default to the kernels' tile shape."""
     if bm is None or bn is None:
         bm, bn = swa_tile_config(dtype, d, dv)
-    m = BlockMask(N, window, stride, bm, bn, torch.device(device))
+    if into is not None:
+        if (into.N, into.window, into.stride, into.bm, into.bn) != (N, window, stride, bm, bn):
+            raise ValueError("`into` was allocated for another mask")
+        m = into
+    else:
+        m = BlockMask(N, window, stride, bm, bn, torch.device(device))
     _check(_lib.swa_block_mask_build(ctypes.byref(m.c), _stream(m.row_ptr)), "swa_block_mask_build")
     return m
 

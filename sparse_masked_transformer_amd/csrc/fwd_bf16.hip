@@ -11,8 +11,9 @@
 //
 // Workgroup: 256 threads = 4 waves; wave w owns query rows q0 .. q0+31 of the
 // 128-row query tile.  Per 64-key tile:
-//   * K (and V) tiles are staged HBM -> VGPR -> LDS, double-buffered, with a
-//     16-byte-chunk XOR swizzle on every row.
+//   * K (and V) tiles are staged HBM -> VGPR -> LDS, double-buffered; the
+//     next tile's loads are in flight while the current tile is computed.
+//     LDS rows are padded by 32 bytes (bank spread).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand,
 //     Q^T held in registers as the B operand).  In the 32x32 accumulator
 //     layout lane l holds query column l%32 and keys (r%4) + 8(r/4) + 4(l/32)
@@ -40,6 +41,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -47,25 +49,21 @@ constexpr float kSlack = 8.0f;       // log2 units the running maximum may lag
 constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-// Byte offset of 16-byte chunk c of row r in a tile of rows with `cols`
-// bf16 elements.
-template <int COLS>
-__device__ __forceinline__ int chunk_off(int r, int c) {
-    constexpr int cpr = COLS / 8;
-    constexpr int cmask = (cpr < 8 ? cpr : 8) - 1;
-    return r * (COLS * 2) + ((c ^ (swz(r) & cmask)) << 4);
-}
-
 template <int D, int DV, int NMAPS>
 struct Cfg {
-    static constexpr int kTile = 64 * D * 2;                  // one K tile, bytes
-    static constexpr int vTile = 64 * DV * 2;                 // one V tile, bytes
-    static constexpr int buf = NMAPS * kTile + vTile;         // one stage
-    static constexpr int chunks = buf / 16;                   // 16-byte chunks per stage
-    static constexpr int per_thread = chunks / kThreads;
-    static_assert(chunks % kThreads == 0, "stage must split evenly over the workgroup");
+    // Rows are padded by 32 bytes: consecutive rows start 8 banks apart, so
+    // the 16-byte reads of 8 rows and the transposed 8-byte reads of 4 rows
+    // fall in distinct banks, and every LDS address is a per-lane base plus
+    // a compile-time offset.
+    static constexpr int kRow = 2 * D + 32;                   // K row stride, bytes
+    static constexpr int vRow = 2 * DV + 32;                  // V row stride, bytes
+    static constexpr int kTile = 64 * kRow;                   // one K tile
+    static constexpr int vTile = 64 * vRow;                   // one V tile
+    static constexpr int stage = NMAPS * kTile + vTile;       // one buffer
+    static constexpr int kPer = D / 32;                       // K chunks per thread
+    static constexpr int vPer = DV / 32;                      // V chunks per thread
+    static constexpr int kRowStep = kThreads / (D / 8);       // rows between a thread's chunks
+    static constexpr int vRowStep = kThreads / (DV / 8);
 };
 
 struct Params {
@@ -80,18 +78,10 @@ struct Params {
     float lambda;
 };
 
-// Key index of row r of item `it` of a query tile's walk: items below
-// n_pre are stride-prefix chunks, the rest window tiles.
-struct Walk {
-    int n_pre;     // number of 64-key stride-prefix chunks
-    int sk;        // stride keys in the prefix
-    int band0;     // list index of the first window tile
-};
-
 template <int D, int DV, int NMAPS>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
+__device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     using C = Cfg<D, DV, NMAPS>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::buf];
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::stage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5;          // which half of the wave
@@ -102,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
     // ---- workgroup -> (b, kv head, query tile, head in group) -------------
     // Consecutive workgroup ids go to the 8 XCDs in turn; remap so each XCD
     // receives a contiguous run of logical ids (the same key/value head, so
-    // its L2 serves the 4 query heads and neighbouring query tiles).
+    // its L2 serves the query heads of the group and neighbouring tiles).
     int total = gridDim.x, pid = blockIdx.x, lid = pid;
     if ((total & 7) == 0)
         lid = (pid & 7) * (total >> 3) + (pid >> 3);
@@ -126,67 +116,62 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
         for (int ks = 0; ks < D / 16; ++ks)
             qf[m][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
 
-    // ---- the walk -----------------------------------------------------------
-    Walk w;
-    w.sk = p.mask.stride_keys[qt];
-    w.n_pre = (w.sk + 63) >> 6;
-    w.band0 = p.mask.band_begin[qt];
-    const int n_items = w.n_pre + (p.mask.row_ptr[qt + 1] - w.band0);
-
+    // ---- the walk: stride-prefix chunks, then window tiles ----------------
+    const int sk = p.mask.stride_keys[qt];
+    const int n_pre = (sk + 63) >> 6;
+    const int band0 = p.mask.band_begin[qt];
+    const int n_items = n_pre + (p.mask.row_ptr[qt + 1] - band0);
     const int64_t kv_head = (int64_t)(b * p.Hkv + g) * p.N;
-    auto item_key0 = [&](int it) -> int {  // first key of a window tile
-        return p.mask.kv_tile[w.band0 + (it - w.n_pre)] * 64;
+
+    // first key of item it (window tiles only)
+    auto item_key0 = [&](int it) -> int {
+        return it >= n_pre ? p.mask.kv_tile[band0 + (it - n_pre)] * 64 : 0;
     };
-    // key index (global row) of tile row r of item it, clamped into [0, N)
+    // global row of tile row r of item it, always inside [0, N)
     auto key_of = [&](int it, int key0, int r) -> int {
-        if (it < w.n_pre) {
-            int kn = it * 64 + r;
-            return kn < w.sk ? kn * p.stride : 0;
-        }
-        int j = key0 + r;
-        return j < p.N ? j : p.N - 1;
+        int kn = it * 64 + r;
+        int pre_key = kn < sk ? kn * p.stride : 0;
+        int win_key = key0 + r < p.N ? key0 + r : p.N - 1;
+        return it < n_pre ? pre_key : win_key;
     };
 
-    u32x4 stage[C::per_thread];
+    // per-thread staging: thread t owns chunk column t % (D/8) of rows
+    // t / (D/8) + u * kRowStep (same for V with DV)
+    const int kc = tid % (D / 8), kr0 = tid / (D / 8);
+    const int vc = tid % (DV / 8), vr0 = tid / (DV / 8);
+    u32x4 kst[NMAPS][C::kPer], vst[C::vPer];
     auto load_stage = [&](int it) {
-        int key0 = it >= w.n_pre ? item_key0(it) : 0;
+        const int key0 = item_key0(it);
 #pragma unroll
-        for (int u = 0; u < C::per_thread; ++u) {
-            int x = tid + u * kThreads;
-            const __bf16 *src;
-            int r, c;
-            if (x < NMAPS * (C::kTile / 16)) {
-                int m = x / (C::kTile / 16);
-                int y = x - m * (C::kTile / 16);
-                r = y / (D / 8);
-                c = y % (D / 8);
-                src = p.k[m] + (kv_head + key_of(it, key0, r)) * D + c * 8;
-            } else {
-                int y = x - NMAPS * (C::kTile / 16);
-                r = y / (DV / 8);
-                c = y % (DV / 8);
-                src = p.v + (kv_head + key_of(it, key0, r)) * DV + c * 8;
-            }
-            stage[u] = *reinterpret_cast<const u32x4 *>(src);
+        for (int u = 0; u < C::kPer; ++u) {
+            const int64_t row = kv_head + key_of(it, key0, kr0 + u * C::kRowStep);
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                kst[m][u] = *reinterpret_cast<const u32x4 *>(p.k[m] + row * D + kc * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < C::vPer; ++u) {
+            const int64_t row = kv_head + key_of(it, key0, vr0 + u * C::vRowStep);
+            vst[u] = *reinterpret_cast<const u32x4 *>(p.v + row * DV + vc * 8);
         }
     };
     auto store_stage = [&](int buf) {
-        char *base = smem + buf * C::buf;
+        char *kbase = smem + buf * C::stage + kr0 * C::kRow + kc * 16;
+        char *vbase = smem + buf * C::stage + NMAPS * C::kTile + vr0 * C::vRow + vc * 16;
 #pragma unroll
-        for (int u = 0; u < C::per_thread; ++u) {
-            int x = tid + u * kThreads;
-            int off;
-            if (x < NMAPS * (C::kTile / 16)) {
-                int m = x / (C::kTile / 16);
-                int y = x - m * (C::kTile / 16);
-                off = m * C::kTile + chunk_off<D>(y / (D / 8), y % (D / 8));
-            } else {
-                int y = x - NMAPS * (C::kTile / 16);
-                off = NMAPS * C::kTile + chunk_off<DV>(y / (DV / 8), y % (DV / 8));
-            }
-            *reinterpret_cast<u32x4 *>(base + off) = stage[u];
-        }
+        for (int u = 0; u < C::kPer; ++u)
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                *reinterpret_cast<u32x4 *>(kbase + m * C::kTile + u * C::kRowStep * C::kRow) = kst[m][u];
+#pragma unroll
+        for (int u = 0; u < C::vPer; ++u)
+            *reinterpret_cast<u32x4 *>(vbase + u * C::vRowStep * C::vRow) = vst[u];
     };
+
+    // per-lane LDS read bases (everything else is a compile-time offset)
+    const int grp = lane >> 4, sl = lane & 15;
+    const int k_lane = col * C::kRow + hl * 16;
+    const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * C::vRow + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
     // ---- running state ------------------------------------------------------
     f32x16 o[NMAPS][DV / 32];
@@ -209,16 +194,16 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
     const int last_row = q0 + 31;
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
-        if (it + 1 < n_items)
-            load_stage(it + 1);
+        // prefetch the next item (the last item re-reads itself; harmless)
+        load_stage(it + 1 < n_items ? it + 1 : it);
 
         // ---- classify this tile for this wave's rows -----------------------
-        const bool pre = it < w.n_pre;
-        const int key0 = pre ? 0 : item_key0(it);
+        const bool pre = it < n_pre;
+        const int key0 = item_key0(it);
         bool empty = false, full;
         uint64_t smask = 0;  // stride keys of a window tile, bit per tile row
         if (pre) {
-            full = (it + 1) * 64 <= w.sk;
+            full = (it + 1) * 64 <= sk;
         } else {
             if (p.stride > 0) {
                 int f = ((key0 + p.stride - 1) / p.stride) * p.stride;
@@ -230,25 +215,29 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
         }
 
         if (!empty) {
-            const char *kb_base = smem + buf * C::buf;
-            const char *vb_base = kb_base + NMAPS * C::kTile;
+            const char *kb_base = smem + buf * C::stage + k_lane;
+            const char *vb_base = smem + buf * C::stage + NMAPS * C::kTile + v_lane;
 
             // ---- S^T = K Q^T -------------------------------------------------
             f32x16 s[NMAPS][2];
 #pragma unroll
-            for (int m = 0; m < NMAPS; ++m)
+            for (int m = 0; m < NMAPS; ++m) {
+                bf16x8 ka[2][D / 16];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        ka[kb][ks] = *reinterpret_cast<const bf16x8 *>(
+                            kb_base + m * C::kTile + kb * 32 * C::kRow + ks * 32);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     f32x16 acc = f32x16{};
-                    const char *kt = kb_base + m * C::kTile;
 #pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                            kt + chunk_off<D>(kb * 32 + col, ks * 2 + hl));
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m][ks], acc, 0, 0, 0);
-                    }
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qf[m][ks], acc, 0, 0, 0);
                     s[m][kb] = acc;
                 }
+            }
 
             // ---- per-cell mask on partial tiles -------------------------------
             if (!full) {
@@ -256,13 +245,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        int kk = kb * 32 + (r & 3) + 8 * (r >> 2) + 4 * hl;
+                        const int kk = kb * 32 + (r & 3) + 8 * (r >> 2) + 4 * hl;
                         bool ok;
                         if (pre) {
-                            ok = it * 64 + kk < w.sk;
+                            ok = it * 64 + kk < sk;
                         } else {
-                            int j = key0 + kk;
-                            int dist = my_row - j;
+                            const int j = key0 + kk;
+                            const int dist = my_row - j;
                             ok = j < p.N && dist >= 0 &&
                                  (dist < p.window || ((smask >> kk) & 1ull));
                         }
@@ -285,10 +274,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                     for (int r = 0; r < 16; ++r)
                         mx = fmaxf(mx, s[m][kb][r]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                float mxs = mx * p.c;
+                const float mxs = mx * p.c;
                 if (__builtin_amdgcn_ballot_w64(mxs > m_run[m] + kSlack) != 0) {
-                    float m_new = fmaxf(m_run[m], mxs);
-                    float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
+                    const float m_new = fmaxf(m_run[m], mxs);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
                     l_run[m] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db)
@@ -304,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                         bf16x8 v8;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kb][hf * 8 + e], p.c, nm));
+                            const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kb][hf * 8 + e], p.c, nm));
                             lsum += pv;
                             v8[e] = (__bf16)pv;
                         }
@@ -314,7 +303,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
             }
 
             // ---- O^T += V^T P^T --------------------------------------------
-            const int grp = lane >> 4, sl = lane & 15;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -322,17 +310,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                     const int kbase = kb * 32 + hf * 16;
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db) {
-                        const int d0 = db * 32 + 16 * (grp & 1) + 4 * (sl & 3);
-                        const int r0 = kbase + 4 * (grp >> 1) + (sl >> 2);
-                        const int r1 = r0 + 8;
-                        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                        i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(vb_base + chunk_off<DV>(r0, d0 >> 3) + (d0 & 7) * 2));
-                        i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(vb_base + chunk_off<DV>(r1, d0 >> 3) + (d0 & 7) * 2));
-                        bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
-                        bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
-                        bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        const char *a = vb_base + kbase * C::vRow + db * 64;
+                        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a);
+                        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 8 * C::vRow));
+                        const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
+                        const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
+                        const bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
                         for (int m = 0; m < NMAPS; ++m)
                             o[m][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -341,8 +324,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                 }
         }
 
-        if (it + 1 < n_items)
-            store_stage(buf ^ 1);
+        store_stage(buf ^ 1);
         __syncthreads();
     }
 
@@ -350,12 +332,11 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
     float inv[NMAPS];
 #pragma unroll
     for (int m = 0; m < NMAPS; ++m) {
-        float lt = l_run[m] + __shfl_xor(l_run[m], 32);
+        const float lt = l_run[m] + __shfl_xor(l_run[m], 32);
         inv[m] = lt > 0.f ? 1.f / lt : 0.f;
         if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row < p.N)
             p.lse[(int64_t)(b * p.Hq + h) * p.N + my_row] =
                 lt > 0.f ? (m_run[m] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
-        l_run[m] = lt;
     }
     if (my_row < p.N) {
         __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + my_row) * DV;
@@ -374,6 +355,20 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
                 *reinterpret_cast<bf16x4 *>(dst + db * 32 + 8 * r4 + 4 * hl) = v4;
             }
     }
+}
+
+// Single-map kernels fit in 256 registers per lane, which lets two waves
+// share each SIMD (one wave's softmax overlaps the other's matrix work);
+// two-map kernels need more state and run one wave per SIMD.
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(Params p) {
+    fwd_bf16_body<D, DV, 1>(p);
+}
+
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void diff_bf16_kernel(Params p) {
+    fwd_bf16_body<D, DV, 2>(p);
 }
 
 template <int D, int DV, int NMAPS>
@@ -396,7 +391,10 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     p.lambda = a.lambda;
     unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, NMAPS>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if constexpr (NMAPS == 1)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, DV>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((diff_bf16_kernel<D, DV>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

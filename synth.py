@@ -42,9 +42,10 @@ WORKLOADS = {
 def round_bf16(x):
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # finite inputs only: the largest finite pattern plus 0x8000 stays below 2**32
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(x.shape)
 
 
 def _draw(rng, shape, dtype, scale=1.0):
