@@ -19,6 +19,8 @@ and times the fp64 CPU oracle on a bounded sample of prefill rows
 (cpu_baseline), which also yields a parity check of those rows.
 
 Kernel times come from HIP events recorded on the stream the kernels run on.
+Each workload is warmed up for at least 0.5 s (and at least --warmup calls)
+before its timed calls, so the GPU clock has settled.
 """
 import argparse
 import concurrent.futures
@@ -58,12 +60,19 @@ def cells_of(cfg):
     return c
 
 
-def timed(fn, steps, warmup, torch):
-    """Run fn warmup+steps times; return (ms per call by wall clock, ms per
-    call by HIP events on the current stream)."""
+def timed(fn, steps, warmup, torch, min_warm_s=0.5):
+    """Run fn `warmup` times and, if that took less than min_warm_s seconds,
+    keep warming until it has (clocks settle under sustained load), then time
+    `steps` calls; return (ms per call by wall clock, ms per call by HIP events
+    on the current stream)."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            fn(0)
+        torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()

@@ -31,6 +31,8 @@
 // Local+strided problems first visit a dense prefix of stride keys
 // (0, s, 2s, ... below the query tile's first window tile), which every row
 // of the tile attends, gathered 64 at a time, then the window tiles.
+#include <type_traits>
+
 #include "swa_internal.h"
 
 namespace swa {
@@ -48,15 +50,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;       // log2 units the running maximum may lag
 constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = 256;
+// dword 3 of a raw (untyped) buffer descriptor on gfx950
+constexpr int kBufferDword3 = 0x00020000;
 
 template <int D, int DV, int NMAPS>
 struct Cfg {
-    // Rows are padded by 32 bytes: consecutive rows start 8 banks apart, so
-    // the 16-byte reads of 8 rows and the transposed 8-byte reads of 4 rows
-    // fall in distinct banks, and every LDS address is a per-lane base plus
-    // a compile-time offset.
-    static constexpr int kRow = 2 * D + 32;                   // K row stride, bytes
-    static constexpr int vRow = 2 * DV + 32;                  // V row stride, bytes
+    // Row padding (bank spread, with every LDS address a per-lane base plus
+    // a compile-time offset):
+    //   K rows +16 bytes: consecutive rows start 4 banks apart, so the
+    //     16-byte reads of 16 rows at one column cover all 64 banks once;
+    //   V rows +64 bytes: consecutive rows start 16 banks apart, so the
+    //     transposed 8-byte reads of 4 rows x 64 bytes do not overlap.
+    static constexpr int kRow = 2 * D + 16;                   // K row stride, bytes
+    static constexpr int vRow = 2 * DV + 64;                  // V row stride, bytes
     static constexpr int kTile = 64 * kRow;                   // one K tile
     static constexpr int vTile = 64 * vRow;                   // one V tile
     static constexpr int stage = NMAPS * kTile + vTile;       // one buffer
@@ -127,32 +133,57 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     auto item_key0 = [&](int it) -> int {
         return it >= n_pre ? p.mask.kv_tile[band0 + (it - n_pre)] * 64 : 0;
     };
-    // global row of tile row r of item it, always inside [0, N)
-    auto key_of = [&](int it, int key0, int r) -> int {
-        int kn = it * 64 + r;
-        int pre_key = kn < sk ? kn * p.stride : 0;
-        int win_key = key0 + r < p.N ? key0 + r : p.N - 1;
-        return it < n_pre ? pre_key : win_key;
-    };
 
     // per-thread staging: thread t owns chunk column t % (D/8) of rows
     // t / (D/8) + u * kRowStep (same for V with DV)
     const int kc = tid % (D / 8), kr0 = tid / (D / 8);
     const int vc = tid % (DV / 8), vr0 = tid / (DV / 8);
     u32x4 kst[NMAPS][C::kPer], vst[C::vPer];
-    auto load_stage = [&](int it) {
-        const int key0 = item_key0(it);
+    // Buffer descriptors over this (b, kv head)'s K and V rows: N rows of D
+    // (DV) bf16.  Reads at or past row N return zeros (no clamping needed);
+    // the per-tile offset lives in a scalar register.
+    __amdgpu_buffer_rsrc_t krs[NMAPS];
 #pragma unroll
-        for (int u = 0; u < C::kPer; ++u) {
-            const int64_t row = kv_head + key_of(it, key0, kr0 + u * C::kRowStep);
+    for (int m = 0; m < NMAPS; ++m)
+        krs[m] = __builtin_amdgcn_make_buffer_rsrc((void *)(p.k[m] + kv_head * D), 0,
+                                                   p.N * D * 2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + kv_head * DV), 0, p.N * DV * 2, kBufferDword3);
+    const int k_goff = (kr0 * D + kc * 8) * 2;
+    const int v_goff = (vr0 * DV + vc * 8) * 2;
+    auto load_stage = [&](int it) {
+        if (it >= n_pre) {
+            // window tile: rows key0 .. key0+63
+            const int key0 = item_key0(it);
 #pragma unroll
             for (int m = 0; m < NMAPS; ++m)
-                kst[m][u] = *reinterpret_cast<const u32x4 *>(p.k[m] + row * D + kc * 8);
-        }
 #pragma unroll
-        for (int u = 0; u < C::vPer; ++u) {
-            const int64_t row = kv_head + key_of(it, key0, vr0 + u * C::vRowStep);
-            vst[u] = *reinterpret_cast<const u32x4 *>(p.v + row * DV + vc * 8);
+                for (int u = 0; u < C::kPer; ++u)
+                    kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        krs[m], k_goff, (key0 + u * C::kRowStep) * D * 2, 0));
+#pragma unroll
+            for (int u = 0; u < C::vPer; ++u)
+                vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    vrs, v_goff, (key0 + u * C::vRowStep) * DV * 2, 0));
+        } else {
+            // stride-prefix chunk: rows kn * stride for kn < sk (others read
+            // past the end, i.e. zeros)
+#pragma unroll
+            for (int u = 0; u < C::kPer; ++u) {
+                const int kn = it * 64 + kr0 + u * C::kRowStep;
+                const int row = kn < sk ? kn * p.stride : p.N;
+#pragma unroll
+                for (int m = 0; m < NMAPS; ++m)
+                    kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        krs[m], (row * D + kc * 8) * 2, 0, 0));
+            }
+#pragma unroll
+            for (int u = 0; u < C::vPer; ++u) {
+                const int kn = it * 64 + vr0 + u * C::vRowStep;
+                const int row = kn < sk ? kn * p.stride : p.N;
+                vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    vrs, (row * DV + vc * 8) * 2, 0, 0));
+            }
         }
     };
     auto store_stage = [&](int buf) {
@@ -218,93 +249,131 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             const char *kb_base = smem + buf * C::stage + k_lane;
             const char *vb_base = smem + buf * C::stage + NMAPS * C::kTile + v_lane;
 
-            // ---- S^T = K Q^T -------------------------------------------------
-            f32x16 s[NMAPS][2];
+            // Two 32-key halves, software-pipelined so MFMA and VALU work of
+            // one wave overlap: QK^T(half 1) is in flight during the softmax
+            // of half 0, and PV(half 0) during the softmax of half 1.
+            f32x16 sh[2][NMAPS];
+            auto qk_half = [&](int kb) {
 #pragma unroll
-            for (int m = 0; m < NMAPS; ++m) {
-                bf16x8 ka[2][D / 16];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int m = 0; m < NMAPS; ++m) {
+                    bf16x8 ka[D / 16];
 #pragma unroll
                     for (int ks = 0; ks < D / 16; ++ks)
-                        ka[kb][ks] = *reinterpret_cast<const bf16x8 *>(
+                        ka[ks] = *reinterpret_cast<const bf16x8 *>(
                             kb_base + m * C::kTile + kb * 32 * C::kRow + ks * 32);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
                     f32x16 acc = f32x16{};
 #pragma unroll
                     for (int ks = 0; ks < D / 16; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qf[m][ks], acc, 0, 0, 0);
-                    s[m][kb] = acc;
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[m][ks], acc, 0, 0, 0);
+                    sh[kb][m] = acc;
                 }
-            }
-
-            // ---- per-cell mask on partial tiles -------------------------------
-            if (!full) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+            };
+            // per-cell mask of half kb on partial tiles (branch-free selects);
+            // lane key kk = kb*32 + kc + 4*hl with kc a compile-time constant
+            auto mask_half = [&](int kb) {
+                const float ninf = -__builtin_inff();
+                if (pre) {
+                    const int lim = sk - it * 64 - kb * 32 - 4 * hl;  // attended iff kc < lim
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int kk = kb * 32 + (r & 3) + 8 * (r >> 2) + 4 * hl;
-                        bool ok;
-                        if (pre) {
-                            ok = it * 64 + kk < sk;
-                        } else {
-                            const int j = key0 + kk;
-                            const int dist = my_row - j;
-                            ok = j < p.N && dist >= 0 &&
-                                 (dist < p.window || ((smask >> kk) & 1ull));
-                        }
-                        if (!ok) {
+                        const int kcst = (r & 3) + 8 * (r >> 2);
+#pragma unroll
+                        for (int m = 0; m < NMAPS; ++m)
+                            sh[kb][m][r] = kcst < lim ? sh[kb][m][r] : ninf;
+                    }
+                } else {
+                    // dist = i - j = base - kc; window part iff 0 <= dist < W
+                    const int base = my_row - key0 - kb * 32 - 4 * hl;
+                    const unsigned W = (unsigned)p.window;
+                    if (smask == 0) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kcst = (r & 3) + 8 * (r >> 2);
+                            const bool ok = (unsigned)(base - kcst) < W;
 #pragma unroll
                             for (int m = 0; m < NMAPS; ++m)
-                                s[m][kb][r] = -__builtin_inff();
+                                sh[kb][m][r] = ok ? sh[kb][m][r] : ninf;
+                        }
+                    } else {
+                        const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kcst = (r & 3) + 8 * (r >> 2);
+                            const int dist = base - kcst;
+                            // bitwise, not short-circuit: no per-cell branch
+                            const bool ok = ((unsigned)dist < W) |
+                                            ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
+#pragma unroll
+                            for (int m = 0; m < NMAPS; ++m)
+                                sh[kb][m][r] = ok ? sh[kb][m][r] : ninf;
                         }
                     }
-            }
-
-            // ---- online softmax ------------------------------------------------
-            bf16x8 pf[NMAPS][4];
+                }
+            };
+            // online softmax of half kb, split in two phases: the row maximum
+            // and rescale (with a wave-uniform branch), then the exponentials
+            // (branch-free, so the scheduler can interleave them with MFMAs)
+            bf16x8 pf[NMAPS][2];
+            // Returns whether the running maximum moved; l is rescaled here,
+            // O by the caller (alpha[m]) once every PV product that used the
+            // old maximum has been accumulated.
+            float alpha[NMAPS];
+            auto softmax_max = [&](int kb) -> bool {
+                bool moved = false;
 #pragma unroll
-            for (int m = 0; m < NMAPS; ++m) {
-                float mx = s[m][0][0];
+                for (int m = 0; m < NMAPS; ++m) {
+                    const f32x16 &sv = sh[kb][m];
+                    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+                    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                                         fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+                    // row maximum across the two lane halves holding the row
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                                     __builtin_bit_cast(unsigned, mx),
+                                                                     false, false);
+                    mx = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]),
+                               __builtin_bit_cast(float, (unsigned)sw[1]));
+                    const float mxs = mx * p.c;
+                    alpha[m] = 1.f;
+                    if (__builtin_amdgcn_ballot_w64(mxs > m_run[m] + kSlack) != 0) {
+                        const float m_new = fmaxf(m_run[m], mxs);
+                        alpha[m] = __builtin_amdgcn_exp2f(m_run[m] - m_new);
+                        l_run[m] *= alpha[m];
+                        m_run[m] = m_new;
+                        moved = true;
+                    }
+                }
+                return moved;
+            };
+            auto rescale_o = [&]() {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        mx = fmaxf(mx, s[m][kb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mxs = mx * p.c;
-                if (__builtin_amdgcn_ballot_w64(mxs > m_run[m] + kSlack) != 0) {
-                    const float m_new = fmaxf(m_run[m], mxs);
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
-                    l_run[m] *= alpha;
+                for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db)
-                        o[m][db] *= alpha;
-                    m_run[m] = m_new;
-                }
-                const float nm = -m_run[m];
-                float lsum = 0.f;
+                        o[m][db] *= alpha[m];
+            };
+            auto softmax_exp = [&](int kb) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int m = 0; m < NMAPS; ++m) {
+                    const f32x16 &sv = sh[kb][m];
+                    const float nm = -m_run[m];
+                    float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
                         bf16x8 v8;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kb][hf * 8 + e], p.c, nm));
-                            lsum += pv;
+                            const float pv = __builtin_amdgcn_exp2f(fmaf(sv[hf * 8 + e], p.c, nm));
+                            lsum[e & 3] += pv;
                             v8[e] = (__bf16)pv;
                         }
-                        pf[m][kb * 2 + hf] = v8;
+                        pf[m][hf] = v8;
                     }
-                l_run[m] += lsum;
-            }
-
-            // ---- O^T += V^T P^T --------------------------------------------
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                    l_run[m] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+                }
+            };
+            // O^T += V^T P^T over the 32 keys of half kb
+            auto pv_half = [&](int kb) {
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const int kbase = kb * 32 + hf * 16;
@@ -318,10 +387,48 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                         const bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
                         for (int m = 0; m < NMAPS; ++m)
-                            o[m][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                va, pf[m][kb * 2 + hf], o[m][db], 0, 0, 0);
+                            o[m][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[m][hf], o[m][db], 0, 0, 0);
                     }
                 }
+            };
+            // scheduling hint for one branch-free block: after its n_ds LDS
+            // reads, alternate one MFMA with a few VALU instructions
+            auto interleave = [&](auto n_ds, auto n_mfma, auto n_valu) {
+                __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds)::value, 0);
+#pragma unroll
+                for (int i = 0; i < decltype(n_mfma)::value; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, decltype(n_valu)::value, 0);
+                }
+            };
+            using QkDs = std::integral_constant<int, NMAPS * D / 16>;
+            using QkMfma = std::integral_constant<int, NMAPS * D / 16>;
+            using PvDs = std::integral_constant<int, 4 * (DV / 32)>;
+            using PvMfma = std::integral_constant<int, NMAPS * 2 * (DV / 32)>;
+            using Valu = std::integral_constant<int, 6>;
+
+            qk_half(0);
+            if (!full)
+                mask_half(0);
+            if (softmax_max(0))
+                rescale_o();
+            qk_half(1);       // matrix work ...
+            softmax_exp(0);   // ... overlapped with the exponentials of half 0
+            interleave(QkDs{}, QkMfma{}, Valu{});
+            // keep the half-0 exponentials in this block (otherwise they are
+            // sunk past the next branch, next to their use)
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                asm volatile("" ::"v"(pf[m][0]), "v"(pf[m][1]), "v"(l_run[m]));
+            if (!full)
+                mask_half(1);
+            const bool moved1 = softmax_max(1);
+            pv_half(0);       // matrix work (probabilities of the old maximum) ...
+            softmax_exp(1);   // ... overlapped with the exponentials of half 1
+            interleave(PvDs{}, PvMfma{}, Valu{});
+            if (moved1)
+                rescale_o();
+            pv_half(1);
         }
 
         store_stage(buf ^ 1);
