@@ -19,7 +19,7 @@ and times the fp64 CPU oracle on a bounded sample of prefill rows
 (cpu_baseline), which also yields a parity check of those rows.
 
 Kernel times come from HIP events recorded on the stream the kernels run on.
-Each workload is warmed up for at least 0.5 s (and at least --warmup calls)
+Each workload is warmed up for at least --warm-seconds (default 0.5 s) and --warmup calls
 before its timed calls, so the GPU clock has settled.
 """
 import argparse
@@ -60,11 +60,16 @@ def cells_of(cfg):
     return c
 
 
-def timed(fn, steps, warmup, torch, min_warm_s=0.5):
+WARM_S = 0.5
+
+
+def timed(fn, steps, warmup, torch, min_warm_s=None):
     """Run fn `warmup` times and, if that took less than min_warm_s seconds,
     keep warming until it has (clocks settle under sustained load), then time
     `steps` calls; return (ms per call by wall clock, ms per call by HIP events
     on the current stream)."""
+    if min_warm_s is None:
+        min_warm_s = WARM_S
     t0 = time.perf_counter()
     for _ in range(warmup):
         fn(0)
@@ -139,11 +144,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="minimum warm-up time per workload (0 for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "strided", "diff", "copy"], default=None,
                     help="time one workload only (for profiler runs); `copy` times a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
     args = ap.parse_args()
+    global WARM_S
+    WARM_S = args.warm_seconds
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU design is described, not built).", file=sys.stderr)
