@@ -22,9 +22,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
 
+# Device code never produces NaN (masked scores are -inf, running maxima start
+# finite), so min/max need no NaN canonicalization.  Host-side argument
+# checks (swa_abi.cpp) keep full IEEE semantics: they must reject NaN.
+KERNEL_ONLY = ["-fno-honor-nans"]
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    extra = KERNEL_ONLY if src.endswith(".hip") else []
+    cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
