@@ -244,7 +244,8 @@ def main():
     if args.only in (None, "diff"):
         fcfg = synth.workload("diff_bf16")
         fins = [dev(x, torch, bf16) for x in synth.diff_inputs(fcfg)]
-        fmask = swa.swa_block_mask_build(fcfg["N"], fcfg["window"], 0, d=fcfg["d"], dv=fcfg["dv"])
+        fmask = swa.swa_block_mask_build(fcfg["N"], fcfg["window"], 0, d=fcfg["d"], dv=fcfg["dv"],
+                                         op=swa.SWA_OP_DIFF)
         fout = torch.empty((fcfg["B"], fcfg["Hq"], fcfg["N"], fcfg["dv"]), dtype=bf16, device="cuda")
         fn = lambda i: swa.diff_attn_fwd(*fins, fcfg["window"], 0, fcfg["scale"], fcfg["lam"], fmask,
                                          out=fout)

@@ -53,6 +53,9 @@ typedef enum {
 
 typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
 
+/* The attention call a block mask is built for (their tile shapes differ). */
+typedef enum { SWA_OP_ATTN = 0, SWA_OP_DIFF = 1 } swa_op_t;
+
 /* Largest sequence length any entry point accepts (keeps every index and
  * cell count of one (batch, head) inside int32). */
 #define SWA_MAX_N (1 << 22)
@@ -93,10 +96,11 @@ typedef struct {
     int32_t *band_begin;
 } swa_block_mask_t;
 
-/* Tile shape (rows bm, keys bn) the attention kernels walk for this dtype
- * and head sizes; a block mask built with other sizes is rejected.
- * Host only, no HIP call.  d, dv in {32, 64, 128}. */
-int swa_tile_config(swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn);
+/* Tile shape (query rows bm, keys bn) the kernel of `op` walks for this
+ * dtype and head sizes (swa_attn_fwd: SWA_OP_ATTN, diff_attn_fwd:
+ * SWA_OP_DIFF); a block mask built with other sizes is rejected by that
+ * call.  Host only, no HIP call.  d, dv in {32, 64, 128}. */
+int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn);
 
 /* Number of query tiles and list entries of the block mask of
  * (N, window, stride, bm, bn).  Host only, no HIP call.
@@ -122,7 +126,8 @@ int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stre
  *   lse            nullable; fp32 [B, Hq, N] natural-log sum of
  *                  exp(score * scale) over the attended keys
  *   d in {32, 64, 128} for SWA_BF16 and SWA_F32
- *   mask           built for (N, window, stride) and swa_tile_config's tiles
+ *   mask           built for (N, window, stride) and the tiles of
+ *                  swa_tile_config(SWA_OP_ATTN, dt, d, d)
  * Arithmetic: bf16 inputs, fp32 accumulation, output rounded to bf16
  * (SWA_BF16) or kept fp32 (SWA_F32).
  */
@@ -167,7 +172,8 @@ int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void 
  *   q1, q2     [B, Hq, N, d]      k1, k2  [B, Hkv, N, d]
  *   v          [B, Hkv, N, dv]    out     [B, Hq, N, dv]
  *   d in {32, 64, 128}, dv in {32, 64, 128}; no normalisation follows the
- *   subtraction.
+ *   subtraction.  mask: built for the tiles of
+ *   swa_tile_config(SWA_OP_DIFF, dt, d, dv).
  */
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2,
                   const void *v, void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N,

@@ -23,6 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP = 0, -1, -2, -3, -4
 SWA_F32, SWA_BF16 = 0, 1
+SWA_OP_ATTN, SWA_OP_DIFF = 0, 1
 SWA_MAX_N = 1 << 22
 
 _p = ctypes.c_void_p
@@ -39,7 +40,7 @@ class swa_block_mask_t(ctypes.Structure):
 
 
 _lib.swa_tile_config.restype = _i
-_lib.swa_tile_config.argtypes = [_i, _i, _i, _i32p, _i32p]
+_lib.swa_tile_config.argtypes = [_i, _i, _i, _i, _i32p, _i32p]
 _lib.swa_block_mask_query.restype = _i
 _lib.swa_block_mask_query.argtypes = [_i, _i, _i, _i, _i, _i32p, _i32p]
 _lib.swa_block_mask_build.restype = _i
@@ -99,11 +100,11 @@ def swa_strerror(status):
     return _lib.swa_strerror(status).decode()
 
 
-def swa_tile_config(dtype, d, dv=None):
-    """(bm, bn): query-tile rows and key-tile keys the kernels walk."""
+def swa_tile_config(dtype, d, dv=None, op=SWA_OP_ATTN):
+    """(bm, bn): query-tile rows and key-tile keys the kernel of `op` walks."""
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     code = SWA_BF16 if dtype == torch.bfloat16 else SWA_F32
-    _check(_lib.swa_tile_config(code, d, dv or d, ctypes.byref(bm), ctypes.byref(bn)),
+    _check(_lib.swa_tile_config(op, code, d, dv or d, ctypes.byref(bm), ctypes.byref(bn)),
            "swa_tile_config")
     return bm.value, bn.value
 
@@ -145,12 +146,12 @@ class BlockMask:
 
 
 def swa_block_mask_build(N, window, stride=0, bm=None, bn=None, device="cuda",
-                         dtype=torch.bfloat16, d=128, dv=None, into=None):
+                         dtype=torch.bfloat16, d=128, dv=None, into=None, op=SWA_OP_ATTN):
     """Build the block mask on the GPU (asynchronous on the current stream),
     into a new BlockMask or into `into` (same sizes, arrays reused).  bm/bn
-    default to the kernels' tile shape."""
+    default to the tile shape of the kernel serving (op, dtype)."""
     if bm is None or bn is None:
-        bm, bn = swa_tile_config(dtype, d, dv)
+        bm, bn = swa_tile_config(dtype, d, dv, op)
     if into is not None:
         if (into.N, into.window, into.stride, into.bm, into.bn) != (N, window, stride, bm, bn):
             raise ValueError("`into` was allocated for another mask")

@@ -15,7 +15,7 @@ namespace {
 constexpr int kSub = 16;  // keys staged per LDS step
 
 template <int D, int DV, int NMAPS>
-__global__ __launch_bounds__(kBM) void fwd_f32_kernel(const float *q0p, const float *k0p,
+__global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const float *k0p,
                                                       const float *q1p, const float *k1p,
                                                       const float *vp, float *out, float *lse,
                                                       MaskView mask, int Hq, int Hkv, int N,
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kBM) void fwd_f32_kernel(const float *q0p, const fl
     const int bh = blockIdx.x / nq;
     const int h = bh % Hq, b = bh / Hq;
     const int g = h / (Hq / Hkv);
-    const int i = qt * kBM + threadIdx.x;
+    const int i = qt * kF32BM + threadIdx.x;
     const int irow = i < N ? i : N - 1;
 
     float qr[NMAPS][D], o[NMAPS][DV], m[NMAPS], l[NMAPS];
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const float *q, const fl
 template <int D, int DV, int NMAPS>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
     unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, DV, NMAPS>), dim3(grid), dim3(kBM), 0, stream,
+    hipLaunchKernelGGL((fwd_f32_kernel<D, DV, NMAPS>), dim3(grid), dim3(kF32BM), 0, stream,
                        static_cast<const float *>(a.q[0]), static_cast<const float *>(a.k[0]),
                        static_cast<const float *>(a.q[1]), static_cast<const float *>(a.k[1]),
                        static_cast<const float *>(a.v), static_cast<float *>(a.out), a.lse, a.mask,

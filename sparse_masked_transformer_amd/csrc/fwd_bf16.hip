@@ -84,14 +84,16 @@ struct Params {
     float lambda;
 };
 
-template <int D, int DV, int NMAPS>
+template <int D, int DV, int NMAPS, int RG>
 __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     using C = Cfg<D, DV, NMAPS>;
+    constexpr int BM = 128 * RG;       // query rows per workgroup
+    constexpr int ROWS = 32 * RG;      // query rows per wave (RG groups of 32)
     __shared__ __attribute__((aligned(16))) char smem[2 * C::stage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5;          // which half of the wave
-    const int col = lane & 31;         // query column within the wave
+    const int col = lane & 31;         // query column within a row group
     const int G = p.Hq / p.Hkv;
     const int nq = p.mask.num_q_tiles;
 
@@ -110,17 +112,24 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int b = rest / p.Hkv;
     const int h = g * G + hg;
 
-    const int q0 = qt * kBM + wave * 32;  // first row of this wave
-    const int my_row = q0 + col;
-    const int64_t q_off = ((int64_t)(b * p.Hq + h) * p.N + (my_row < p.N ? my_row : p.N - 1)) * D;
+    const int q0 = qt * BM + wave * ROWS;  // first row of this wave
+    int my_row[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+        my_row[rg] = q0 + 32 * rg + col;
 
     // ---- Q^T fragments (B operand), one per 16-channel step ----------------
-    bf16x8 qf[NMAPS][D / 16];
+    bf16x8 qf[NMAPS][RG][D / 16];
 #pragma unroll
-    for (int m = 0; m < NMAPS; ++m)
+    for (int rg = 0; rg < RG; ++rg) {
+        const int row = my_row[rg] < p.N ? my_row[rg] : p.N - 1;
+        const int64_t q_off = ((int64_t)(b * p.Hq + h) * p.N + row) * D;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qf[m][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
+        for (int m = 0; m < NMAPS; ++m)
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                qf[m][rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
+    }
 
     // ---- the walk: stride-prefix chunks, then window tiles ----------------
     const int sk = p.mask.stride_keys[qt];
@@ -204,17 +213,19 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int k_lane = col * C::kRow + hl * 16;
     const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * C::vRow + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
-    // ---- running state ------------------------------------------------------
-    f32x16 o[NMAPS][DV / 32];
-    float m_run[NMAPS], l_run[NMAPS];
+    // ---- running state (per map, per row group) --------------------------------
+    f32x16 o[NMAPS][RG][DV / 32];
+    float m_run[NMAPS][RG], l_run[NMAPS][RG];
 #pragma unroll
-    for (int m = 0; m < NMAPS; ++m) {
-        m_run[m] = kNegBig;
-        l_run[m] = 0.f;
+    for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db)
-            o[m][db] = f32x16{};
-    }
+        for (int rg = 0; rg < RG; ++rg) {
+            m_run[m][rg] = kNegBig;
+            l_run[m][rg] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db)
+                o[m][rg][db] = f32x16{};
+        }
 
     if (n_items > 0) {
         load_stage(0);
@@ -222,55 +233,63 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     }
     __syncthreads();
 
-    const int last_row = q0 + 31;
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
         // prefetch the next item (the last item re-reads itself; harmless)
         load_stage(it + 1 < n_items ? it + 1 : it);
 
-        // ---- classify this tile for this wave's rows -----------------------
+        // ---- classify this tile for each row group of this wave -------------
         const bool pre = it < n_pre;
         const int key0 = item_key0(it);
-        bool empty = false, full;
         uint64_t smask = 0;  // stride keys of a window tile, bit per tile row
-        if (pre) {
-            full = (it + 1) * 64 <= sk;
-        } else {
-            if (p.stride > 0) {
-                int f = ((key0 + p.stride - 1) / p.stride) * p.stride;
-                for (int j = f; j < key0 + 64; j += p.stride)
-                    smask |= 1ull << (j - key0);
+        if (!pre && p.stride > 0) {
+            const int f = ((key0 + p.stride - 1) / p.stride) * p.stride;
+            for (int j = f; j < key0 + 64; j += p.stride)
+                smask |= 1ull << (j - key0);
+        }
+        bool full[RG], any = false;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const int r0 = q0 + 32 * rg, r1 = r0 + 31;
+            bool empty;
+            if (pre) {
+                empty = false;
+                full[rg] = (it + 1) * 64 <= sk;
+            } else {
+                empty = key0 > r1 || (key0 + 63 < r0 - p.window + 1 && smask == 0);
+                full[rg] = !empty && key0 + 63 <= r0 && key0 >= r1 - p.window + 1 && key0 + 64 <= p.N;
             }
-            empty = key0 > last_row || (key0 + 63 < q0 - p.window + 1 && smask == 0);
-            full = key0 + 63 <= q0 && key0 >= last_row - p.window + 1 && key0 + 64 <= p.N;
+            any = any || !empty;
         }
 
-        if (!empty) {
+        if (any) {
             const char *kb_base = smem + buf * C::stage + k_lane;
             const char *vb_base = smem + buf * C::stage + NMAPS * C::kTile + v_lane;
 
-            // Two 32-key halves, software-pipelined so MFMA and VALU work of
-            // one wave overlap: QK^T(half 1) is in flight during the softmax
-            // of half 0, and PV(half 0) during the softmax of half 1.
-            f32x16 sh[2][NMAPS];
-            auto qk_half = [&](int kb) {
+            // Scores of row group rg, key half kb (32 keys): S^T = K Q^T.
+            f32x16 sh[RG][2][NMAPS];
+            bf16x8 ka[NMAPS][D / 16];
+            auto read_k = [&](int kb) {
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m) {
-                    bf16x8 ka[D / 16];
+                for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
                     for (int ks = 0; ks < D / 16; ++ks)
-                        ka[ks] = *reinterpret_cast<const bf16x8 *>(
+                        ka[m][ks] = *reinterpret_cast<const bf16x8 *>(
                             kb_base + m * C::kTile + kb * 32 * C::kRow + ks * 32);
+            };
+            auto qk = [&](int rg, int kb) {
+#pragma unroll
+                for (int m = 0; m < NMAPS; ++m) {
                     f32x16 acc = f32x16{};
 #pragma unroll
                     for (int ks = 0; ks < D / 16; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[m][ks], acc, 0, 0, 0);
-                    sh[kb][m] = acc;
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[m][ks], qf[m][rg][ks], acc, 0, 0, 0);
+                    sh[rg][kb][m] = acc;
                 }
             };
-            // per-cell mask of half kb on partial tiles (branch-free selects);
-            // lane key kk = kb*32 + kc + 4*hl with kc a compile-time constant
-            auto mask_half = [&](int kb) {
+            // per-cell mask (branch-free selects); lane key kk = kb*32 + kc +
+            // 4*hl with kc a compile-time constant
+            auto mask = [&](int rg, int kb) {
                 const float ninf = -__builtin_inff();
                 if (pre) {
                     const int lim = sk - it * 64 - kb * 32 - 4 * hl;  // attended iff kc < lim
@@ -279,11 +298,11 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                         const int kcst = (r & 3) + 8 * (r >> 2);
 #pragma unroll
                         for (int m = 0; m < NMAPS; ++m)
-                            sh[kb][m][r] = kcst < lim ? sh[kb][m][r] : ninf;
+                            sh[rg][kb][m][r] = kcst < lim ? sh[rg][kb][m][r] : ninf;
                     }
                 } else {
                     // dist = i - j = base - kc; window part iff 0 <= dist < W
-                    const int base = my_row - key0 - kb * 32 - 4 * hl;
+                    const int base = my_row[rg] - key0 - kb * 32 - 4 * hl;
                     const unsigned W = (unsigned)p.window;
                     if (smask == 0) {
 #pragma unroll
@@ -292,7 +311,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             const bool ok = (unsigned)(base - kcst) < W;
 #pragma unroll
                             for (int m = 0; m < NMAPS; ++m)
-                                sh[kb][m][r] = ok ? sh[kb][m][r] : ninf;
+                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
                         }
                     } else {
                         const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
@@ -305,24 +324,22 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                                             ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
 #pragma unroll
                             for (int m = 0; m < NMAPS; ++m)
-                                sh[kb][m][r] = ok ? sh[kb][m][r] : ninf;
+                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
                         }
                     }
                 }
             };
-            // online softmax of half kb, split in two phases: the row maximum
-            // and rescale (with a wave-uniform branch), then the exponentials
-            // (branch-free, so the scheduler can interleave them with MFMAs)
-            bf16x8 pf[NMAPS][2];
-            // Returns whether the running maximum moved; l is rescaled here,
-            // O by the caller (alpha[m]) once every PV product that used the
-            // old maximum has been accumulated.
-            float alpha[NMAPS];
-            auto softmax_max = [&](int kb) -> bool {
+            // Online softmax, split in two phases: the row maximum and the
+            // rescale decision (wave-uniform branch), then the exponentials
+            // (branch-free, so the scheduler can interleave them with MFMAs).
+            // l is rescaled here, O by rescale_o once every PV product that
+            // used the old maximum has been accumulated.
+            float alpha[NMAPS][RG];
+            auto softmax_max = [&](int rg, int kb) -> bool {
                 bool moved = false;
 #pragma unroll
                 for (int m = 0; m < NMAPS; ++m) {
-                    const f32x16 &sv = sh[kb][m];
+                    const f32x16 &sv = sh[rg][kb][m];
                     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
                     mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
@@ -334,29 +351,30 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                     mx = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]),
                                __builtin_bit_cast(float, (unsigned)sw[1]));
                     const float mxs = mx * p.c;
-                    alpha[m] = 1.f;
-                    if (__builtin_amdgcn_ballot_w64(mxs > m_run[m] + kSlack) != 0) {
-                        const float m_new = fmaxf(m_run[m], mxs);
-                        alpha[m] = __builtin_amdgcn_exp2f(m_run[m] - m_new);
-                        l_run[m] *= alpha[m];
-                        m_run[m] = m_new;
+                    alpha[m][rg] = 1.f;
+                    if (__builtin_amdgcn_ballot_w64(mxs > m_run[m][rg] + kSlack) != 0) {
+                        const float m_new = fmaxf(m_run[m][rg], mxs);
+                        alpha[m][rg] = __builtin_amdgcn_exp2f(m_run[m][rg] - m_new);
+                        l_run[m][rg] *= alpha[m][rg];
+                        m_run[m][rg] = m_new;
                         moved = true;
                     }
                 }
                 return moved;
             };
-            auto rescale_o = [&]() {
+            auto rescale_o = [&](int rg) {
 #pragma unroll
                 for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db)
-                        o[m][db] *= alpha[m];
+                        o[m][rg][db] *= alpha[m][rg];
             };
-            auto softmax_exp = [&](int kb) {
+            bf16x8 pf[RG][2][NMAPS][2];
+            auto softmax_exp = [&](int rg, int kb) {
 #pragma unroll
                 for (int m = 0; m < NMAPS; ++m) {
-                    const f32x16 &sv = sh[kb][m];
-                    const float nm = -m_run[m];
+                    const f32x16 &sv = sh[rg][kb][m];
+                    const float nm = -m_run[m][rg];
                     float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
@@ -367,68 +385,97 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             lsum[e & 3] += pv;
                             v8[e] = (__bf16)pv;
                         }
-                        pf[m][hf] = v8;
+                        pf[rg][kb][m][hf] = v8;
                     }
-                    l_run[m] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+                    l_run[m][rg] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
                 }
             };
-            // O^T += V^T P^T over the 32 keys of half kb
-            auto pv_half = [&](int kb) {
+            // keep a block's exponentials in that block (otherwise they are
+            // sunk past the next branch, next to their use)
+            auto pin = [&](int rg, int kb) {
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int kbase = kb * 32 + hf * 16;
+                for (int m = 0; m < NMAPS; ++m)
+                    asm volatile("" ::"v"(pf[rg][kb][m][0]), "v"(pf[rg][kb][m][1]), "v"(l_run[m][rg]));
+            };
+            // V^T fragments of key half kb, shared by every row group
+            bf16x8 va[2][DV / 32];
+            auto read_v = [&](int kb) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db) {
-                        const char *a = vb_base + kbase * C::vRow + db * 64;
+                        const char *a = vb_base + (kb * 32 + hf * 16) * C::vRow + db * 64;
                         const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a);
                         const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 8 * C::vRow));
                         const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
                         const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
-                        const bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        va[hf][db] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    }
+            };
+            // O^T += V^T P^T over the 32 keys of half kb
+            auto pv = [&](int rg, int kb) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
                         for (int m = 0; m < NMAPS; ++m)
-                            o[m][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[m][hf], o[m][db], 0, 0, 0);
-                    }
-                }
+                            o[m][rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                va[hf][db], pf[rg][kb][m][hf], o[m][rg][db], 0, 0, 0);
             };
-            // scheduling hint for one branch-free block: after its n_ds LDS
-            // reads, alternate one MFMA with a few VALU instructions
-            auto interleave = [&](auto n_ds, auto n_mfma, auto n_valu) {
-                __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds)::value, 0);
+            // scheduling hint for one branch-free block: alternate one MFMA
+            // with a few VALU instructions
+            auto interleave = [&](auto n_mfma) {
 #pragma unroll
                 for (int i = 0; i < decltype(n_mfma)::value; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, decltype(n_valu)::value, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
                 }
             };
-            using QkDs = std::integral_constant<int, NMAPS * D / 16>;
             using QkMfma = std::integral_constant<int, NMAPS * D / 16>;
-            using PvDs = std::integral_constant<int, 4 * (DV / 32)>;
             using PvMfma = std::integral_constant<int, NMAPS * 2 * (DV / 32)>;
-            using Valu = std::integral_constant<int, 6>;
 
-            qk_half(0);
-            if (!full)
-                mask_half(0);
-            if (softmax_max(0))
-                rescale_o();
-            qk_half(1);       // matrix work ...
-            softmax_exp(0);   // ... overlapped with the exponentials of half 0
-            interleave(QkDs{}, QkMfma{}, Valu{});
-            // keep the half-0 exponentials in this block (otherwise they are
-            // sunk past the next branch, next to their use)
+            // ---- the tile, software-pipelined over (row group, key half) ----
+            read_k(0);
 #pragma unroll
-            for (int m = 0; m < NMAPS; ++m)
-                asm volatile("" ::"v"(pf[m][0]), "v"(pf[m][1]), "v"(l_run[m]));
-            if (!full)
-                mask_half(1);
-            const bool moved1 = softmax_max(1);
-            pv_half(0);       // matrix work (probabilities of the old maximum) ...
-            softmax_exp(1);   // ... overlapped with the exponentials of half 1
-            interleave(PvDs{}, PvMfma{}, Valu{});
-            if (moved1)
-                rescale_o();
-            pv_half(1);
+            for (int rg = 0; rg < RG; ++rg)
+                qk(rg, 0);
+            read_k(1);                     // in flight during the maxima below
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                if (!full[rg])
+                    mask(rg, 0);
+                if (softmax_max(rg, 0))
+                    rescale_o(rg);
+            }
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                qk(rg, 1);                 // matrix work ...
+                softmax_exp(rg, 0);        // ... overlapped with exponentials
+                interleave(QkMfma{});
+                pin(rg, 0);
+            }
+            read_v(0);                     // in flight during the maxima below
+            bool moved[RG];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                if (!full[rg])
+                    mask(rg, 1);
+                moved[rg] = softmax_max(rg, 1);
+            }
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                pv(rg, 0);                 // probabilities of the old maximum ...
+                softmax_exp(rg, 1);        // ... overlapped with exponentials
+                interleave(PvMfma{});
+                pin(rg, 1);
+                if (moved[rg])
+                    rescale_o(rg);
+            }
+            read_v(1);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+                pv(rg, 1);
         }
 
         store_stage(buf ^ 1);
@@ -436,46 +483,50 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     }
 
     // ---- epilogue: O / l -> bf16 ------------------------------------------
-    float inv[NMAPS];
 #pragma unroll
-    for (int m = 0; m < NMAPS; ++m) {
-        const float lt = l_run[m] + __shfl_xor(l_run[m], 32);
-        inv[m] = lt > 0.f ? 1.f / lt : 0.f;
-        if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row < p.N)
-            p.lse[(int64_t)(b * p.Hq + h) * p.N + my_row] =
-                lt > 0.f ? (m_run[m] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
-    }
-    if (my_row < p.N) {
-        __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + my_row) * DV;
+    for (int rg = 0; rg < RG; ++rg) {
+        float inv[NMAPS];
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db)
+        for (int m = 0; m < NMAPS; ++m) {
+            const float lt = l_run[m][rg] + __shfl_xor(l_run[m][rg], 32);
+            inv[m] = lt > 0.f ? 1.f / lt : 0.f;
+            if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row[rg] < p.N)
+                p.lse[(int64_t)(b * p.Hq + h) * p.N + my_row[rg]] =
+                    lt > 0.f ? (m_run[m][rg] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+        }
+        if (my_row[rg] < p.N) {
+            __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + my_row[rg]) * DV;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 v4;
+            for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = o[0][db][r4 * 4 + i] * inv[0];
-                    if (NMAPS == 2)
-                        x -= p.lambda * (o[NMAPS - 1][db][r4 * 4 + i] * inv[NMAPS - 1]);
-                    v4[i] = (__bf16)x;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    bf16x4 v4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = o[0][rg][db][r4 * 4 + i] * inv[0];
+                        if (NMAPS == 2)
+                            x -= p.lambda * (o[NMAPS - 1][rg][db][r4 * 4 + i] * inv[NMAPS - 1]);
+                        v4[i] = (__bf16)x;
+                    }
+                    *reinterpret_cast<bf16x4 *>(dst + db * 32 + 8 * r4 + 4 * hl) = v4;
                 }
-                *reinterpret_cast<bf16x4 *>(dst + db * 32 + 8 * r4 + 4 * hl) = v4;
-            }
+        }
     }
 }
 
-// Single-map kernels fit in 256 registers per lane, which lets two waves
-// share each SIMD (one wave's softmax overlaps the other's matrix work);
-// two-map kernels need more state and run one wave per SIMD.
+// Single-map kernels with one row group (32 rows per wave) fit in 256
+// registers per lane, which lets two waves share each SIMD (one wave's
+// softmax overlaps the other's matrix work).  Two-map kernels need more
+// state and run one wave per SIMD.
 template <int D, int DV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFwdRowGroups == 1 ? 2 : 1, 2)))
 void fwd_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 1>(p);
+    fwd_bf16_body<D, DV, 1, kFwdRowGroups>(p);
 }
 
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void diff_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 2>(p);
+    fwd_bf16_body<D, DV, 2, kDiffRowGroups>(p);
 }
 
 template <int D, int DV, int NMAPS>

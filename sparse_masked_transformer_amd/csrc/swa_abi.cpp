@@ -8,7 +8,6 @@
 
 #include "swa_internal.h"
 
-using swa::kBM;
 using swa::kBN;
 
 namespace {
@@ -56,14 +55,14 @@ int mask_query(int N, int window, int stride, int bm, int bn, int32_t *nq_out, i
     return SWA_OK;
 }
 
-// The mask must describe exactly this problem and the kernels' tiling.
-int check_mask(const swa_block_mask_t *m, int N, int window, int stride) {
+// The mask must describe exactly this problem and the kernel's tiling.
+int check_mask(const swa_block_mask_t *m, int N, int window, int stride, int bm) {
     if (m == nullptr)
         return SWA_ERR_INVALID_ARG;
-    if (m->N != N || m->window != window || m->stride != stride || m->bm != kBM || m->bn != kBN)
+    if (m->N != N || m->window != window || m->stride != stride || m->bm != bm || m->bn != kBN)
         return SWA_ERR_INVALID_ARG;
     int32_t nq = 0, nnz = 0;
-    int st = mask_query(N, window, stride, kBM, kBN, &nq, &nnz);
+    int st = mask_query(N, window, stride, bm, kBN, &nq, &nnz);
     if (st != SWA_OK)
         return st;
     if (m->num_q_tiles != nq || m->nnz != nnz)
@@ -106,10 +105,11 @@ int decode_splits(int window) {
 
 extern "C" {
 
-int swa_tile_config(swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn) {
-    if ((dt != SWA_F32 && dt != SWA_BF16) || !head_dim_ok(d) || !head_dim_ok(dv) || !bm || !bn)
+int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn) {
+    if ((op != SWA_OP_ATTN && op != SWA_OP_DIFF) || (dt != SWA_F32 && dt != SWA_BF16) ||
+        !head_dim_ok(d) || !head_dim_ok(dv) || !bm || !bn)
         return SWA_ERR_INVALID_ARG;
-    *bm = kBM;
+    *bm = swa::tile_rows(op, dt);
     *bn = kBN;
     return SWA_OK;
 }
@@ -158,7 +158,7 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
         return st;
     if (!head_dim_ok(d))
         return SWA_ERR_UNSUPPORTED;
-    st = check_mask(mask, N, window, stride);
+    st = check_mask(mask, N, window, stride, swa::tile_rows(SWA_OP_ATTN, dt));
     if (st != SWA_OK)
         return st;
     swa::FwdArgs a{};
@@ -254,7 +254,7 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
     // bf16: two K tiles and one V tile of 64 keys, double-buffered, in 64 KiB of LDS
     if (dt == SWA_BF16 && 2 * d + dv > 256)
         return SWA_ERR_UNSUPPORTED;
-    st = check_mask(mask, N, window, stride);
+    st = check_mask(mask, N, window, stride, swa::tile_rows(SWA_OP_DIFF, dt));
     if (st != SWA_OK)
         return st;
     swa::FwdArgs a{};

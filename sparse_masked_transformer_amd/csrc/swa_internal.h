@@ -9,9 +9,21 @@
 
 namespace swa {
 
-// Query tile rows and key tile size every attention kernel walks.
-constexpr int kBM = 128;
+// Key tile size every attention kernel walks.
 constexpr int kBN = 64;
+// bf16 kernels: 4 waves per workgroup, each owning this many groups of 32
+// query rows (single map: 2, i.e. 256-row query tiles; two maps: 1).
+constexpr int kFwdRowGroups = 1;
+constexpr int kDiffRowGroups = 1;
+// fp32 kernels: one thread per row of a 128-row query tile.
+constexpr int kF32BM = 128;
+
+// Query tile rows of the kernel serving (op, dtype).
+inline int tile_rows(swa_op_t op, swa_dtype_t dt) {
+    if (dt == SWA_F32)
+        return kF32BM;
+    return 128 * (op == SWA_OP_DIFF ? kDiffRowGroups : kFwdRowGroups);
+}
 
 // Device view of a block mask.
 struct MaskView {

@@ -74,10 +74,14 @@ def test_strerror(swa):
 
 def test_tile_config(swa):
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    assert swa.lib.swa_tile_config(1, 128, 128, ctypes.byref(bm), ctypes.byref(bn)) == 0
-    assert (bm.value, bn.value) == (128, 64)
-    assert swa.lib.swa_tile_config(1, 48, 48, ctypes.byref(bm), ctypes.byref(bn)) == swa.SWA_ERR_INVALID_ARG
-    assert swa.lib.swa_tile_config(7, 64, 64, ctypes.byref(bm), ctypes.byref(bn)) == swa.SWA_ERR_INVALID_ARG
+    cfg = lambda op, dt, d, dv: (swa.lib.swa_tile_config(op, dt, d, dv, ctypes.byref(bm), ctypes.byref(bn)),
+                                 bm.value, bn.value)
+    assert cfg(swa.SWA_OP_ATTN, swa.SWA_BF16, 128, 128) == (0, 128, 64)
+    assert cfg(swa.SWA_OP_DIFF, swa.SWA_BF16, 64, 128) == (0, 128, 64)    # 32 rows per wave
+    assert cfg(swa.SWA_OP_ATTN, swa.SWA_F32, 32, 32) == (0, 128, 64)
+    assert cfg(swa.SWA_OP_ATTN, swa.SWA_BF16, 48, 48)[0] == swa.SWA_ERR_INVALID_ARG
+    assert cfg(swa.SWA_OP_ATTN, 7, 64, 64)[0] == swa.SWA_ERR_INVALID_ARG
+    assert cfg(5, swa.SWA_BF16, 64, 64)[0] == swa.SWA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("N,W,s,bm,bn", [
@@ -100,7 +104,7 @@ def test_mask_query_rejects(swa):
 
 
 def fake_mask(swa, N, W, s, bm=128, bn=64, nq=None, nnz=None, null=False):
-    q, z = swa.swa_block_mask_query(N, W, s, 128, 64)
+    q, z = swa.swa_block_mask_query(N, W, s, bm, 64)
     p = 0 if null else FAKE
     return swa.swa_block_mask_t(N, W, s, bm, bn, q if nq is None else nq, z if nnz is None else nnz,
                                 p, p, p, p, p, p)
@@ -131,7 +135,7 @@ def test_fwd_rejections(swa):
     assert fwd(swa, mask=fake_mask(swa, 255, 32, 0)) == E          # built for another N
     assert fwd(swa, mask=fake_mask(swa, 256, 33, 0)) == E          # another window
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 4)) == E          # another stride
-    assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, bm=64)) == E   # another tiling
+    assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, bm=256)) == E  # another tiling
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, nnz=1)) == E   # wrong size
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, null=True)) == E
     assert swa.lib.swa_attn_fwd(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 4, 2, 256, 64, 32, 0, 0.125,
@@ -177,14 +181,15 @@ def test_diff_rejections(swa):
     E, U = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED
 
     def call(d=64, dv=128, dt=1, lam=0.5, q2=FAKE, W=32, mask=None):
-        m = fake_mask(swa, 256, W, 0) if mask is None else mask
+        m = fake_mask(swa, 256, W, 0, bm=128) if mask is None else mask
         return swa.lib.diff_attn_fwd(FAKE, FAKE, q2, FAKE, FAKE, FAKE, dt, 1, 4, 4, 256, d, dv, W, 0,
                                      0.125, lam, ctypes.byref(m), None)
     assert call(q2=0) == E
     assert call(lam=float("inf")) == E
     assert call(d=128, dv=128) == U              # bf16: 2d + dv > 256 does not fit LDS
     assert call(d=96) == U
-    assert call(mask=fake_mask(swa, 256, 31, 0)) == E
+    assert call(mask=fake_mask(swa, 256, 31, 0, bm=128)) == E
+    assert call(mask=fake_mask(swa, 256, 32, 0, bm=64)) == E         # another tiling
 
 
 def test_block_mask_build_rejections(swa):

@@ -56,9 +56,10 @@ MASK_CASES = [(1, 1, 0), (5, 3, 0), (130, 7, 0), (300, 64, 5), (300, 1000, 0), (
 
 
 @pytest.mark.parametrize("N,W,s", MASK_CASES)
-def test_block_mask_bit_exact(swa, N, W, s):
-    banner(f"block mask N={N} W={W} s={s}")
-    m = swa.swa_block_mask_build(N, W, s)
+@pytest.mark.parametrize("bm", [128, 256])
+def test_block_mask_bit_exact(swa, N, W, s, bm):
+    banner(f"block mask N={N} W={W} s={s} bm={bm}")
+    m = swa.swa_block_mask_build(N, W, s, bm=bm, bn=64)
     got = m.host()
     want = oracle.tile_list(N, W, s, m.bm, m.bn)
     assert got["nnz"] == want["nnz"] and got["num_q_tiles"] == want["num_q_tiles"]
@@ -178,7 +179,7 @@ def run_diff(swa, cfg, q1, k1, q2, k2, v):
     dt = cfg["dtype"]
     mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"],
                                     dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
-                                    d=cfg["d"], dv=cfg["dv"])
+                                    d=cfg["d"], dv=cfg["dv"], op=swa.SWA_OP_DIFF)
     out = swa.diff_attn_fwd(dev(q1, dt), dev(k1, dt), dev(q2, dt), dev(k2, dt), dev(v, dt),
                             cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], mask)
     torch.cuda.synchronize()
