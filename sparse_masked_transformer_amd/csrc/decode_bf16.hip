@@ -7,8 +7,9 @@
 //
 // Split kernel: one wave per (sequence, key/value head, split of the ring).
 //   * The wave streams its slots 32 at a time: coalesced 16-byte loads into
-//     registers one step ahead, then into LDS (rows carry a 16-byte-chunk
-//     XOR swizzle).  Several such waves per CU keep enough bytes in flight.
+//     registers two steps ahead (two register stages), then into LDS.  LDS
+//     rows are padded (K +16 bytes, V +64 bytes) so the 16-byte and the
+//     transposed reads are free of bank conflicts.
 //   * The G query heads sharing the key/value head form the 16 columns of a
 //     v_mfma_f32_16x16x32_bf16 (unused columns are zero): S^T = K Q^T with K
 //     from LDS as the A operand; lane l holds head l%16 and keys 4(l/16)+i.
@@ -27,19 +28,21 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1e30f;
 constexpr int kStepKeys = 32;
-
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+constexpr int kMaxSplits = 16;
 
 template <int D>
-__device__ __forceinline__ int chunk_off(int r, int c) {
-    constexpr int cpr = D / 8;
-    constexpr int cmask = (cpr < 8 ? cpr : 8) - 1;
-    return r * (D * 2) + ((c ^ (swz(r) & cmask)) << 4);
-}
+struct Lay {
+    static constexpr int kRow = 2 * D + 16;   // K row stride in LDS, bytes
+    static constexpr int vRow = 2 * D + 64;   // V row stride in LDS, bytes
+    static constexpr int kTile = kStepKeys * kRow;
+    static constexpr int vTile = kStepKeys * vRow;
+    static constexpr int chunks = kStepKeys * D / 8 / 64;  // 16-byte chunks per lane per tensor
+};
 
 struct SplitParams {
     const __bf16 *q;
@@ -52,13 +55,11 @@ struct SplitParams {
     float c;        // scale * log2(e)
 };
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
-    constexpr int kTileBytes = kStepKeys * D * 2;      // one K (or V) step
-    constexpr int kChunks = kTileBytes / 16 / 64;      // 16-byte chunks per lane per tensor
-    __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_split_kernel(SplitParams p) {
+    using Y = Lay<D>;
+    __shared__ __attribute__((aligned(16))) char smem[Y::kTile + Y::vTile];
 
     const int lane = threadIdx.x;
     const int split = blockIdx.x % p.splits;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
     const __bf16 *vbase = p.v + ring * D;
 
     // ---- Q^T fragments: column = query head within the group ----------------
-    const int colq = lane & 15, grp = lane >> 4;
+    const int colq = lane & 15, grp = lane >> 4, sl = lane & 15;
     bf16x8 qf[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -89,28 +90,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
             qf[ks] = bf16x8{};
     }
 
-    // Step st's K and V rows, 16 bytes per lane per load, consecutive lanes
+    // A step's K and V rows, 16 bytes per lane per load, consecutive lanes
     // reading consecutive chunks of a row (coalesced); slots past the ring
     // end are clamped (and masked out below).
-    u32x4 kst[kChunks], vst[kChunks];
-    auto load = [&](int st) {
+    u32x4 kst[2][Y::chunks], vst[2][Y::chunks];
+    auto load = [&](int st, int reg) {
 #pragma unroll
-        for (int u = 0; u < kChunks; ++u) {
-            int x = lane + 64 * u;
-            int r = x / (D / 8), c = x % (D / 8);
+        for (int u = 0; u < Y::chunks; ++u) {
+            const int x = lane + 64 * u;
+            const int r = x / (D / 8), c = x % (D / 8);
             int slot = s0 + st * kStepKeys + r;
             slot = slot < p.window ? slot : p.window - 1;
-            kst[u] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)slot * D + c * 8);
-            vst[u] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)slot * D + c * 8);
+            kst[reg][u] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)slot * D + c * 8);
+            vst[reg][u] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)slot * D + c * 8);
         }
     };
-    auto store = [&]() {
+    // one wave: its LDS writes land after its reads of the previous step
+    auto store = [&](int reg) {
 #pragma unroll
-        for (int u = 0; u < kChunks; ++u) {
-            int x = lane + 64 * u;
-            int r = x / (D / 8), c = x % (D / 8);
-            *reinterpret_cast<u32x4 *>(smem + chunk_off<D>(r, c)) = kst[u];
-            *reinterpret_cast<u32x4 *>(smem + kTileBytes + chunk_off<D>(r, c)) = vst[u];
+        for (int u = 0; u < Y::chunks; ++u) {
+            const int x = lane + 64 * u;
+            const int r = x / (D / 8), c = x % (D / 8);
+            *reinterpret_cast<u32x4 *>(smem + r * Y::kRow + c * 16) = kst[reg][u];
+            *reinterpret_cast<u32x4 *>(smem + Y::kTile + r * Y::vRow + c * 16) = vst[reg][u];
         }
     };
 
@@ -120,40 +122,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
         o[db] = f32x4{};
     float m_run = kNegBig, l_run = 0.f;
 
-    if (nsteps > 0)
-        load(0);
-    for (int st = 0; st < nsteps; ++st) {
-        // one wave: its LDS writes land after its reads of the previous step
-        store();
-        if (st + 1 < nsteps)
-            load(st + 1);
-        const char *kb = smem;
-        const char *vb = smem + kTileBytes;
+    // per-lane LDS read bases (the rest are compile-time offsets)
+    const char *kb = smem + colq * Y::kRow + grp * 16;
+    const char *vb = smem + Y::kTile + (4 * grp + (sl >> 2)) * Y::vRow + 4 * (sl & 3) * 2;
 
-    // ---- S^T = K Q^T for two 16-key blocks ---------------------------
+    auto compute = [&](int st) {
+        // ---- S^T = K Q^T for two 16-key blocks -----------------------------
         f32x4 s[2];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk) {
             f32x4 acc = f32x4{};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-                bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    kb + chunk_off<D>(kbk * 16 + colq, ks * 4 + grp));
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + kbk * 16 * Y::kRow + ks * 64);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
             }
             s[kbk] = acc;
         }
-        // ---- mask slots past the valid range -----------------------------
+        // ---- mask slots past the valid range -------------------------------
         const int base_slot = s0 + st * kStepKeys;
         if (base_slot + kStepKeys > s1) {
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (base_slot + kbk * 16 + grp * 4 + i >= s1)
-                        s[kbk][i] = -__builtin_inff();
+                    s[kbk][i] = base_slot + kbk * 16 + grp * 4 + i < s1 ? s[kbk][i] : -__builtin_inff();
         }
-        // ---- online softmax (row = query head column) ---------------------
+        // ---- online softmax (row = query head column) ------------------------
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -172,28 +167,41 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[kbk][i], p.c, -m_run));
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kbk][i], p.c, -m_run));
                 l_run += pv;
                 pf[kbk * 4 + i] = (__bf16)pv;
             }
-        // ---- O^T += V^T P^T ------------------------------------------------
-        const int sl = lane & 15;
+        // ---- O^T += V^T P^T -------------------------------------------------
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) {
-            const int d0 = db * 16 + 4 * (sl & 3);
-            const int r0 = 4 * grp + (sl >> 2);
-            i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(vb + chunk_off<D>(r0, d0 >> 3) + (d0 & 7) * 2));
-            i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(vb + chunk_off<D>(r0 + 16, d0 >> 3) + (d0 & 7) * 2));
-            bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
-            bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
-            bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + db * 32));
+            const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + 16 * Y::vRow + db * 32));
+            const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
+            const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
+            const bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[db], 0, 0, 0);
+        }
+    };
+
+    // two register stages: steps st (even) and st+1 (odd) alternate
+    if (nsteps > 0)
+        load(0, 0);
+    if (nsteps > 1)
+        load(1, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+        store(0);
+        if (st + 2 < nsteps)
+            load(st + 2, 0);
+        compute(st);
+        if (st + 1 < nsteps) {
+            store(1);
+            if (st + 3 < nsteps)
+                load(st + 3, 1);
+            compute(st + 1);
         }
     }
 
-    // ---- partial results of this split -------------------------------------
+    // ---- partial results of this split ---------------------------------------
     float lt = l_run + __shfl_xor(l_run, 16);
     lt += __shfl_xor(lt, 32);
     if (colq < G) {
@@ -208,33 +216,45 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
     }
 }
 
+// One wave per (sequence, query head).  All split partials are loaded up
+// front (the split count is at most kMaxSplits), so the loads overlap.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_ml, const float *ws_o,
                                                              __bf16 *out, int rows, int splits) {
+    constexpr int kPerLane = (D + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, query head)
     if (row >= rows)
         return;
+    float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits][kPerLane];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        const int64_t r = (int64_t)row * splits + (s < splits ? s : 0);
+        ms[s] = s < splits ? ws_ml[r * 2] : kNegBig;
+        ls[s] = s < splits ? ws_ml[r * 2 + 1] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            os[s][i] = (s < splits && lane + 64 * i < D) ? ws_o[r * D + lane + 64 * i] : 0.f;
+    }
     float mstar = kNegBig;
-    for (int s = 0; s < splits; ++s)
-        mstar = fmaxf(mstar, ws_ml[((int64_t)row * splits + s) * 2]);
-    float lsum = 0.f;
-    float acc[(D + 63) / 64];
 #pragma unroll
-    for (int i = 0; i < (D + 63) / 64; ++i)
+    for (int s = 0; s < kMaxSplits; ++s)
+        mstar = fmaxf(mstar, ms[s]);
+    float lsum = 0.f, acc[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i)
         acc[i] = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const int64_t r = (int64_t)row * splits + s;
-        const float wgt = __builtin_amdgcn_exp2f(ws_ml[r * 2] - mstar);
-        lsum += wgt * ws_ml[r * 2 + 1];
 #pragma unroll
-        for (int i = 0; i < (D + 63) / 64; ++i)
-            if (lane + 64 * i < D)
-                acc[i] += wgt * ws_o[r * D + lane + 64 * i];
+    for (int s = 0; s < kMaxSplits; ++s) {
+        const float wgt = __builtin_amdgcn_exp2f(ms[s] - mstar);
+        lsum += wgt * ls[s];
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            acc[i] += wgt * os[s][i];
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-    for (int i = 0; i < (D + 63) / 64; ++i)
+    for (int i = 0; i < kPerLane; ++i)
         if (lane + 64 * i < D)
             out[(int64_t)row * D + lane + 64 * i] = (__bf16)(acc[i] * inv);
 }
@@ -268,6 +288,7 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
+    static_assert(kMaxSplits >= 16, "decode_splits() returns at most 16");
     switch (a.d) {
     case 32: return launch<32>(a, stream);
     case 64: return launch<64>(a, stream);
