@@ -11,6 +11,9 @@ The same run also measures, each on its own seeded synthetic inputs:
              d=128 (GB/s over the algorithmic bytes: the K and V window, q and
              out, each once; two independent ring sets alternate so no
              iteration finds the previous one's data in cache)
+  sink_decode  the same plus 4 sink slots per (sequence, key/value head)
+  diff_decode  differential decode, 32 sequences x ring 4096, H=16, d=64 per
+             map, dv=128 (both K rings and the one V ring, each read once)
   strided    local+strided prefill, B=2, H=16, N=16384, d=64, W=256, s=128
   diff       differential attention, B=1, H=16, N=4096, d=64/dv=128, W=1024
   tiny_f32   the small fp32 window problem (latency only)
@@ -28,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -147,7 +151,8 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="minimum warm-up time per workload (0 for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "strided", "diff", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "sink_decode", "diff_decode", "strided", "diff",
+                                       "copy"], default=None,
                     help="time one workload only (for profiler runs); `copy` times a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -160,8 +165,8 @@ def main():
 
     import torch
     if not os.path.exists(os.path.join(ROOT, "sparse_masked_transformer_amd", "libswa.so")):
-        from sparse_masked_transformer_amd.build import build
-        build()
+        subprocess.run([sys.executable, os.path.join(ROOT, "sparse_masked_transformer_amd", "build.py")],
+                       check=True)
     import sparse_masked_transformer_amd as swa
     import synth
 
@@ -197,31 +202,73 @@ def main():
         res["prefill"] = dict(wall_ms=wall_ms, event_ms=ev_ms, tflops=flops / (ev_ms * 1e-3) / 1e12)
         log(f"prefill: {ev_ms * 1e3:.1f} us/launch, {res['prefill']['tflops']:.1f} TFLOP/s")
 
-    # ---- decode -------------------------------------------------------------
+    # ---- decode: window, window + sinks, differential ------------------------
+    def time_decode(name, make_inputs, call, alg_bytes):
+        """Two seeded input sets alternate, so no step reads a cache that the
+        previous step left in L2/MALL."""
+        sets = [make_inputs(s) for s in range(2)]
+        fn = lambda i: call(sets[i & 1])
+        log(f"{name}: {K} steps after {W} warmup")
+        wall_ms, ev_ms = timed(fn, K, W, torch)
+        gbs = alg_bytes / (ev_ms * 1e-3) / 1e9
+        log(f"{name}: {ev_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        del sets
+        return dict(wall_ms=wall_ms, event_ms=ev_ms, alg_bytes=alg_bytes, gbs=gbs)
+
+    def i32(x):
+        return torch.from_numpy(x.astype(np.int32)).cuda()
+
     if args.only in (None, "decode"):
         dcfg = synth.workload("window_decode_bf16")
-        sets = []
-        for s in range(2):
+        B, Hq, Hkv, d, Wr = dcfg["B"], dcfg["Hq"], dcfg["Hkv"], dcfg["d"], dcfg["window"]
+
+        def mk(s):
             ins = synth.decode_inputs(dict(dcfg, seed=dcfg["seed"] + 10 * s))
-            sets.append(dict(q=dev(ins["q"], torch, bf16), k=dev(ins["k_ring"], torch, bf16),
-                             v=dev(ins["v_ring"], torch, bf16),
-                             sl=torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda()))
-            del ins
-        B, Hq, d, Wr = dcfg["B"], dcfg["Hq"], dcfg["d"], dcfg["window"]
-        ws = torch.empty(swa.swa_attn_decode_workspace_bytes(B, Hq, d, Wr), dtype=torch.uint8,
-                         device="cuda")
+            return dict(q=dev(ins["q"], torch, bf16), k=dev(ins["k_ring"], torch, bf16),
+                        v=dev(ins["v_ring"], torch, bf16), sl=i32(ins["seq_len"]))
+        ws = torch.empty(max(1, swa.swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, Wr)),
+                         dtype=torch.uint8, device="cuda")
         dout = torch.empty((B, Hq, d), dtype=bf16, device="cuda")
-        dec = lambda i: swa.swa_attn_decode(sets[i & 1]["q"], sets[i & 1]["k"], sets[i & 1]["v"],
-                                            sets[i & 1]["sl"], dcfg["scale"], workspace=ws, out=dout)
-        log(f"decode: {K} steps after {W} warmup")
-        wall_ms, ev_ms = timed(dec, K, W, torch)
-        kv_bytes = 2 * B * dcfg["Hkv"] * Wr * d * 2
-        alg_bytes = kv_bytes + 2 * B * Hq * d * 2
-        res["decode"] = dict(wall_ms=wall_ms, event_ms=ev_ms, alg_bytes=alg_bytes,
-                             gbs=alg_bytes / (ev_ms * 1e-3) / 1e9,
-                             kv_gbs=kv_bytes / (ev_ms * 1e-3) / 1e9)
-        log(f"decode: {ev_ms * 1e3:.1f} us/step, {res['decode']['gbs']:.0f} GB/s")
-        del sets, ws
+        kv_bytes = 2 * B * Hkv * Wr * d * 2
+        res["decode"] = time_decode(
+            "decode", mk, lambda t: swa.swa_attn_decode(t["q"], t["k"], t["v"], t["sl"], dcfg["scale"],
+                                                        workspace=ws, out=dout),
+            kv_bytes + 2 * B * Hq * d * 2)
+        res["decode"]["kv_gbs"] = kv_bytes / (res["decode"]["event_ms"] * 1e-3) / 1e9
+
+    if args.only in (None, "sink_decode"):
+        scfg_ = synth.workload("sink_decode_bf16")
+        B, Hq, Hkv, d, Wr, S = (scfg_[x] for x in ("B", "Hq", "Hkv", "d", "window", "n_sink"))
+
+        def mk(s):
+            ins = synth.decode_inputs(dict(scfg_, seed=scfg_["seed"] + 10 * s))
+            return {x: dev(ins[x], torch, bf16) for x in ("q", "k_sink", "v_sink", "k_ring", "v_ring")} | \
+                dict(sl=i32(ins["seq_len"]))
+        ws = torch.empty(max(1, swa.swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, Wr, S)),
+                         dtype=torch.uint8, device="cuda")
+        dout = torch.empty((B, Hq, d), dtype=bf16, device="cuda")
+        res["sink_decode"] = time_decode(
+            "sink decode", mk,
+            lambda t: swa.swa_attn_decode_sinks(t["q"], t["k_sink"], t["v_sink"], t["k_ring"], t["v_ring"],
+                                                t["sl"], scfg_["scale"], workspace=ws, out=dout),
+            2 * B * Hkv * (Wr + S) * d * 2 + 2 * B * Hq * d * 2)
+
+    if args.only in (None, "diff_decode"):
+        gcfg = synth.workload("diff_decode_bf16")
+        B, Hq, Hkv, d, dv, Wr = (gcfg[x] for x in ("B", "Hq", "Hkv", "d", "dv", "window"))
+
+        def mk(s):
+            ins = synth.diff_decode_inputs(dict(gcfg, seed=gcfg["seed"] + 10 * s))
+            return {x: dev(ins[x], torch, bf16) for x in ("q1", "k1_ring", "q2", "k2_ring", "v_ring")} | \
+                dict(sl=i32(ins["seq_len"]))
+        ws = torch.empty(max(1, swa.swa_attn_decode_workspace_bytes(B, Hq, Hkv, dv, Wr, 0, swa.SWA_OP_DIFF)),
+                         dtype=torch.uint8, device="cuda")
+        dout = torch.empty((B, Hq, dv), dtype=bf16, device="cuda")
+        res["diff_decode"] = time_decode(
+            "diff decode", mk,
+            lambda t: swa.diff_attn_decode(t["q1"], t["k1_ring"], t["q2"], t["k2_ring"], t["v_ring"], t["sl"],
+                                           gcfg["scale"], gcfg["lam"], workspace=ws, out=dout),
+            B * Hkv * Wr * (2 * d + dv) * 2 + B * Hq * (2 * d + dv) * 2)
 
     # ---- local + strided prefill ----------------------------------------------
     if args.only in (None, "strided"):
@@ -313,6 +360,14 @@ def main():
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": round(dd["gbs"] / PEAK_HBM_GBS, 4),
                                        "traffic": traffic_record(dsrc, "decode_bf16_window")}}
+    for key, wl in (("sink_decode", "sink_decode_bf16"), ("diff_decode", "diff_decode_bf16")):
+        if key in res:
+            dd = res[key]
+            line[key] = {"workload": wl, "value": round(dd["gbs"], 1), "unit": "GB/s",
+                         "us_per_step": round(dd["event_ms"] * 1e3, 2),
+                         "roofline": {"bound": "hbm", "achieved": round(dd["gbs"], 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(dd["gbs"] / PEAK_HBM_GBS, 4)}}
     if "strided" in res:
         s = res["strided"]
         t_hbm = s["alg_bytes"] / (PEAK_HBM_GBS * 1e9)

@@ -135,8 +135,13 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
                  swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                  float scale, const swa_block_mask_t *mask, hipStream_t stream);
 
-/* Bytes of device workspace swa_attn_decode needs for these sizes. */
-size_t swa_attn_decode_workspace_bytes(int B, int Hq, int d, int window);
+/* Bytes of device workspace a decode call needs: op SWA_OP_ATTN for
+ * swa_attn_decode and swa_attn_decode_sinks (dv = d), SWA_OP_DIFF for
+ * diff_attn_decode; n_sink = 0 except for swa_attn_decode_sinks.  0 means
+ * the call needs none (workspace may then be NULL); also 0 for invalid
+ * sizes, which the call itself rejects. */
+size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int dv, int window,
+                                       int n_sink);
 
 /*
  * One decode step over a rolling KV window (Learn: Sparse & Sliding-Window
@@ -151,15 +156,56 @@ size_t swa_attn_decode_workspace_bytes(int B, int Hq, int d, int window);
  *              (the attended positions are max(0, L-window) .. L-1), or NULL
  *              for every sequence at length N.  A sequence with L <= 0
  *              attends nothing and gets zeros.
- *   workspace  device scratch of swa_attn_decode_workspace_bytes bytes,
- *              owned by the caller; contents on entry do not matter.
+ *   workspace  device scratch of swa_attn_decode_workspace_bytes(SWA_OP_ATTN,
+ *              B, Hq, Hkv, d, window, 0) bytes, owned by the caller; contents
+ *              on entry do not matter.
  *   stride     must be 0: stride keys older than the window are not in the
  *              ring (SWA_ERR_UNSUPPORTED otherwise).
+ * bf16 needs Hq / Hkv <= 16 (SWA_ERR_UNSUPPORTED otherwise).
  */
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,
                     swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                     float scale, hipStream_t stream);
+
+/*
+ * Decode step with attention sinks (Learn: Sparse & Sliding-Window Attention,
+ * §4, StreamingLLM: the first few tokens stay in the cache next to the
+ * rolling window).  As swa_attn_decode, plus
+ *   k_sink, v_sink  [B, Hkv, n_sink, d]: positions 0 .. n_sink-1 in sink
+ *                   slots (nullable when n_sink == 0)
+ * The attended positions are {p < n_sink} united with the window
+ * max(0, L-window) .. L-1; a position in both is attended once (from the
+ * ring), and only positions < L are attended.  n_sink = 0 is swa_attn_decode.
+ * workspace: swa_attn_decode_workspace_bytes(SWA_OP_ATTN, B, Hq, Hkv, d,
+ * window, n_sink) bytes.
+ */
+int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink, int n_sink,
+                          const void *k_ring, const void *v_ring, void *out,
+                          const int32_t *seq_len, void *workspace, size_t workspace_bytes,
+                          swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window,
+                          float scale, hipStream_t stream);
+
+/*
+ * Differential-attention decode step over a rolling window ("Attention
+ * Variants — Sliding Window, Sparse, Differential": two maps from separate
+ * query/key projections, the second subtracted with weight lambda; the same
+ * page notes that reading the value cache twice slows decoding, so V is read
+ * once for both maps):
+ *
+ *   out = softmax(q1 K1^T * scale) V - lambda * softmax(q2 K2^T * scale) V
+ *
+ * over the window positions of swa_attn_decode.
+ *   q1, q2          [B, Hq, d]            k1_ring, k2_ring  [B, Hkv, window, d]
+ *   v_ring          [B, Hkv, window, dv]  out               [B, Hq, dv]
+ * d, dv in {32, 64, 128}; bf16 also needs 2 d + dv <= 256.
+ * workspace: swa_attn_decode_workspace_bytes(SWA_OP_DIFF, B, Hq, Hkv, dv,
+ * window, 0) bytes.
+ */
+int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const void *k2_ring,
+                     const void *v_ring, void *out, const int32_t *seq_len, void *workspace,
+                     size_t workspace_bytes, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d,
+                     int dv, int window, float scale, float lambda, hipStream_t stream);
 
 /*
  * Differential attention ("Attention Variants — Sliding Window, Sparse,

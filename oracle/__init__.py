@@ -227,6 +227,17 @@ def decode(q, k_ring, v_ring, seq_len, scale, k_sink=None, v_sink=None, with_lse
     return (out, lse) if with_lse else out
 
 
+def diff_decode(q1, k1_ring, q2, k2_ring, v_ring, seq_len, scale, lam):
+    """Differential attention for one decode step over a rolling window
+    ("Attention Variants — Sliding Window, Sparse, Differential": the second
+    map's attention output, weighted by lambda, is subtracted from the
+    first's; both read the same values):
+    decode(q1, K1, V) - lam * decode(q2, K2, V).  Shapes as decode()."""
+    a = decode(q1, k1_ring, v_ring, seq_len, scale)
+    b = decode(q2, k2_ring, v_ring, seq_len, scale)
+    return a - lam * b
+
+
 def count_nsa(n, l, k, w):
     """count_nsa(N, l, k, W): keys read per query by native sparse attention."""
     return int(_load().orc_count_nsa(n, l, k, w))

@@ -4,7 +4,7 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/swa.h, and each function here
 has the name of the C entry point it calls.  PyTorch provides device memory
 and the current HIP stream.  Importing this package fails if the library has
-not been built (``python -m sparse_masked_transformer_amd.build``); there is
+not been built (``python sparse_masked_transformer_amd/build.py``); there is
 no fallback.
 """
 import ctypes
@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libswa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
-                      "`python -m sparse_masked_transformer_amd.build` (hipcc, gfx950)")
+                      "`python sparse_masked_transformer_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -51,10 +51,16 @@ _lib.swa_attn_fwd.restype = _i
 _lib.swa_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                               ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
 _lib.swa_attn_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.swa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.swa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.swa_attn_decode.restype = _i
 _lib.swa_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i, _i, _i,
                                  _i, _i, ctypes.c_float, _p]
+_lib.swa_attn_decode_sinks.restype = _i
+_lib.swa_attn_decode_sinks.argtypes = [_p, _p, _p, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i,
+                                       _i, _i, _i, _i, _i, ctypes.c_float, _p]
+_lib.diff_attn_decode.restype = _i
+_lib.diff_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i,
+                                  _i, _i, _i, _i, ctypes.c_float, ctypes.c_float, _p]
 _lib.diff_attn_fwd.restype = _i
 _lib.diff_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                ctypes.c_float, ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
@@ -183,8 +189,15 @@ def swa_attn_fwd(q, k, v, window, stride, scale, mask, out=None, lse=None):
     return out
 
 
-def swa_attn_decode_workspace_bytes(B, Hq, d, window):
-    return int(_lib.swa_attn_decode_workspace_bytes(B, Hq, d, window))
+def swa_attn_decode_workspace_bytes(B, Hq, Hkv, dv, window, n_sink=0, op=SWA_OP_ATTN):
+    """Workspace bytes of a decode call (0: none needed)."""
+    return int(_lib.swa_attn_decode_workspace_bytes(op, B, Hq, Hkv, dv, window, n_sink))
+
+
+def _workspace(workspace, nbytes, device):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def swa_attn_decode(q, k_ring, v_ring, seq_len, scale, workspace=None, out=None, N=0, stride=0):
@@ -194,15 +207,52 @@ def swa_attn_decode(q, k_ring, v_ring, seq_len, scale, workspace=None, out=None,
         _need(t, n)
     B, Hq, d = q.shape
     Hkv, W = k_ring.shape[1], k_ring.shape[2]
-    if workspace is None:
-        workspace = torch.empty(swa_attn_decode_workspace_bytes(B, Hq, d, W), dtype=torch.uint8,
-                                device=q.device)
+    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W), q.device)
     if out is None:
         out = torch.empty_like(q)
     _check(_lib.swa_attn_decode(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(out), _ptr(seq_len),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _dtype_code(q), B, Hq, Hkv, N, d, W, stride, float(scale),
-                                _stream(q)), "swa_attn_decode")
+                                _ptr(ws), ws_bytes, _dtype_code(q), B, Hq, Hkv, N, d, W, stride,
+                                float(scale), _stream(q)), "swa_attn_decode")
+    return out
+
+
+def swa_attn_decode_sinks(q, k_sink, v_sink, k_ring, v_ring, seq_len, scale, workspace=None,
+                          out=None, N=0):
+    """Decode step with sink slots.  k_sink/v_sink [B,Hkv,S,d] hold positions
+    0..S-1; k_ring/v_ring [B,Hkv,W,d]; returns out [B,Hq,d]."""
+    for t, n in ((q, "q"), (k_sink, "k_sink"), (v_sink, "v_sink"), (k_ring, "k_ring"),
+                 (v_ring, "v_ring")):
+        _need(t, n)
+    B, Hq, d = q.shape
+    Hkv, S, W = k_ring.shape[1], k_sink.shape[2], k_ring.shape[2]
+    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W, S),
+                              q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.swa_attn_decode_sinks(_ptr(q), _ptr(k_sink), _ptr(v_sink), S, _ptr(k_ring),
+                                      _ptr(v_ring), _ptr(out), _ptr(seq_len), _ptr(ws), ws_bytes,
+                                      _dtype_code(q), B, Hq, Hkv, N, d, W, float(scale), _stream(q)),
+           "swa_attn_decode_sinks")
+    return out
+
+
+def diff_attn_decode(q1, k1_ring, q2, k2_ring, v_ring, seq_len, scale, lam, workspace=None,
+                     out=None, N=0):
+    """Differential decode step.  q1/q2 [B,Hq,d]; k1_ring/k2_ring [B,Hkv,W,d];
+    v_ring [B,Hkv,W,dv]; returns out [B,Hq,dv]."""
+    for t, n in ((q1, "q1"), (k1_ring, "k1_ring"), (q2, "q2"), (k2_ring, "k2_ring"),
+                 (v_ring, "v_ring")):
+        _need(t, n)
+    B, Hq, d = q1.shape
+    Hkv, W, dv = v_ring.shape[1], v_ring.shape[2], v_ring.shape[3]
+    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, dv, W, 0,
+                                                                         SWA_OP_DIFF), q1.device)
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=q1.dtype, device=q1.device)
+    _check(_lib.diff_attn_decode(_ptr(q1), _ptr(k1_ring), _ptr(q2), _ptr(k2_ring), _ptr(v_ring),
+                                 _ptr(out), _ptr(seq_len), _ptr(ws), ws_bytes, _dtype_code(q1), B,
+                                 Hq, Hkv, N, d, dv, W, float(scale), float(lam), _stream(q1)),
+           "diff_attn_decode")
     return out
 
 
@@ -221,5 +271,6 @@ def diff_attn_fwd(q1, k1, q2, k2, v, window, stride, scale, lam, mask, out=None)
 
 
 __all__ = ["swa_tile_config", "swa_block_mask_query", "swa_block_mask_build", "swa_mask_dense",
-           "swa_attn_fwd", "swa_attn_decode_workspace_bytes", "swa_attn_decode", "diff_attn_fwd",
+           "swa_attn_fwd", "swa_attn_decode_workspace_bytes", "swa_attn_decode",
+           "swa_attn_decode_sinks", "diff_attn_decode", "diff_attn_fwd",
            "swa_strerror", "SwaError", "BlockMask"]

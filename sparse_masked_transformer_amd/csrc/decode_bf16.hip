@@ -1,23 +1,33 @@
-// One decode step over a rolling KV window, bf16 on gfx950.
+// One decode step over a rolling KV window, bf16 on gfx950, with optional
+// sink slots and one or two score maps.
 //
 // Learn: Sparse & Sliding-Window Attention, §4 and §6: decoding keeps only
 // the last `window` tokens' keys and values in a fixed-size rolling buffer
 // (position p in slot p mod window), so the step reads the whole window once
-// and is bound by HBM bandwidth; each K and V byte is read exactly once.
+// and is bound by HBM bandwidth; StreamingLLM (same page, §4) also keeps the
+// first few tokens in sink slots.  Attention Variants — Sliding Window,
+// Sparse, Differential, "Differential attention": two maps share one value
+// cache, which must not be read twice (each K and V byte is read once here).
 //
-// Split kernel: one wave per (sequence, key/value head, split of the ring).
-//   * The wave streams its slots 32 at a time: coalesced 16-byte loads into
-//     registers two steps ahead (two register stages), then into LDS.  LDS
-//     rows are padded (K +16 bytes, V +64 bytes) so the 16-byte and the
-//     transposed reads are free of bank conflicts.
+// A sequence's cache is walked as one list of "virtual slots": first the
+// sink slots that the ring no longer covers, then the valid ring slots
+// (attention does not depend on key order).
+//
+// Workgroup: `waves` waves for one (sequence, key/value head, split of the
+// virtual slots); each wave takes a contiguous run of whole 32-slot steps.
+//   * A wave streams its slots 32 at a time: coalesced 16-byte loads into
+//     registers two steps ahead (two register stages), then into its own LDS
+//     area, rows padded (K +16 bytes, V +64 bytes) against bank conflicts.
 //   * The G query heads sharing the key/value head form the 16 columns of a
 //     v_mfma_f32_16x16x32_bf16 (unused columns are zero): S^T = K Q^T with K
 //     from LDS as the A operand; lane l holds head l%16 and keys 4(l/16)+i.
-//   * fp32 online softmax in registers (exp2, log2(e) folded into the scale);
-//     O^T += V^T P^T with V^T fragments from ds_read_b64_tr_b16.
-//   * The split's (max, sum, unnormalised output) go to the workspace.
-// Combine kernel: one wave per (sequence, query head) merges the splits:
-//   m* = max m_s, l* = sum l_s 2^(m_s - m*), out = sum o_s 2^(m_s - m*) / l*.
+//   * fp32 online softmax per map (exp2, log2(e) folded into the scale);
+//     O^T += V^T P^T with V^T fragments from ds_read_b64_tr_b16, one V
+//     fragment feeding both maps.
+//   * The waves' (max, sum, output) are merged through LDS in a fixed order.
+//     With one split the workgroup writes the output; otherwise it writes a
+//     partial to the workspace and a combine kernel merges the splits:
+//     m* = max m_s, l* = sum l_s 2^(m_s - m*), o = sum o_s 2^(m_s - m*) / l*.
 #include "swa_internal.h"
 
 namespace swa {
@@ -29,157 +39,228 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
+
+// 16-byte load from a global byte address (a plain global load; a generic
+// pointer rebuilt from an integer would become a flat load)
+__device__ inline u32x4 load16(uintptr_t addr) { return *reinterpret_cast<global_u32x4 *>(addr); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1e30f;
-constexpr int kStepKeys = 32;
-constexpr int kMaxSplits = 16;
 
-template <int D>
+template <int D, int DV, int NMAPS>
 struct Lay {
-    static constexpr int kRow = 2 * D + 16;   // K row stride in LDS, bytes
-    static constexpr int vRow = 2 * D + 64;   // V row stride in LDS, bytes
-    static constexpr int kTile = kStepKeys * kRow;
-    static constexpr int vTile = kStepKeys * vRow;
-    static constexpr int chunks = kStepKeys * D / 8 / 64;  // 16-byte chunks per lane per tensor
+    static constexpr int kRow = 2 * D + 16;    // K row stride in LDS, bytes
+    static constexpr int vRow = 2 * DV + 64;   // V row stride in LDS, bytes
+    static constexpr int kTile = kDecodeStep * kRow;
+    static constexpr int vTile = kDecodeStep * vRow;
+    static constexpr int wave_bytes = NMAPS * kTile + vTile;
+    static constexpr int kChunks = kDecodeStep * D / 8 / 64;   // 16-byte chunks per lane
+    static constexpr int vChunks = kDecodeStep * DV / 8 / 64;
 };
 
-struct SplitParams {
-    const __bf16 *q;
-    const __bf16 *k;
-    const __bf16 *v;
+// Waves per SIMD: two, unless two register stages of two K rows and a V row
+// (2 d + dv > 192) no longer fit half the register file.
+template <int D, int DV, int NMAPS>
+constexpr int occupancy() { return NMAPS == 2 && 2 * D + DV > 192 ? 1 : 2; }
+
+// LDS bytes of a workgroup: the waves' tiles, or the merge area if larger.
+template <int D, int DV, int NMAPS>
+size_t lds_bytes(int waves, int G) {
+    size_t tiles = static_cast<size_t>(waves) * Lay<D, DV, NMAPS>::wave_bytes;
+    size_t merge = static_cast<size_t>(waves) * NMAPS * (2 * 16 + G * DV) * sizeof(float);
+    return tiles > merge ? tiles : merge;
+}
+
+struct Params {
+    const __bf16 *q[2];   // [B, Hq, D]
+    const __bf16 *k[2];   // rings [B, Hkv, window, D]
+    const __bf16 *v;      // ring  [B, Hkv, window, DV]
+    const __bf16 *ks[2];  // sink slots [B, Hkv, n_sink, D] (n_sink == 0: unused)
+    const __bf16 *vs;     // sink slots [B, Hkv, n_sink, DV]
     const int32_t *seq_len;
-    float *ws_ml;   // [B*Hq*S][2]  (max in log2 units, sum)
-    float *ws_o;    // [B*Hq*S][D]
-    int B, Hq, Hkv, N, window, splits, split_len;
-    float c;        // scale * log2(e)
+    __bf16 *out;          // [B, Hq, DV]
+    float *ws_ml;         // [B*Hq*splits*NMAPS][2]  (max in log2 units, sum)
+    float *ws_o;          // [B*Hq*splits*NMAPS][DV]
+    int B, Hq, Hkv, N, window, n_sink, splits, steps_per_wave;
+    float c;              // scale * log2(e)
+    float lambda;
 };
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_split_kernel(SplitParams p) {
-    using Y = Lay<D>;
-    __shared__ __attribute__((aligned(16))) char smem[Y::kTile + Y::vTile];
+template <int D, int DV, int NMAPS>
+__global__ __launch_bounds__(64 * kDecodeMaxWaves)
+__attribute__((amdgpu_waves_per_eu(occupancy<D, DV, NMAPS>(), occupancy<D, DV, NMAPS>())))
+void decode_kernel(Params p) {
+    using Y = Lay<D, DV, NMAPS>;
+    extern __shared__ __attribute__((aligned(16))) char dsm[];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int waves = blockDim.x >> 6;
     const int split = blockIdx.x % p.splits;
     const int bg = blockIdx.x / p.splits;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
     const int G = p.Hq / p.Hkv;
 
+    // ---- this wave's virtual slots -------------------------------------------
     const int L = p.seq_len ? p.seq_len[b] : p.N;
     const int nvalid = L <= 0 ? 0 : (L < p.window ? L : p.window);
-    const int s0 = split * p.split_len;
-    int s1 = s0 + p.split_len;
-    s1 = s1 < nvalid ? s1 : nvalid;
-    const int nsteps = s1 > s0 ? (s1 - s0 + kStepKeys - 1) / kStepKeys : 0;
+    const int first = L - p.window > 0 ? L - p.window : 0;   // oldest position in the ring
+    const int s_eff = first < p.n_sink ? first : p.n_sink;   // sink slots not in the ring
+    const int T = s_eff + nvalid;
+    const int v0 = (split * waves + wave) * p.steps_per_wave * kDecodeStep;
+    int v1 = v0 + p.steps_per_wave * kDecodeStep;
+    v1 = v1 < T ? v1 : T;
+    const int nsteps = v1 > v0 ? (v1 - v0 + kDecodeStep - 1) / kDecodeStep : 0;
 
-    const int64_t ring = (int64_t)(b * p.Hkv + g) * p.window;
-    const __bf16 *kbase = p.k + ring * D;
-    const __bf16 *vbase = p.v + ring * D;
+    const int64_t kv = static_cast<int64_t>(b) * p.Hkv + g;
+    const int64_t ring = kv * p.window, sink = kv * p.n_sink;
 
     // ---- Q^T fragments: column = query head within the group ----------------
     const int colq = lane & 15, grp = lane >> 4, sl = lane & 15;
-    bf16x8 qf[D / 32];
+    bf16x8 qf[NMAPS][D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-        if (colq < G)
-            qf[ks] = *reinterpret_cast<const bf16x8 *>(
-                p.q + ((int64_t)b * p.Hq + g * G + colq) * D + ks * 32 + grp * 8);
-        else
-            qf[ks] = bf16x8{};
-    }
+    for (int m = 0; m < NMAPS; ++m)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            if (colq < G)
+                qf[m][ks] = *reinterpret_cast<const bf16x8 *>(
+                    p.q[m] + (kv * G + colq) * D + ks * 32 + grp * 8);
+            else
+                qf[m][ks] = bf16x8{};
+        }
 
     // A step's K and V rows, 16 bytes per lane per load, consecutive lanes
-    // reading consecutive chunks of a row (coalesced); slots past the ring
-    // end are clamped (and masked out below).
-    u32x4 kst[2][Y::chunks], vst[2][Y::chunks];
-    auto load = [&](int st, int reg) {
+    // reading consecutive chunks of a row (coalesced); virtual slots past the
+    // end are clamped to the last one (and masked out below).  Addresses are
+    // built from wave-uniform byte bases: selecting between two pointers held
+    // in the argument block would turn into a per-lane load of the pointer.
+    uintptr_t kring_b[NMAPS], ksink_b[NMAPS];
 #pragma unroll
-        for (int u = 0; u < Y::chunks; ++u) {
+    for (int m = 0; m < NMAPS; ++m) {
+        kring_b[m] = reinterpret_cast<uintptr_t>(p.k[m]) + static_cast<uintptr_t>(ring) * (2 * D);
+        ksink_b[m] = reinterpret_cast<uintptr_t>(p.ks[m]) + static_cast<uintptr_t>(sink) * (2 * D);
+    }
+    const uintptr_t vring_b = reinterpret_cast<uintptr_t>(p.v) + static_cast<uintptr_t>(ring) * (2 * DV);
+    const uintptr_t vsink_b = reinterpret_cast<uintptr_t>(p.vs) + static_cast<uintptr_t>(sink) * (2 * DV);
+    u32x4 kst[2][NMAPS][Y::kChunks], vst[2][Y::vChunks];
+    auto load = [&](int st, int reg) {
+        const int base = v0 + st * kDecodeStep;
+#pragma unroll
+        for (int u = 0; u < Y::kChunks; ++u) {
             const int x = lane + 64 * u;
             const int r = x / (D / 8), c = x % (D / 8);
-            int slot = s0 + st * kStepKeys + r;
-            slot = slot < p.window ? slot : p.window - 1;
-            kst[reg][u] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)slot * D + c * 8);
-            vst[reg][u] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)slot * D + c * 8);
+            const int vs = base + r < T ? base + r : T - 1;
+            const bool in_sink = vs < s_eff;
+            const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * D) + c * 16;
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                kst[reg][m][u] = load16((in_sink ? ksink_b[m] : kring_b[m]) + off);
+        }
+#pragma unroll
+        for (int u = 0; u < Y::vChunks; ++u) {
+            const int x = lane + 64 * u;
+            const int r = x / (DV / 8), c = x % (DV / 8);
+            const int vs = base + r < T ? base + r : T - 1;
+            const bool in_sink = vs < s_eff;
+            const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * DV) + c * 16;
+            vst[reg][u] = load16((in_sink ? vsink_b : vring_b) + off);
         }
     };
-    // one wave: its LDS writes land after its reads of the previous step
+    char *smem = dsm + wave * Y::wave_bytes;
+    // one wave per LDS area: its writes land after its reads of the previous step
     auto store = [&](int reg) {
 #pragma unroll
-        for (int u = 0; u < Y::chunks; ++u) {
+        for (int u = 0; u < Y::kChunks; ++u) {
             const int x = lane + 64 * u;
             const int r = x / (D / 8), c = x % (D / 8);
-            *reinterpret_cast<u32x4 *>(smem + r * Y::kRow + c * 16) = kst[reg][u];
-            *reinterpret_cast<u32x4 *>(smem + Y::kTile + r * Y::vRow + c * 16) = vst[reg][u];
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                *reinterpret_cast<u32x4 *>(smem + m * Y::kTile + r * Y::kRow + c * 16) = kst[reg][m][u];
+        }
+#pragma unroll
+        for (int u = 0; u < Y::vChunks; ++u) {
+            const int x = lane + 64 * u;
+            const int r = x / (DV / 8), c = x % (DV / 8);
+            *reinterpret_cast<u32x4 *>(smem + NMAPS * Y::kTile + r * Y::vRow + c * 16) = vst[reg][u];
         }
     };
 
-    f32x4 o[D / 16];
+    f32x4 o[NMAPS][DV / 16];
+    float m_run[NMAPS], l_run[NMAPS];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-        o[db] = f32x4{};
-    float m_run = kNegBig, l_run = 0.f;
+    for (int m = 0; m < NMAPS; ++m) {
+#pragma unroll
+        for (int db = 0; db < DV / 16; ++db)
+            o[m][db] = f32x4{};
+        m_run[m] = kNegBig;
+        l_run[m] = 0.f;
+    }
 
     // per-lane LDS read bases (the rest are compile-time offsets)
     const char *kb = smem + colq * Y::kRow + grp * 16;
-    const char *vb = smem + Y::kTile + (4 * grp + (sl >> 2)) * Y::vRow + 4 * (sl & 3) * 2;
+    const char *vb = smem + NMAPS * Y::kTile + (4 * grp + (sl >> 2)) * Y::vRow + 4 * (sl & 3) * 2;
 
     auto compute = [&](int st) {
-        // ---- S^T = K Q^T for two 16-key blocks -----------------------------
-        f32x4 s[2];
+        const int base = v0 + st * kDecodeStep;
+        bf16x8 pf[NMAPS];
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
-            f32x4 acc = f32x4{};
+        for (int m = 0; m < NMAPS; ++m) {
+            // ---- S^T = K Q^T for two 16-key blocks ---------------------------
+            f32x4 s[2];
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + kbk * 16 * Y::kRow + ks * 64);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
+            for (int kbk = 0; kbk < 2; ++kbk) {
+                f32x4 acc = f32x4{};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                        kb + m * Y::kTile + kbk * 16 * Y::kRow + ks * 64);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[m][ks], acc, 0, 0, 0);
+                }
+                s[kbk] = acc;
             }
-            s[kbk] = acc;
-        }
-        // ---- mask slots past the valid range -------------------------------
-        const int base_slot = s0 + st * kStepKeys;
-        if (base_slot + kStepKeys > s1) {
+            // ---- mask virtual slots past this wave's run -----------------------
+            if (base + kDecodeStep > v1) {
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[kbk][i] = base + kbk * 16 + grp * 4 + i < v1 ? s[kbk][i] : -__builtin_inff();
+            }
+            // ---- online softmax (row = query head column) ----------------------
+            float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mxs = mx * p.c;
+            if (mxs > m_run[m]) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run[m] - mxs);
+                l_run[m] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DV / 16; ++db)
+                    o[m][db] *= alpha;
+                m_run[m] = mxs;
+            }
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s[kbk][i] = base_slot + kbk * 16 + grp * 4 + i < s1 ? s[kbk][i] : -__builtin_inff();
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[kbk][i], p.c, -m_run[m]));
+                    l_run[m] += pv;
+                    pf[m][kbk * 4 + i] = (__bf16)pv;
+                }
         }
-        // ---- online softmax (row = query head column) ------------------------
-        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mxs = mx * p.c;
-        if (mxs > m_run) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mxs);
-            l_run *= alpha;
+        // ---- O^T += V^T P^T, one V fragment for every map ---------------------
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db)
-                o[db] *= alpha;
-            m_run = mxs;
-        }
-        bf16x8 pf;
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kbk][i], p.c, -m_run));
-                l_run += pv;
-                pf[kbk * 4 + i] = (__bf16)pv;
-            }
-        // ---- O^T += V^T P^T -------------------------------------------------
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
+        for (int db = 0; db < DV / 16; ++db) {
             const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + db * 32));
             const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + 16 * Y::vRow + db * 32));
             const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
             const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
             const bf16x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[db], 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < NMAPS; ++m)
+                o[m][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[m], o[m][db], 0, 0, 0);
         }
     };
 
@@ -201,99 +282,192 @@ void decode_split_kernel(SplitParams p) {
         }
     }
 
-    // ---- partial results of this split ---------------------------------------
-    float lt = l_run + __shfl_xor(l_run, 16);
-    lt += __shfl_xor(lt, 32);
-    if (colq < G) {
-        const int64_t row = ((int64_t)b * p.Hq + g * G + colq) * p.splits + split;
-        if (grp == 0) {
-            p.ws_ml[row * 2] = m_run;
-            p.ws_ml[row * 2 + 1] = lt;
-        }
+    // ---- merge the waves through LDS ------------------------------------------
+    float lt[NMAPS];
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-            *reinterpret_cast<f32x4 *>(p.ws_o + row * D + db * 16 + grp * 4) = o[db];
+    for (int m = 0; m < NMAPS; ++m) {
+        lt[m] = l_run[m] + __shfl_xor(l_run[m], 16);
+        lt[m] += __shfl_xor(lt[m], 32);
+    }
+    __syncthreads();  // every wave is done with its tiles
+    float *mw = reinterpret_cast<float *>(dsm);   // [waves][NMAPS][16]
+    float *lw = mw + waves * NMAPS * 16;          // [waves][NMAPS][16]
+    float *ow = lw + waves * NMAPS * 16;          // [waves][NMAPS][G][DV]
+    if (grp == 0) {
+#pragma unroll
+        for (int m = 0; m < NMAPS; ++m) {
+            mw[(wave * NMAPS + m) * 16 + colq] = m_run[m];
+            lw[(wave * NMAPS + m) * 16 + colq] = lt[m];
+        }
+    }
+    if (colq < G) {
+#pragma unroll
+        for (int m = 0; m < NMAPS; ++m)
+#pragma unroll
+            for (int db = 0; db < DV / 16; ++db)
+                *reinterpret_cast<f32x4 *>(ow + ((wave * NMAPS + m) * G + colq) * DV + db * 16 + grp * 4) =
+                    o[m][db];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * DV; e += blockDim.x) {
+        const int col = e / DV, dd = e % DV;
+        const int64_t head = kv * G + col;   // b * Hq + query head
+        float res = 0.f;
+#pragma unroll
+        for (int m = 0; m < NMAPS; ++m) {
+            float mstar = kNegBig;
+            for (int w = 0; w < waves; ++w)
+                mstar = fmaxf(mstar, mw[(w * NMAPS + m) * 16 + col]);
+            float l = 0.f, acc = 0.f;
+            for (int w = 0; w < waves; ++w) {
+                const float wgt = __builtin_amdgcn_exp2f(mw[(w * NMAPS + m) * 16 + col] - mstar);
+                l += wgt * lw[(w * NMAPS + m) * 16 + col];
+                acc += wgt * ow[((w * NMAPS + m) * G + col) * DV + dd];
+            }
+            if (p.splits == 1) {
+                const float r = l > 0.f ? acc / l : 0.f;
+                res += m == 0 ? r : -p.lambda * r;
+            } else {
+                const int64_t part = (head * p.splits + split) * NMAPS + m;
+                p.ws_o[part * DV + dd] = acc;
+                if (dd == 0) {
+                    p.ws_ml[part * 2] = mstar;
+                    p.ws_ml[part * 2 + 1] = l;
+                }
+            }
+        }
+        if (p.splits == 1)
+            p.out[head * DV + dd] = (__bf16)res;
     }
 }
 
-// One wave per (sequence, query head).  All split partials are loaded up
-// front (the split count is at most kMaxSplits), so the loads overlap.
-template <int D>
+// One wave per (sequence, query head) merges the splits of every map.  All
+// partials are loaded up front (at most kDecodeMaxSplits), so the loads overlap.
+template <int DV, int NMAPS>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_ml, const float *ws_o,
-                                                             __bf16 *out, int rows, int splits) {
-    constexpr int kPerLane = (D + 63) / 64;
+                                                             __bf16 *out, int rows, int splits,
+                                                             float lambda) {
+    constexpr int kPerLane = (DV + 63) / 64;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, query head)
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + query head
     if (row >= rows)
         return;
-    float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits][kPerLane];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        const int64_t r = (int64_t)row * splits + (s < splits ? s : 0);
-        ms[s] = s < splits ? ws_ml[r * 2] : kNegBig;
-        ls[s] = s < splits ? ws_ml[r * 2 + 1] : 0.f;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
-            os[s][i] = (s < splits && lane + 64 * i < D) ? ws_o[r * D + lane + 64 * i] : 0.f;
-    }
-    float mstar = kNegBig;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        mstar = fmaxf(mstar, ms[s]);
-    float lsum = 0.f, acc[kPerLane];
+    float res[kPerLane];
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i)
-        acc[i] = 0.f;
+        res[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        const float wgt = __builtin_amdgcn_exp2f(ms[s] - mstar);
-        lsum += wgt * ls[s];
+    for (int m = 0; m < NMAPS; ++m) {
+        float ms[kDecodeMaxSplits], ls[kDecodeMaxSplits], os[kDecodeMaxSplits][kPerLane];
+#pragma unroll
+        for (int s = 0; s < kDecodeMaxSplits; ++s) {
+            const int64_t part = (static_cast<int64_t>(row) * splits + (s < splits ? s : 0)) * NMAPS + m;
+            ms[s] = s < splits ? ws_ml[part * 2] : kNegBig;
+            ls[s] = s < splits ? ws_ml[part * 2 + 1] : 0.f;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i)
+                os[s][i] = (s < splits && lane + 64 * i < DV) ? ws_o[part * DV + lane + 64 * i] : 0.f;
+        }
+        float mstar = kNegBig;
+#pragma unroll
+        for (int s = 0; s < kDecodeMaxSplits; ++s)
+            mstar = fmaxf(mstar, ms[s]);
+        float lsum = 0.f, acc[kPerLane];
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i)
-            acc[i] += wgt * os[s][i];
+            acc[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < kDecodeMaxSplits; ++s) {
+            const float wgt = __builtin_amdgcn_exp2f(ms[s] - mstar);
+            lsum += wgt * ls[s];
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i)
+                acc[i] += wgt * os[s][i];
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            res[i] += (m == 0 ? 1.f : -lambda) * (acc[i] * inv);
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i)
-        if (lane + 64 * i < D)
-            out[(int64_t)row * D + lane + 64 * i] = (__bf16)(acc[i] * inv);
+        if (lane + 64 * i < DV)
+            out[static_cast<int64_t>(row) * DV + lane + 64 * i] = (__bf16)res[i];
 }
 
-template <int D>
+template <int D, int DV, int NMAPS>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
-    SplitParams p;
-    p.q = static_cast<const __bf16 *>(a.q);
-    p.k = static_cast<const __bf16 *>(a.k_ring);
+    const DecodePlan plan = decode_plan(a.B, a.Hkv, a.window + a.n_sink);
+    Params p;
+    for (int m = 0; m < 2; ++m) {
+        p.q[m] = static_cast<const __bf16 *>(a.q[m]);
+        p.k[m] = static_cast<const __bf16 *>(a.k_ring[m]);
+        p.ks[m] = static_cast<const __bf16 *>(a.k_sink[m]);
+    }
     p.v = static_cast<const __bf16 *>(a.v_ring);
+    p.vs = static_cast<const __bf16 *>(a.v_sink);
     p.seq_len = a.seq_len;
-    p.splits = decode_splits(a.window);
-    p.split_len = ((a.window + p.splits - 1) / p.splits + kStepKeys - 1) / kStepKeys * kStepKeys;
-    const int64_t rows = (int64_t)a.B * a.Hq;
+    p.out = static_cast<__bf16 *>(a.out);
+    const int64_t rows = static_cast<int64_t>(a.B) * a.Hq;
     p.ws_ml = static_cast<float *>(a.workspace);
-    p.ws_o = p.ws_ml + (rows * p.splits * 2 + 3) / 4 * 4;  // 16-byte aligned section
+    p.ws_o = p.ws_ml + decode_ws_ml_floats(rows * plan.splits * NMAPS);
     p.B = a.B;
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;
     p.N = a.N;
     p.window = a.window;
+    p.n_sink = a.n_sink;
+    p.splits = plan.splits;
+    p.steps_per_wave = plan.steps_per_wave;
     p.c = a.scale * kLog2e;
-    unsigned grid = static_cast<unsigned>((int64_t)a.B * a.Hkv * p.splits);
-    hipLaunchKernelGGL(decode_split_kernel<D>, dim3(grid), dim3(64), 0, stream, p);
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<unsigned>((rows + 3) / 4)),
-                       dim3(256), 0, stream, p.ws_ml, p.ws_o, static_cast<__bf16 *>(a.out),
-                       static_cast<int>(rows), p.splits);
+    p.lambda = a.lambda;
+
+    const size_t lds = lds_bytes<D, DV, NMAPS>(plan.waves, a.Hq / a.Hkv);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, NMAPS>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess)
+            return e;
+    }
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * plan.splits);
+    hipLaunchKernelGGL((decode_kernel<D, DV, NMAPS>), dim3(grid), dim3(64 * plan.waves),
+                       static_cast<unsigned>(lds), stream, p);
+    if (plan.splits > 1)
+        hipLaunchKernelGGL((decode_combine_kernel<DV, NMAPS>), dim3(static_cast<unsigned>((rows + 3) / 4)),
+                           dim3(256), 0, stream, p.ws_ml, p.ws_o, p.out, static_cast<int>(rows),
+                           plan.splits, p.lambda);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
-    static_assert(kMaxSplits >= 16, "decode_splits() returns at most 16");
-    switch (a.d) {
-    case 32: return launch<32>(a, stream);
-    case 64: return launch<64>(a, stream);
-    case 128: return launch<128>(a, stream);
+    static_assert(kDecodeMaxWaves <= 4, "two waves per SIMD: at most 4 waves fit 2 per CU");
+    if (a.nmaps == 1) {
+        if (a.d != a.dv)
+            return hipErrorInvalidValue;
+        if (a.d == 32)
+            return launch<32, 32, 1>(a, stream);
+        if (a.d == 64)
+            return launch<64, 64, 1>(a, stream);
+        if (a.d == 128)
+            return launch<128, 128, 1>(a, stream);
+        return hipErrorInvalidValue;
     }
+    // two maps: 2 d + dv <= 256 (the register stages hold two K rows and a V row)
+    if (a.d == 32 && a.dv == 32)
+        return launch<32, 32, 2>(a, stream);
+    if (a.d == 32 && a.dv == 64)
+        return launch<32, 64, 2>(a, stream);
+    if (a.d == 32 && a.dv == 128)
+        return launch<32, 128, 2>(a, stream);
+    if (a.d == 64 && a.dv == 32)
+        return launch<64, 32, 2>(a, stream);
+    if (a.d == 64 && a.dv == 64)
+        return launch<64, 64, 2>(a, stream);
+    if (a.d == 64 && a.dv == 128)
+        return launch<64, 128, 2>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -6,7 +6,7 @@
 // the block mask lists (stride-prefix keys first, then window tiles), staging
 // 16 keys at a time in LDS, with a per-key online softmax
 // (Attention Variants Compared, "Flash style softmax").
-// Decode: one thread per (sequence, query head) over the valid ring slots.
+// Decode: one thread per (sequence, query head) over the sink and ring slots.
 #include "swa_internal.h"
 
 namespace swa {
@@ -109,39 +109,54 @@ __global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const
         lse[(int64_t)bh * N + i] = m[0] + logf(l[0]);
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_f32_kernel(const float *q, const float *kr,
-                                                        const float *vr, float *out,
-                                                        const int32_t *seq_len, int B, int Hq,
-                                                        int Hkv, int N, int window, float scale) {
-    int row = blockIdx.x * blockDim.x + threadIdx.x;  // b * Hq + h
-    if (row >= B * Hq)
+// One thread per (sequence, query head): the sink slots the ring no longer
+// covers, then the valid ring slots, each with a per-key online softmax per
+// map; out = o1 / l1 - lambda * o2 / l2 for two maps.
+template <int D, int DV, int NMAPS>
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;  // b * Hq + h
+    if (row >= a.B * a.Hq)
         return;
-    int b = row / Hq, h = row % Hq, g = h / (Hq / Hkv);
-    int L = seq_len ? seq_len[b] : N;
-    int nvalid = L <= 0 ? 0 : (L < window ? L : window);
-    const float *qv = q + (int64_t)row * D;
-    const float *kb = kr + (int64_t)(b * Hkv + g) * window * D;
-    const float *vb = vr + (int64_t)(b * Hkv + g) * window * D;
-    float o[D], m = -__builtin_inff(), l = 0.f;
-    for (int c = 0; c < D; ++c)
-        o[c] = 0.f;
-    for (int slot = 0; slot < nvalid; ++slot) {
-        float s = 0.f;
-        for (int c = 0; c < D; ++c)
-            s = fmaf(qv[c], kb[(int64_t)slot * D + c], s);
-        s *= scale;
-        float mn = fmaxf(m, s);
-        float alpha = expf(m - mn);
-        float e = expf(s - mn);
-        l = l * alpha + e;
-        for (int c = 0; c < D; ++c)
-            o[c] = fmaf(o[c], alpha, e * vb[(int64_t)slot * D + c]);
-        m = mn;
+    const int b = row / a.Hq, h = row % a.Hq, g = h / (a.Hq / a.Hkv);
+    const int L = a.seq_len ? a.seq_len[b] : a.N;
+    const int nvalid = L <= 0 ? 0 : (L < a.window ? L : a.window);
+    const int first = L - a.window > 0 ? L - a.window : 0;
+    const int s_eff = first < a.n_sink ? first : a.n_sink;
+    const int64_t kv = static_cast<int64_t>(b) * a.Hkv + g;
+    float o[NMAPS][DV], m[NMAPS], l[NMAPS];
+    for (int mp = 0; mp < NMAPS; ++mp) {
+        for (int c = 0; c < DV; ++c)
+            o[mp][c] = 0.f;
+        m[mp] = -__builtin_inff();
+        l[mp] = 0.f;
     }
-    float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int c = 0; c < D; ++c)
-        out[(int64_t)row * D + c] = o[c] * inv;
+    for (int t = 0; t < s_eff + nvalid; ++t) {
+        const bool in_sink = t < s_eff;
+        const int64_t r = in_sink ? kv * a.n_sink + t : kv * a.window + (t - s_eff);
+        const float *vrow = static_cast<const float *>(in_sink ? a.v_sink : a.v_ring) + r * DV;
+        for (int mp = 0; mp < NMAPS; ++mp) {
+            const float *qv = static_cast<const float *>(a.q[mp]) + static_cast<int64_t>(row) * D;
+            const float *krow = static_cast<const float *>(in_sink ? a.k_sink[mp] : a.k_ring[mp]) + r * D;
+            float s = 0.f;
+            for (int c = 0; c < D; ++c)
+                s = fmaf(qv[c], krow[c], s);
+            s *= a.scale;
+            const float mn = fmaxf(m[mp], s);
+            const float alpha = expf(m[mp] - mn);  // m = -inf on the first key -> 0
+            const float e = expf(s - mn);
+            l[mp] = l[mp] * alpha + e;
+            for (int c = 0; c < DV; ++c)
+                o[mp][c] = fmaf(o[mp][c], alpha, e * vrow[c]);
+            m[mp] = mn;
+        }
+    }
+    float *dst = static_cast<float *>(a.out) + static_cast<int64_t>(row) * DV;
+    for (int c = 0; c < DV; ++c) {
+        float x = l[0] > 0.f ? o[0][c] / l[0] : 0.f;
+        if (NMAPS == 2)
+            x -= a.lambda * (l[NMAPS - 1] > 0.f ? o[NMAPS - 1][c] / l[NMAPS - 1] : 0.f);
+        dst[c] = x;
+    }
 }
 
 template <int D, int DV, int NMAPS>
@@ -176,18 +191,26 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t stream) {
-    unsigned grid = static_cast<unsigned>((a.B * a.Hq + 63) / 64);
-#define SWA_DEC_CASE(DQ)                                                                      \
-    if (a.d == DQ) {                                                                          \
-        hipLaunchKernelGGL(decode_f32_kernel<DQ>, dim3(grid), dim3(64), 0, stream,            \
-                           static_cast<const float *>(a.q), static_cast<const float *>(a.k_ring), \
-                           static_cast<const float *>(a.v_ring), static_cast<float *>(a.out), \
-                           a.seq_len, a.B, a.Hq, a.Hkv, a.N, a.window, a.scale);              \
-        return hipGetLastError();                                                             \
+    const unsigned grid = static_cast<unsigned>((static_cast<int64_t>(a.B) * a.Hq + 63) / 64);
+#define SWA_DEC_CASE(DQ, DVV)                                                            \
+    if (a.d == DQ && a.dv == DVV) {                                                      \
+        if (a.nmaps == 1)                                                                \
+            hipLaunchKernelGGL((decode_f32_kernel<DQ, DVV, 1>), dim3(grid), dim3(64), 0, \
+                               stream, a);                                               \
+        else                                                                             \
+            hipLaunchKernelGGL((decode_f32_kernel<DQ, DVV, 2>), dim3(grid), dim3(64), 0, \
+                               stream, a);                                               \
+        return hipGetLastError();                                                        \
     }
-    SWA_DEC_CASE(32)
-    SWA_DEC_CASE(64)
-    SWA_DEC_CASE(128)
+    SWA_DEC_CASE(32, 32)
+    SWA_DEC_CASE(32, 64)
+    SWA_DEC_CASE(32, 128)
+    SWA_DEC_CASE(64, 32)
+    SWA_DEC_CASE(64, 64)
+    SWA_DEC_CASE(64, 128)
+    SWA_DEC_CASE(128, 32)
+    SWA_DEC_CASE(128, 64)
+    SWA_DEC_CASE(128, 128)
 #undef SWA_DEC_CASE
     return hipErrorInvalidValue;
 }

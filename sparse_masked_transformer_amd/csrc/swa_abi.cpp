@@ -92,16 +92,85 @@ swa::MaskView view_of(const swa_block_mask_t *m) {
 }  // namespace
 
 namespace swa {
-int decode_splits(int window) {
-    // Each split covers at least 256 ring slots; at most 16 splits.
-    int s = window / 256;
-    if (s < 1)
-        s = 1;
-    if (s > 16)
-        s = 16;
-    return s;
+DecodePlan decode_plan(int B, int Hkv, int slots) {
+    // At least 8 steps per wave where the cache allows; enough workgroups to
+    // fill the chip once; every wave at least one step.
+    const int64_t steps = (static_cast<int64_t>(slots > 0 ? slots : 1) + kDecodeStep - 1) / kDecodeStep;
+    int64_t waves = (steps + 7) / 8;
+    waves = waves < 1 ? 1 : (waves > kDecodeMaxWaves ? kDecodeMaxWaves : waves);
+    const int64_t pairs = static_cast<int64_t>(B) * Hkv;
+    const int64_t want_wgs = (kDecodeTargetWaves + waves - 1) / waves;
+    int64_t splits = (want_wgs + pairs - 1) / pairs;
+    int64_t max_splits = (steps + waves - 1) / waves;
+    max_splits = max_splits < kDecodeMaxSplits ? max_splits : kDecodeMaxSplits;
+    splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+    const int64_t spw = (steps + splits * waves - 1) / (splits * waves);
+    return DecodePlan{static_cast<int>(waves), static_cast<int>(splits), static_cast<int>(spw)};
 }
 }  // namespace swa
+
+namespace {
+
+size_t decode_ws_bytes(int nmaps, int B, int Hq, int Hkv, int dv, int window, int n_sink) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(dv) || window < 1 ||
+        window > SWA_MAX_N || n_sink < 0 || n_sink > SWA_MAX_N)
+        return 0;
+    const swa::DecodePlan plan = swa::decode_plan(B, Hkv, window + n_sink);
+    if (plan.splits == 1)
+        return 0;  // the workgroups write the output directly
+    // per (sequence, query head, split, map): running max and sum (section
+    // padded to 16 bytes), then dv partial sums; all fp32
+    const int64_t parts = static_cast<int64_t>(B) * Hq * plan.splits * nmaps;
+    return static_cast<size_t>(swa::decode_ws_ml_floats(parts) + parts * dv) * sizeof(float);
+}
+
+// Checks shared by the decode entry points; fills nothing on failure.
+int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes) {
+    for (int m = 0; m < a.nmaps; ++m) {
+        if (!aligned16(a.q[m]) || !aligned16(a.k_ring[m]))
+            return SWA_ERR_INVALID_ARG;
+        if (a.n_sink > 0 && !aligned16(a.k_sink[m]))
+            return SWA_ERR_INVALID_ARG;
+    }
+    if (!aligned16(a.v_ring) || !aligned16(a.out) || (a.n_sink > 0 && !aligned16(a.v_sink)))
+        return SWA_ERR_INVALID_ARG;
+    if (a.seq_len != nullptr && (reinterpret_cast<uintptr_t>(a.seq_len) & 3u) != 0)
+        return SWA_ERR_INVALID_ARG;
+    if (dt != SWA_F32 && dt != SWA_BF16)
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(a.scale) || !(a.scale > 0.f) || !std::isfinite(a.lambda))
+        return SWA_ERR_INVALID_ARG;
+    if (a.B < 1 || a.Hq < 1 || a.Hkv < 1 || a.Hq % a.Hkv != 0 || a.window < 1 ||
+        a.window > SWA_MAX_N || a.n_sink < 0 || a.n_sink > SWA_MAX_N || stride < 0 ||
+        (a.seq_len == nullptr && a.N < 0))
+        return SWA_ERR_INVALID_ARG;
+    if (dt == SWA_BF16 && a.Hq / a.Hkv > 16)
+        return SWA_ERR_UNSUPPORTED;  // the query heads of a group share one 16-column tile
+    if (static_cast<int64_t>(a.B) * a.Hkv * (a.window + a.n_sink) > INT32_MAX)
+        return SWA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(a.d) || !head_dim_ok(a.dv))
+        return SWA_ERR_UNSUPPORTED;
+    // bf16, two maps: two K rows and a V row per slot in the register stages
+    if (dt == SWA_BF16 && a.nmaps == 2 && 2 * a.d + a.dv > 256)
+        return SWA_ERR_UNSUPPORTED;
+    if (stride != 0)
+        return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
+    const size_t need = decode_ws_bytes(a.nmaps, a.B, a.Hq, a.Hkv, a.dv, a.window, a.n_sink);
+    if (need > 0 && (a.workspace == nullptr || !aligned16(a.workspace) || workspace_bytes < need))
+        return SWA_ERR_WORKSPACE;
+    return SWA_OK;
+}
+
+int decode_run(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes,
+               hipStream_t stream) {
+    int st = decode_checks(a, dt, stride, workspace_bytes);
+    if (st != SWA_OK)
+        return st;
+    return hip_status(dt == SWA_BF16 ? swa::launch_decode_bf16(a, stream)
+                                     : swa::launch_decode_f32(a, stream));
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -182,44 +251,20 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
 }
 
-size_t swa_attn_decode_workspace_bytes(int B, int Hq, int d, int window) {
-    if (B < 1 || Hq < 1 || !head_dim_ok(d) || window < 1)
+size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int dv, int window,
+                                       int n_sink) {
+    if (op != SWA_OP_ATTN && op != SWA_OP_DIFF)
         return 0;
-    // per (sequence, query head, split): running max and sum (section padded
-    // to 16 bytes), then d partial sums; all fp32
-    size_t parts = static_cast<size_t>(B) * Hq * swa::decode_splits(window);
-    return (((parts * 2 + 3) / 4) * 4 + parts * d) * sizeof(float);
+    return decode_ws_bytes(op == SWA_OP_DIFF ? 2 : 1, B, Hq, Hkv, dv, window, n_sink);
 }
 
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,
                     swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                     float scale, hipStream_t stream) {
-    if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out))
-        return SWA_ERR_INVALID_ARG;
-    if (seq_len != nullptr && (reinterpret_cast<uintptr_t>(seq_len) & 3u) != 0)
-        return SWA_ERR_INVALID_ARG;
-    if (dt != SWA_F32 && dt != SWA_BF16)
-        return SWA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale) || !(scale > 0.f))
-        return SWA_ERR_INVALID_ARG;
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || window < 1 || window > SWA_MAX_N ||
-        stride < 0 || (seq_len == nullptr && N < 0))
-        return SWA_ERR_INVALID_ARG;
-    if (dt == SWA_BF16 && Hq / Hkv > 16)
-        return SWA_ERR_UNSUPPORTED;  // the query heads of a group share one 16-column tile
-    if (static_cast<int64_t>(B) * Hkv * window > INT32_MAX)
-        return SWA_ERR_UNSUPPORTED;
-    if (!head_dim_ok(d))
-        return SWA_ERR_UNSUPPORTED;
-    if (stride != 0)
-        return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
-    if (workspace == nullptr || !aligned16(workspace) ||
-        workspace_bytes < swa_attn_decode_workspace_bytes(B, Hq, d, window))
-        return SWA_ERR_WORKSPACE;
     swa::DecodeArgs a{};
-    a.q = q;
-    a.k_ring = k_ring;
+    a.q[0] = q;
+    a.k_ring[0] = k_ring;
     a.v_ring = v_ring;
     a.out = out;
     a.seq_len = seq_len;
@@ -229,10 +274,68 @@ int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void 
     a.Hkv = Hkv;
     a.N = N;
     a.d = d;
+    a.dv = d;
     a.window = window;
+    a.n_sink = 0;
+    a.nmaps = 1;
     a.scale = scale;
-    return hip_status(dt == SWA_BF16 ? swa::launch_decode_bf16(a, stream)
-                                     : swa::launch_decode_f32(a, stream));
+    a.lambda = 0.f;
+    return decode_run(a, dt, stride, workspace_bytes, stream);
+}
+
+int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink, int n_sink,
+                          const void *k_ring, const void *v_ring, void *out,
+                          const int32_t *seq_len, void *workspace, size_t workspace_bytes,
+                          swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window,
+                          float scale, hipStream_t stream) {
+    swa::DecodeArgs a{};
+    a.q[0] = q;
+    a.k_ring[0] = k_ring;
+    a.v_ring = v_ring;
+    a.k_sink[0] = k_sink;
+    a.v_sink = v_sink;
+    a.out = out;
+    a.seq_len = seq_len;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.dv = d;
+    a.window = window;
+    a.n_sink = n_sink;
+    a.nmaps = 1;
+    a.scale = scale;
+    a.lambda = 0.f;
+    return decode_run(a, dt, 0, workspace_bytes, stream);
+}
+
+int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const void *k2_ring,
+                     const void *v_ring, void *out, const int32_t *seq_len, void *workspace,
+                     size_t workspace_bytes, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d,
+                     int dv, int window, float scale, float lambda, hipStream_t stream) {
+    swa::DecodeArgs a{};
+    a.q[0] = q1;
+    a.q[1] = q2;
+    a.k_ring[0] = k1_ring;
+    a.k_ring[1] = k2_ring;
+    a.v_ring = v_ring;
+    a.out = out;
+    a.seq_len = seq_len;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.dv = dv;
+    a.window = window;
+    a.n_sink = 0;
+    a.nmaps = 2;
+    a.scale = scale;
+    a.lambda = lambda;
+    return decode_run(a, dt, 0, workspace_bytes, stream);
 }
 
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,

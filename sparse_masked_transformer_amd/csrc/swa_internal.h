@@ -49,19 +49,39 @@ struct FwdArgs {
     MaskView mask;
 };
 
+// One decode step (one or two score maps, optional sink slots).
 struct DecodeArgs {
-    const void *q;
-    const void *k_ring;
+    const void *q[2];
+    const void *k_ring[2];
     const void *v_ring;
+    const void *k_sink[2];   // used when n_sink > 0
+    const void *v_sink;
     void *out;
     const int32_t *seq_len;
     void *workspace;
-    int B, Hq, Hkv, N, d, window;
+    int B, Hq, Hkv, N, d, dv, window, n_sink, nmaps;
     float scale;
+    float lambda;   // weight of the second map (two-map problems only)
 };
 
-// Number of key splits the decode kernel uses for a ring of `window` slots.
-int decode_splits(int window);
+// Decode work split (bf16 kernel): slots are walked in steps of kDecodeStep;
+// a workgroup of `waves` waves (at most kDecodeMaxWaves) covers one split of
+// one (sequence, key/value head), each wave `steps_per_wave` steps.
+constexpr int kDecodeStep = 32;
+constexpr int kDecodeMaxWaves = 4;
+constexpr int kDecodeMaxSplits = 16;
+// Waves resident on the chip at two per SIMD (256 CUs x 4 SIMDs x 2).
+constexpr int kDecodeTargetWaves = 2048;
+
+struct DecodePlan {
+    int waves, splits, steps_per_wave;
+};
+// Plan for B*Hkv (sequence, key/value head) pairs and at most `slots` cache
+// slots (window + sink slots) per pair.
+DecodePlan decode_plan(int B, int Hkv, int slots);
+// fp32 count of the (max, sum) section of the decode workspace for `parts`
+// partial results, padded so the output section starts 16-byte aligned.
+inline int64_t decode_ws_ml_floats(int64_t parts) { return (parts * 2 + 3) / 4 * 4; }
 
 hipError_t launch_block_mask_build(const swa_block_mask_t &m, hipStream_t stream);
 hipError_t launch_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream);

@@ -18,6 +18,11 @@ window_decode_bf16     64 sequences at position 131072, ring W=4096,
                        Hq=32, Hkv=8, d=128, bf16, seed 4
 diff_bf16              B=1, H=16, N=4096, d=64 per map, dv=128, W=1024,
                        lambda 0.5, scale 1/8, bf16, seed 5
+sink_decode_bf16       window_decode_bf16 plus 4 sink slots (positions 0-3),
+                       seed 6
+diff_decode_bf16       32 sequences at position 131072, ring W=4096, H=16,
+                       d=64 per map, dv=128, lambda 0.5, scale 1/8, bf16,
+                       seed 7
 =====================  =====================================================
 """
 import math
@@ -36,6 +41,11 @@ WORKLOADS = {
                                scale=1.0 / math.sqrt(128), seed=4),
     "diff_bf16": dict(kind="diff", dtype="bf16", B=1, Hq=16, Hkv=16, N=4096, d=64, dv=128,
                       window=1024, stride=0, scale=1.0 / 8, lam=0.5, seed=5),
+    "sink_decode_bf16": dict(kind="decode", dtype="bf16", B=64, Hq=32, Hkv=8, window=4096,
+                             d=128, dv=128, position=131072, n_sink=4,
+                             scale=1.0 / math.sqrt(128), seed=6),
+    "diff_decode_bf16": dict(kind="diff_decode", dtype="bf16", B=32, Hq=16, Hkv=16, window=4096,
+                             d=64, dv=128, position=131072, scale=1.0 / 8, lam=0.5, seed=7),
 }
 
 
@@ -101,6 +111,22 @@ def decode_inputs(cfg, seq_len=None):
     if seq_len is None:
         seq_len = np.full(B, cfg["position"] + 1, dtype=np.int64)
     return dict(q=q, k_ring=kr, v_ring=vr, k_sink=ks, v_sink=vs,
+                seq_len=np.asarray(seq_len, dtype=np.int64))
+
+
+def diff_decode_inputs(cfg, seq_len=None):
+    """q1 [B,Hq,d], k1_ring [B,Hkv,W,d], q2, k2_ring, v_ring [B,Hkv,W,dv] and
+    seq_len [B] (int64), drawn in that order; seq_len as in decode_inputs."""
+    rng = np.random.default_rng(cfg["seed"])
+    B, Hq, Hkv, W, d, dv = (cfg[x] for x in ("B", "Hq", "Hkv", "window", "d", "dv"))
+    q1 = _draw(rng, (B, Hq, d), cfg["dtype"])
+    k1 = _draw(rng, (B, Hkv, W, d), cfg["dtype"])
+    q2 = _draw(rng, (B, Hq, d), cfg["dtype"])
+    k2 = _draw(rng, (B, Hkv, W, d), cfg["dtype"])
+    v = _draw(rng, (B, Hkv, W, dv), cfg["dtype"])
+    if seq_len is None:
+        seq_len = np.full(B, cfg["position"] + 1, dtype=np.int64)
+    return dict(q1=q1, k1_ring=k1, q2=q2, k2_ring=k2, v_ring=v,
                 seq_len=np.asarray(seq_len, dtype=np.int64))
 
 

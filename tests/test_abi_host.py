@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -24,8 +25,7 @@ FAKE = 0x7F0000000000  # 16-byte aligned; never dereferenced by a rejected call
 @pytest.fixture(scope="module")
 def swa():
     if not os.path.exists(os.path.join(PKG, "libswa.so")):
-        from sparse_masked_transformer_amd.build import build
-        build()
+        subprocess.run([sys.executable, os.path.join(PKG, "build.py")], check=True)
     import sparse_masked_transformer_amd as m
     return m
 
@@ -37,11 +37,12 @@ def declared_functions():
     return sorted(set(n for n in names if n not in ("if", "while")))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_hot_path_calls():
     names = declared_functions()
-    for n in ("swa_block_mask_build", "swa_attn_fwd", "swa_attn_decode", "diff_attn_fwd"):
+    for n in ("swa_block_mask_build", "swa_attn_fwd", "swa_attn_decode", "swa_attn_decode_sinks",
+              "diff_attn_fwd", "diff_attn_decode"):
         assert n in names
-    assert len(names) == 9, names
+    assert len(names) == 11, names
 
 
 def test_library_exports_every_declared_symbol(swa):
@@ -147,12 +148,13 @@ def test_fwd_rejections(swa):
 def dec(swa, q=FAKE, kr=FAKE, vr=FAKE, out=FAKE, sl=None, ws=FAKE, wsb=None, dt=1, B=2, Hq=8,
         Hkv=2, N=10, d=128, W=64, s=0, scale=0.1):
     if wsb is None:
-        wsb = swa.swa_attn_decode_workspace_bytes(B, Hq, d, W)
+        wsb = swa.swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W)
     return swa.lib.swa_attn_decode(q, kr, vr, out, sl, ws, wsb, dt, B, Hq, Hkv, N, d, W, s, scale, None)
 
 
 def test_decode_rejections(swa):
     E, U, WS = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED, swa.SWA_ERR_WORKSPACE
+    assert swa.swa_attn_decode_workspace_bytes(2, 8, 2, 128, 64) > 0   # the cases below need one
     assert dec(swa, q=0) == E
     assert dec(swa, vr=FAKE + 4) == E
     assert dec(swa, sl=FAKE + 2) == E
@@ -164,17 +166,65 @@ def test_decode_rejections(swa):
     assert dec(swa, s=3) == U                    # stride keys are not in the ring
     assert dec(swa, Hq=32, Hkv=1) == U           # more than 16 heads per key/value head
     assert dec(swa, ws=0) == WS
-    assert dec(swa, wsb=swa.swa_attn_decode_workspace_bytes(2, 8, 128, 64) - 4) == WS
+    assert dec(swa, wsb=swa.swa_attn_decode_workspace_bytes(2, 8, 2, 128, 64) - 4) == WS
     assert dec(swa, ws=FAKE + 8) == WS
 
 
+def test_decode_sinks_rejections(swa):
+    E, U, WS = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED, swa.SWA_ERR_WORKSPACE
+
+    def call(ks=FAKE, vs=FAKE, S=4, ws=FAKE, wsb=None, Hq=8, Hkv=2, d=64, W=60, dt=1):
+        if wsb is None:
+            wsb = swa.swa_attn_decode_workspace_bytes(1, Hq, Hkv, d, W, max(S, 0))
+        return swa.lib.swa_attn_decode_sinks(FAKE, ks, vs, S, FAKE, FAKE, FAKE, None, ws, wsb, dt, 1,
+                                             Hq, Hkv, 100, d, W, 0.125, None)
+    assert call(S=-1) == E
+    assert call(ks=0) == E                       # sink slots without a sink buffer
+    assert call(vs=FAKE + 8) == E
+    assert call(S=swa.SWA_MAX_N + 1) == E
+    assert call(d=48) == U
+    assert call(Hq=34, Hkv=2) == U
+    assert call(ws=0) == WS
+    assert call(wsb=swa.swa_attn_decode_workspace_bytes(1, 8, 2, 64, 60, 4) - 16) == WS
+
+
+def test_diff_decode_rejections(swa):
+    E, U = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED
+
+    def call(q2=FAKE, d=64, dv=128, lam=0.5, dt=1, Hq=4, Hkv=4, scale=0.125):
+        wsb = swa.swa_attn_decode_workspace_bytes(2, Hq, Hkv, dv, 256, 0, swa.SWA_OP_DIFF)
+        return swa.lib.diff_attn_decode(FAKE, FAKE, q2, FAKE, FAKE, FAKE, None, FAKE, wsb, dt, 2, Hq,
+                                        Hkv, 300, d, dv, 256, scale, lam, None)
+    assert call(q2=0) == E
+    assert call(q2=FAKE + 4) == E
+    assert call(lam=float("nan")) == E
+    assert call(scale=-1.0) == E
+    assert call(d=128, dv=128) == U              # bf16: 2d + dv > 256 does not fit the stages
+    assert call(dv=96) == U
+    assert call(Hq=64, Hkv=2) == U
+
+
 def test_decode_workspace_bytes(swa):
-    # 16 splits of 256 slots for a 4096-slot ring; (max, sum) section padded to 16 bytes
-    parts = 64 * 32 * 16
-    assert swa.swa_attn_decode_workspace_bytes(64, 32, 128, 4096) == (parts * 2 + parts * 128) * 4
-    parts = 1 * 3 * 1
-    assert swa.swa_attn_decode_workspace_bytes(1, 3, 32, 100) == (8 + parts * 32) * 4
-    assert swa.swa_attn_decode_workspace_bytes(0, 3, 32, 100) == 0
+    ATTN, DIFF = swa.SWA_OP_ATTN, swa.SWA_OP_DIFF
+    ws = lambda *a: swa.lib.swa_attn_decode_workspace_bytes(*a)
+    # 512 (sequence, key/value head) pairs of a 4096-slot ring fill the chip
+    # with one workgroup each: the output is written directly, no workspace
+    assert ws(ATTN, 64, 32, 8, 128, 4096, 0) == 0
+    assert ws(ATTN, 64, 32, 8, 128, 4096, 4) == 0
+    assert ws(DIFF, 32, 16, 16, 128, 4096, 0) == 0
+    # one pair, 4 steps of 32 slots: 4 splits of one wave; 12 partials of
+    # (max, sum) padded to 24 floats, then 12 x 32 partial outputs
+    assert ws(ATTN, 1, 3, 1, 32, 100, 0) == (24 + 12 * 32) * 4
+    # 4 pairs, 128 steps: 4 waves per workgroup, 16 splits (the cap); two maps
+    parts = 2 * 4 * 16 * 2
+    assert ws(DIFF, 2, 4, 2, 128, 4096, 0) == (parts * 2 + parts * 128) * 4
+    # sink slots count as cache slots: 60 + 4 = 64 slots = 2 steps -> 2 splits
+    parts = 1 * 8 * 2
+    assert ws(ATTN, 1, 8, 2, 64, 60, 4) == (parts * 2 + parts * 64) * 4
+    # invalid sizes
+    assert ws(ATTN, 0, 3, 1, 32, 100, 0) == 0
+    assert ws(ATTN, 1, 3, 2, 32, 100, 0) == 0
+    assert ws(7, 1, 3, 1, 32, 100, 0) == 0
 
 
 def test_diff_rejections(swa):

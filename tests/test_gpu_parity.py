@@ -225,13 +225,18 @@ def run_decode(swa, cfg, ins, pass_len=True):
     return host(out)
 
 
+LENS16 = [(i * 397) % 2100 for i in range(16)]   # 0 .. 2099, below, at and above the window
+
 DECODE_CASES = [
-    # B, Hq, Hkv, W, d, lengths
-    (3, 4, 1, 64, 64, [1, 30, 64]),
-    (2, 8, 2, 300, 128, [299, 1000]),
-    (4, 4, 4, 1000, 32, [0, 5, 999, 1001]),
-    (2, 16, 1, 512, 128, [513, 4096]),
+    # B, Hq, Hkv, W, d, lengths   (bf16 work split: workgroups of 1-4 waves; splits)
+    (3, 4, 1, 64, 64, [1, 30, 64]),            # 1 wave, 2 splits
+    (2, 8, 2, 300, 128, [299, 1000]),          # 2 waves, 5 splits
+    (4, 4, 4, 1000, 32, [0, 5, 999, 1001]),    # 4 waves, 8 splits
+    (2, 16, 1, 512, 128, [513, 4096]),         # 16 heads per key/value head
     (1, 2, 2, 33, 64, [100]),
+    (16, 16, 16, 1000, 64, LENS16),            # 4 waves, 2 splits, 4 steps per wave
+    (64, 8, 8, 1000, 32, [(i * 131) % 1400 for i in range(64)]),  # 512 pairs: 4 waves, one split
+    (64, 8, 8, 520, 32, [(i * 131) % 700 for i in range(64)]),    # 3 waves, 2 splits
 ]
 
 
@@ -255,6 +260,107 @@ def test_decode_default_length(swa):
     got = run_decode(swa, cfg, ins, pass_len=False)
     want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"])
     assert max_err(got, want) <= TOL["bf16"]
+
+
+def run_decode_sinks(swa, cfg, ins):
+    dt = cfg["dtype"]
+    sl = torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda()
+    out = swa.swa_attn_decode_sinks(dev(ins["q"], dt), dev(ins["k_sink"], dt), dev(ins["v_sink"], dt),
+                                    dev(ins["k_ring"], dt), dev(ins["v_ring"], dt), sl, cfg["scale"])
+    torch.cuda.synchronize()
+    return host(out)
+
+
+SINK_CASES = [
+    # B, Hq, Hkv, W, n_sink, d, lengths
+    (2, 8, 2, 64, 4, 128, [3, 200]),           # no sink yet outside the ring; 4 sinks
+    (3, 4, 1, 100, 4, 64, [102, 104, 5000]),   # sinks partly still in the ring
+    (1, 2, 2, 31, 1, 32, [40]),                # sink + ring = exactly one 32-slot step
+    (2, 4, 2, 48, 8, 128, [57, 8]),
+    (16, 16, 16, 1000, 4, 64, LENS16),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,W,S,d,lens", SINK_CASES)
+def test_decode_sinks_parity(swa, dtype, B, Hq, Hkv, W, S, d, lens):
+    banner(f"decode sinks {dtype} B={B} Hq={Hq} Hkv={Hkv} W={W} S={S} d={d} lens={lens}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, window=W, d=d, dv=d, position=0, n_sink=S,
+               scale=1.0 / math.sqrt(d), seed=W + S)
+    ins = synth.decode_inputs(cfg, seq_len=lens)
+    got = run_decode_sinks(swa, cfg, ins)
+    want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"],
+                         k_sink=ins["k_sink"], v_sink=ins["v_sink"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+def run_diff_decode(swa, cfg, ins):
+    dt = cfg["dtype"]
+    sl = torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda()
+    out = swa.diff_attn_decode(dev(ins["q1"], dt), dev(ins["k1_ring"], dt), dev(ins["q2"], dt),
+                               dev(ins["k2_ring"], dt), dev(ins["v_ring"], dt), sl, cfg["scale"],
+                               cfg["lam"])
+    torch.cuda.synchronize()
+    return host(out)
+
+
+DIFF_DECODE_CASES = [
+    # B, Hq, Hkv, W, d, dv, lengths
+    (2, 4, 2, 64, 64, 128, [1, 500]),
+    (3, 2, 2, 300, 32, 64, [0, 299, 1000]),
+    (1, 8, 1, 129, 32, 128, [129]),
+    (2, 4, 4, 96, 64, 64, [50, 97]),
+    (16, 16, 16, 1000, 64, 128, LENS16),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,W,d,dv,lens", DIFF_DECODE_CASES)
+def test_diff_decode_parity(swa, dtype, B, Hq, Hkv, W, d, dv, lens):
+    banner(f"diff decode {dtype} B={B} Hq={Hq} Hkv={Hkv} W={W} d={d} dv={dv} lens={lens}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, window=W, d=d, dv=dv, position=0, scale=0.125,
+               lam=0.5, seed=W + d + dv)
+    ins = synth.diff_decode_inputs(cfg, seq_len=lens)
+    got = run_diff_decode(swa, cfg, ins)
+    want = oracle.diff_decode(ins["q1"], ins["k1_ring"], ins["q2"], ins["k2_ring"], ins["v_ring"],
+                              ins["seq_len"], cfg["scale"], cfg["lam"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+def test_diff_decode_f32_wide_heads(swa):
+    # fp32 has no register-stage limit: d = dv = 128 with two maps
+    cfg = dict(dtype="f32", B=2, Hq=4, Hkv=2, window=80, d=128, dv=128, position=0, scale=0.09,
+               lam=0.8, seed=71)
+    banner("diff decode f32 d=dv=128")
+    ins = synth.diff_decode_inputs(cfg, seq_len=[81, 40])
+    got = run_diff_decode(swa, cfg, ins)
+    want = oracle.diff_decode(ins["q1"], ins["k1_ring"], ins["q2"], ins["k2_ring"], ins["v_ring"],
+                              ins["seq_len"], cfg["scale"], cfg["lam"])
+    assert max_err(got, want) <= TOL["f32"]
+
+
+def test_sink_decode_workload(swa):
+    cfg = synth.workload("sink_decode_bf16")
+    banner("workload sink_decode_bf16 (sequences 0, 29, 63)")
+    ins = synth.decode_inputs(cfg)
+    got = run_decode_sinks(swa, cfg, ins)
+    pick = [0, 29, 63]
+    want = oracle.decode(ins["q"][pick], ins["k_ring"][pick], ins["v_ring"][pick], ins["seq_len"][pick],
+                         cfg["scale"], k_sink=ins["k_sink"][pick], v_sink=ins["v_sink"][pick])
+    assert max_err(got[pick], want) <= TOL["bf16"]
+    assert np.all(np.isfinite(got))
+
+
+def test_diff_decode_workload(swa):
+    cfg = synth.workload("diff_decode_bf16")
+    banner("workload diff_decode_bf16 (sequences 0, 13, 31)")
+    ins = synth.diff_decode_inputs(cfg)
+    got = run_diff_decode(swa, cfg, ins)
+    pick = [0, 13, 31]
+    want = oracle.diff_decode(*(ins[x][pick] for x in ("q1", "k1_ring", "q2", "k2_ring", "v_ring",
+                                                        "seq_len")), cfg["scale"], cfg["lam"])
+    assert max_err(got[pick], want) <= TOL["bf16"]
+    assert np.all(np.isfinite(got))
 
 
 def test_decode_workload(swa):

@@ -408,6 +408,47 @@ def test_decode_with_sinks(L, W, S):
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("L,W", [(1, 8), (6, 8), (8, 8), (29, 8), (40, 16)])
+def test_diff_decode_is_last_row_of_diff_prefill(L, W):
+    # decode of the newest token equals the last row of the masked two-map
+    # prefill over the whole sequence (window of that row = the ring)
+    B, H, d, dv = 2, 3, 8, 12
+    k1seq, k2seq = rand((B, H, L, d), 60), rand((B, H, L, d), 61)
+    vseq = rand((B, H, L, dv), 62)
+    q1seq, q2seq = rand((B, H, L, d), 63), rand((B, H, L, d), 64)
+    k1r, vr = ring_from_sequence(k1seq, vseq, L, W)
+    k2r, _ = ring_from_sequence(k2seq, vseq, L, W)
+    got = oracle.diff_decode(q1seq[:, :, L - 1], k1r, q2seq[:, :, L - 1], k2r, vr, np.full(B, L),
+                             0.3, 0.7)
+    rows = [(b * H + h) * L + L - 1 for b in range(B) for h in range(H)]
+    want = oracle.diff_rows(q1seq, k1seq, q2seq, k2seq, vseq, W, 0, 0.3, 0.7, rows)
+    np.testing.assert_allclose(got.reshape(-1, dv), want, rtol=1e-12, atol=1e-12)
+
+
+def test_diff_decode_special_cases():
+    B, Hq, Hkv, W, d, dv = 2, 4, 2, 8, 8, 8
+    q1, q2 = rand((B, Hq, d), 65), rand((B, Hq, d), 66)
+    k1, k2 = rand((B, Hkv, W, d), 67), rand((B, Hkv, W, d), 68)
+    v = rand((B, Hkv, W, dv), 69)
+    L = np.array([5, 20])
+    # the same map twice: (1 - lambda) times one map, by brute force over the
+    # attended slots (slots 0..4 of sequence 0, every slot of sequence 1)
+    got = oracle.diff_decode(q1, k1, q1, k1, v, L, 0.5, 0.25)
+    for b, n in ((0, 5), (1, W)):
+        G = Hq // Hkv
+        for h in range(Hq):
+            kk, vv = k1[b, h // G, :n].astype(np.float64), v[b, h // G, :n].astype(np.float64)
+            s = kk @ q1[b, h].astype(np.float64) * 0.5
+            p = np.exp(s - s.max())
+            want = 0.75 * (p / p.sum()) @ vv
+            np.testing.assert_allclose(got[b, h], want, rtol=1e-12, atol=1e-12)
+    # lambda = 0: the first map alone; a sequence with no tokens gives zeros
+    L0 = np.array([0, 20])
+    z = oracle.diff_decode(q1, k1, q2, k2, v, L0, 0.5, 0.0)
+    assert np.all(z[0] == 0)
+    np.testing.assert_allclose(z[1], oracle.decode(q1, k1, v, L0, 0.5)[1], rtol=1e-14, atol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # counting helpers and inputs
 # --------------------------------------------------------------------------
