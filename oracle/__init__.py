@@ -26,23 +26,23 @@ _ptr = ctypes.c_void_p
 def _configure(lib):
     """Declare the C signatures of oracle.c on a loaded library."""
     lib.orc_allowed.restype = ctypes.c_int
-    lib.orc_allowed.argtypes = [_i64] * 5
+    lib.orc_allowed.argtypes = [_i64] * 7
     lib.orc_mask_dense.restype = None
-    lib.orc_mask_dense.argtypes = [_i64, _i64, _i64, _ptr]
+    lib.orc_mask_dense.argtypes = [_i64] * 5 + [_ptr]
     lib.orc_count_nonmasked.restype = _i64
-    lib.orc_count_nonmasked.argtypes = [_i64, _i64, _i64, _ptr]
+    lib.orc_count_nonmasked.argtypes = [_i64] * 5 + [_ptr]
     lib.orc_tile_list.restype = _i64
-    lib.orc_tile_list.argtypes = [_i64] * 5 + [_ptr] * 6 + [_i64]
+    lib.orc_tile_list.argtypes = [_i64] * 7 + [_ptr] * 6 + [_i64]
     lib.orc_attention_row.restype = _dbl
     lib.orc_attention_row.argtypes = [_ptr] * 4 + [_i64] * 5 + [_dbl, _ptr, _ptr]
     lib.orc_tiled_softmax_dot.restype = None
     lib.orc_tiled_softmax_dot.argtypes = [_ptr] * 3 + [_i64] * 4 + [_dbl, _ptr]
     lib.orc_attn_rows.restype = None
-    lib.orc_attn_rows.argtypes = [_ptr] * 3 + [_i64] * 8 + [_dbl, _ptr, _i64, _ptr, _ptr]
+    lib.orc_attn_rows.argtypes = [_ptr] * 3 + [_i64] * 10 + [_dbl, _ptr, _i64, _ptr, _ptr]
     lib.orc_attn_full.restype = None
-    lib.orc_attn_full.argtypes = [_ptr] * 3 + [_i64] * 8 + [_dbl, _ptr, _ptr]
+    lib.orc_attn_full.argtypes = [_ptr] * 3 + [_i64] * 10 + [_dbl, _ptr, _ptr]
     lib.orc_diff_rows.restype = None
-    lib.orc_diff_rows.argtypes = [_ptr] * 5 + [_i64] * 8 + [_dbl, _dbl, _ptr, _i64, _ptr]
+    lib.orc_diff_rows.argtypes = [_ptr] * 5 + [_i64] * 10 + [_dbl, _dbl, _ptr, _i64, _ptr]
     lib.orc_decode.restype = None
     lib.orc_decode.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _ptr, _ptr]
     lib.orc_count_nsa.restype = _i64
@@ -82,26 +82,28 @@ def _p(a):
     return a.ctypes.data if a is not None else None
 
 
-def allowed(i, j, n, window, stride=0):
-    """Mask predicate of swa_mask / strided_mask ("Attention Variants Compared")."""
-    return bool(_load().orc_allowed(i, j, n, window, stride))
+def allowed(i, j, n, window, stride=0, dilation=1, n_global=0):
+    """Mask predicate of swa_mask / strided_mask ("Attention Variants Compared"),
+    with Longformer's dilation and global tokens ("Learn: Sparse &
+    Sliding-Window Attention" §3b) under the causal order."""
+    return bool(_load().orc_allowed(i, j, n, window, stride, dilation, n_global))
 
 
-def mask_dense(n, window, stride=0):
+def mask_dense(n, window, stride=0, dilation=1, n_global=0):
     """Dense 0/1 uint8 [n, n] mask (1 = attends)."""
     out = np.zeros((n, n), dtype=np.uint8)
-    _load().orc_mask_dense(n, window, stride, out.ctypes.data)
+    _load().orc_mask_dense(n, window, stride, dilation, n_global, out.ctypes.data)
     return out
 
 
-def count_nonmasked(n, window, stride=0):
+def count_nonmasked(n, window, stride=0, dilation=1, n_global=0):
     """(total, per-row counts) of attended cells -- count_nonmasked(M)."""
     rows = np.zeros(n, dtype=np.int64)
-    total = _load().orc_count_nonmasked(n, window, stride, rows.ctypes.data)
+    total = _load().orc_count_nonmasked(n, window, stride, dilation, n_global, rows.ctypes.data)
     return int(total), rows
 
 
-def tile_list(n, window, stride, bm, bn):
+def tile_list(n, window, stride, bm, bn, dilation=1, n_global=0):
     """Block mask as a CSR over query tiles (see orc_tile_list)."""
     nq, nk = -(-n // bm), -(-n // bn)
     cap = nq * nk
@@ -109,14 +111,15 @@ def tile_list(n, window, stride, bm, bn):
     kv_tile = np.zeros(max(cap, 1), dtype=np.int32)
     kind = np.zeros(max(cap, 1), dtype=np.uint8)
     cells = np.zeros(max(cap, 1), dtype=np.int32)
-    stride_keys = np.zeros(nq, dtype=np.int32)
+    prefix_keys = np.zeros(nq, dtype=np.int32)
     band_begin = np.zeros(nq, dtype=np.int32)
-    nnz = _load().orc_tile_list(n, window, stride, bm, bn, row_ptr.ctypes.data,
-                                kv_tile.ctypes.data, kind.ctypes.data, cells.ctypes.data,
-                                stride_keys.ctypes.data, band_begin.ctypes.data, cap)
+    nnz = _load().orc_tile_list(n, window, stride, dilation, n_global, bm, bn,
+                                row_ptr.ctypes.data, kv_tile.ctypes.data, kind.ctypes.data,
+                                cells.ctypes.data, prefix_keys.ctypes.data, band_begin.ctypes.data,
+                                cap)
     assert nnz >= 0
     return dict(row_ptr=row_ptr, kv_tile=kv_tile[:nnz].copy(), kind=kind[:nnz].copy(),
-                cells=cells[:nnz].copy(), stride_keys=stride_keys, band_begin=band_begin,
+                cells=cells[:nnz].copy(), prefix_keys=prefix_keys, band_begin=band_begin,
                 nnz=int(nnz), num_q_tiles=nq)
 
 
@@ -147,7 +150,7 @@ def tiled_softmax_dot(q, K, V, scale, tile=4):
     return out
 
 
-def attn_rows(q, k, v, window, stride, scale, rows, with_lse=False):
+def attn_rows(q, k, v, window, stride, scale, rows, with_lse=False, dilation=1, n_global=0):
     """Masked attention for selected flat rows (b*Hq + h)*N + i.
 
     q: [B, Hq, N, d]; k: [B, Hkv, N, d]; v: [B, Hkv, N, dv] (float32 values).
@@ -160,12 +163,12 @@ def attn_rows(q, k, v, window, stride, scale, rows, with_lse=False):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((len(rows), dv), dtype=np.float64)
     lse = np.zeros(len(rows), dtype=np.float64)
-    _load().orc_attn_rows(qp, kp, vp, B, Hq, Hkv, N, d, dv, window, stride, scale,
-                          rows.ctypes.data, len(rows), out.ctypes.data, lse.ctypes.data)
+    _load().orc_attn_rows(qp, kp, vp, B, Hq, Hkv, N, d, dv, window, stride, dilation, n_global,
+                          scale, rows.ctypes.data, len(rows), out.ctypes.data, lse.ctypes.data)
     return (out, lse) if with_lse else out
 
 
-def attn_full(q, k, v, window, stride, scale, with_lse=False):
+def attn_full(q, k, v, window, stride, scale, with_lse=False, dilation=1, n_global=0):
     """Masked attention for every row: out [B, Hq, N, dv] float64."""
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -174,12 +177,12 @@ def attn_full(q, k, v, window, stride, scale, with_lse=False):
     Hkv, dv = k.shape[1], v.shape[3]
     out = np.zeros((B, Hq, N, dv), dtype=np.float64)
     lse = np.zeros((B, Hq, N), dtype=np.float64)
-    _load().orc_attn_full(qp, kp, vp, B, Hq, Hkv, N, d, dv, window, stride, scale,
-                          out.ctypes.data, lse.ctypes.data)
+    _load().orc_attn_full(qp, kp, vp, B, Hq, Hkv, N, d, dv, window, stride, dilation, n_global,
+                          scale, out.ctypes.data, lse.ctypes.data)
     return (out, lse) if with_lse else out
 
 
-def diff_rows(q1, k1, q2, k2, v, window, stride, scale, lam, rows):
+def diff_rows(q1, k1, q2, k2, v, window, stride, scale, lam, rows, dilation=1, n_global=0):
     """Differential attention for selected flat rows: out [len(rows), dv]."""
     q1, q1p = _f32(q1)
     k1, k1p = _f32(k1)
@@ -190,14 +193,15 @@ def diff_rows(q1, k1, q2, k2, v, window, stride, scale, lam, rows):
     Hkv, dv = k1.shape[1], v.shape[3]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((len(rows), dv), dtype=np.float64)
-    _load().orc_diff_rows(q1p, k1p, q2p, k2p, vp, B, Hq, Hkv, N, d, dv, window, stride, scale,
-                          lam, rows.ctypes.data, len(rows), out.ctypes.data)
+    _load().orc_diff_rows(q1p, k1p, q2p, k2p, vp, B, Hq, Hkv, N, d, dv, window, stride, dilation,
+                          n_global, scale, lam, rows.ctypes.data, len(rows), out.ctypes.data)
     return out
 
 
-def diff_full(q1, k1, q2, k2, v, window, stride, scale, lam):
+def diff_full(q1, k1, q2, k2, v, window, stride, scale, lam, dilation=1, n_global=0):
     B, Hq, N, _ = q1.shape
-    out = diff_rows(q1, k1, q2, k2, v, window, stride, scale, lam, np.arange(B * Hq * N))
+    out = diff_rows(q1, k1, q2, k2, v, window, stride, scale, lam, np.arange(B * Hq * N),
+                    dilation=dilation, n_global=n_global)
     return out.reshape(B, Hq, N, -1)
 
 

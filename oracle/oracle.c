@@ -29,7 +29,9 @@
  *          attention map from another.
  *
  * Where the pages are silent or disagree, the reading taken is stated at the
- * function that depends on it: the window holds W keys (j in [i-W+1, i]),
+ * function that depends on it: the window holds W keys (j in [i-W+1, i];
+ * with dilation dil, the keys i, i-dil, ..., i-(W-1)*dil), global tokens are
+ * the first n_global positions and keep the causal order,
  * the stride is anchored at key 0, the ring slot of position p is p mod W,
  * query head h uses key/value head h / (Hq/Hkv), and differential attention
  * has no normalisation after the subtraction.
@@ -47,39 +49,52 @@
  * a window >= n therefore gives the full causal mask ([SSW] §3 causal case
  * M_ij = 1[j <= i]).  [VAR] strided_mask: start from the window mask, then
  * also open every stride-th key counting from key 0 up to i
- * (range(0, i + 1, stride)).  stride == 0 means no stride pattern. */
-int orc_allowed(int64_t i, int64_t j, int64_t n, int64_t window, int64_t stride)
+ * (range(0, i + 1, stride)).  stride == 0 means no stride pattern.
+ * [SSW] §3b Longformer, dilation: gaps inside the window, attending every
+ * dilation-th token, so the same budget of `window` keys reaches dilation
+ * times further back: keys i - m*dilation for m = 0 .. window-1
+ * (dilation == 1 is the plain window).  Global tokens: designated positions
+ * that attend to every position and are attended to by every position; here
+ * the first n_global positions, and -- this being causal attention -- only
+ * pairs with j <= i: row i < n_global opens every key j <= i, and key
+ * j < n_global is open to every row i >= j.  (Under the causal order the row
+ * half adds nothing: the keys j <= i < n_global of a global row are all
+ * global columns.  It is kept to state the definition as the page does.) */
+int orc_allowed(int64_t i, int64_t j, int64_t n, int64_t window, int64_t stride,
+                int64_t dilation, int64_t n_global)
 {
     if (i < 0 || i >= n || j < 0 || j >= n)
         return 0;
-    int64_t lo = i - window + 1;
-    if (lo < 0)
-        lo = 0;
-    if (j >= lo && j <= i)
+    int64_t dist = i - j;
+    if (dist >= 0 && dist % dilation == 0 && dist / dilation < window)
         return 1;
     if (stride > 0 && j <= i && j % stride == 0)
+        return 1;
+    if (n_global > 0 && j <= i && (j < n_global || i < n_global))
         return 1;
     return 0;
 }
 
 /* Dense 0/1 mask, row-major n x n (1 = attends).  [VAR] swa_mask/strided_mask
  * build the same matrix with 0.0 / NEG_INF entries. */
-void orc_mask_dense(int64_t n, int64_t window, int64_t stride, uint8_t *out)
+void orc_mask_dense(int64_t n, int64_t window, int64_t stride, int64_t dilation,
+                    int64_t n_global, uint8_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         for (int64_t j = 0; j < n; ++j)
-            out[i * n + j] = (uint8_t)orc_allowed(i, j, n, window, stride);
+            out[i * n + j] = (uint8_t)orc_allowed(i, j, n, window, stride, dilation, n_global);
 }
 
 /* [VAR] count_nonmasked(M): the number of attended cells, here per row and
  * in total, by visiting every cell. */
-int64_t orc_count_nonmasked(int64_t n, int64_t window, int64_t stride, int64_t *row_counts)
+int64_t orc_count_nonmasked(int64_t n, int64_t window, int64_t stride, int64_t dilation,
+                            int64_t n_global, int64_t *row_counts)
 {
     int64_t total = 0;
     for (int64_t i = 0; i < n; ++i) {
         int64_t c = 0;
         for (int64_t j = 0; j < n; ++j)
-            c += orc_allowed(i, j, n, window, stride);
+            c += orc_allowed(i, j, n, window, stride, dilation, n_global);
         if (row_counts)
             row_counts[i] = c;
         total += c;
@@ -96,34 +111,36 @@ int64_t orc_count_nonmasked(int64_t n, int64_t window, int64_t stride, int64_t *
  * qt*bm .. qt*bm+bm-1) and key tile kt (keys kt*bn .. kt*bn+bn-1), both
  * clipped at n, the cells of the tile are visited one by one:
  *   cells == 0                      -> tile not listed
- *   no cell is in the window part   -> kind 2 (stride-only)
+ *   no cell is in the band part     -> kind 2 (prefix-only)
  *   cells == in-range tile area     -> kind 0 (full)
  *   otherwise                       -> kind 1 (partial)
- * The window part of a cell is max(0, i-window+1) <= j <= i.
- * stride_keys[qt] counts the stride keys (multiples of stride) inside the
- * stride-only tiles of query tile qt.  band_begin[qt] is the list index of
- * the first tile of qt that is not stride-only.
+ * The band part of a cell is j <= i with i - j <= (window-1)*dilation (the
+ * span of the window).  The other attended cells are "prefix keys":
+ * multiples of stride, or global columns j < n_global (which also cover the
+ * keys of the global rows, see orc_allowed).
+ * prefix_keys[qt] counts the prefix keys inside the prefix-only tiles of
+ * query tile qt.  band_begin[qt] is the list index of the first tile of qt
+ * that is not prefix-only.
  * Returns nnz, or -1 if the list would exceed cap entries. */
-int64_t orc_tile_list(int64_t n, int64_t window, int64_t stride, int64_t bm, int64_t bn,
-                      int32_t *row_ptr, int32_t *kv_tile, uint8_t *kind, int32_t *cells,
-                      int32_t *stride_keys, int32_t *band_begin, int64_t cap)
+int64_t orc_tile_list(int64_t n, int64_t window, int64_t stride, int64_t dilation,
+                      int64_t n_global, int64_t bm, int64_t bn, int32_t *row_ptr,
+                      int32_t *kv_tile, uint8_t *kind, int32_t *cells, int32_t *prefix_keys,
+                      int32_t *band_begin, int64_t cap)
 {
     int64_t nq = (n + bm - 1) / bm, nk = (n + bn - 1) / bn, nnz = 0;
+    int64_t span = (window - 1) * dilation;
     for (int64_t qt = 0; qt < nq; ++qt) {
         row_ptr[qt] = (int32_t)nnz;
-        stride_keys[qt] = 0;
+        prefix_keys[qt] = 0;
         band_begin[qt] = -1;
         int64_t i0 = qt * bm, i1 = i0 + bm < n ? i0 + bm : n;
         for (int64_t kt = 0; kt < nk; ++kt) {
             int64_t j0 = kt * bn, j1 = j0 + bn < n ? j0 + bn : n;
             int64_t c = 0, band = 0;
             for (int64_t i = i0; i < i1; ++i) {
-                int64_t lo = i - window + 1;
-                if (lo < 0)
-                    lo = 0;
                 for (int64_t j = j0; j < j1; ++j) {
-                    c += orc_allowed(i, j, n, window, stride);
-                    band += (j >= lo && j <= i);
+                    c += orc_allowed(i, j, n, window, stride, dilation, n_global);
+                    band += (j <= i && i - j <= span);
                 }
             }
             if (c == 0)
@@ -139,7 +156,7 @@ int64_t orc_tile_list(int64_t n, int64_t window, int64_t stride, int64_t bm, int
                 k = 1;
             if (k == 2) {
                 for (int64_t j = j0; j < j1; ++j)
-                    stride_keys[qt] += (stride > 0 && j % stride == 0);
+                    prefix_keys[qt] += (j < n_global || (stride > 0 && j % stride == 0));
             } else if (band_begin[qt] < 0) {
                 band_begin[qt] = (int32_t)nnz;
             }
@@ -257,8 +274,8 @@ void orc_tiled_softmax_dot(const float *q, const float *K, const float *V, int64
  * out is [nrows, dv]; lse (nullable) is [nrows]. */
 void orc_attn_rows(const float *q, const float *k, const float *v, int64_t B, int64_t Hq,
                    int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t window,
-                   int64_t stride, double scale, const int64_t *rows, int64_t nrows,
-                   double *out, double *lse)
+                   int64_t stride, int64_t dilation, int64_t n_global, double scale,
+                   const int64_t *rows, int64_t nrows, double *out, double *lse)
 {
     int64_t G = Hq / Hkv;
     uint8_t *mrow = (uint8_t *)malloc((size_t)(N > 0 ? N : 1));
@@ -273,7 +290,7 @@ void orc_attn_rows(const float *q, const float *k, const float *v, int64_t B, in
         }
         int64_t i = flat % N, bh = flat / N, h = bh % Hq, b = bh / Hq, g = h / G;
         for (int64_t j = 0; j < N; ++j)
-            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride);
+            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride, dilation, n_global);
         const float *qi = q + ((b * Hq + h) * N + i) * d;
         const float *kg = k + (b * Hkv + g) * N * d;
         const float *vg = v + (b * Hkv + g) * N * dv;
@@ -287,13 +304,14 @@ void orc_attn_rows(const float *q, const float *k, const float *v, int64_t B, in
 /* All rows of orc_attn_rows; out is [B, Hq, N, dv]. */
 void orc_attn_full(const float *q, const float *k, const float *v, int64_t B, int64_t Hq,
                    int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t window, int64_t stride,
-                   double scale, double *out, double *lse)
+                   int64_t dilation, int64_t n_global, double scale, double *out, double *lse)
 {
     int64_t total = B * Hq * N;
     int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(total > 0 ? total : 1));
     for (int64_t r = 0; r < total; ++r)
         rows[r] = r;
-    orc_attn_rows(q, k, v, B, Hq, Hkv, N, d, dv, window, stride, scale, rows, total, out, lse);
+    orc_attn_rows(q, k, v, B, Hq, Hkv, N, d, dv, window, stride, dilation, n_global, scale, rows,
+                  total, out, lse);
     free(rows);
 }
 
@@ -306,8 +324,9 @@ void orc_attn_full(const float *q, const float *k, const float *v, int64_t B, in
  * q1, q2 are [B, Hq, N, d]; k1, k2 are [B, Hkv, N, d]; v is [B, Hkv, N, dv]. */
 void orc_diff_rows(const float *q1, const float *k1, const float *q2, const float *k2,
                    const float *v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                   int64_t dv, int64_t window, int64_t stride, double scale, double lambda,
-                   const int64_t *rows, int64_t nrows, double *out)
+                   int64_t dv, int64_t window, int64_t stride, int64_t dilation,
+                   int64_t n_global, double scale, double lambda, const int64_t *rows,
+                   int64_t nrows, double *out)
 {
     int64_t G = Hq / Hkv;
     uint8_t *mrow = (uint8_t *)malloc((size_t)(N > 0 ? N : 1));
@@ -323,7 +342,7 @@ void orc_diff_rows(const float *q1, const float *k1, const float *q2, const floa
         }
         int64_t i = flat % N, bh = flat / N, h = bh % Hq, b = bh / Hq, g = h / G;
         for (int64_t j = 0; j < N; ++j)
-            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride);
+            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride, dilation, n_global);
         const float *vg = v + (b * Hkv + g) * N * dv;
         orc_attention_row(q1 + ((b * Hq + h) * N + i) * d, k1 + (b * Hkv + g) * N * d, vg, mrow,
                           N, d, dv, d, dv, scale, tmp, w1);

@@ -17,12 +17,22 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 MUTATIONS = {
-    "window_holds_w_plus_1_keys": ("int64_t lo = i - window + 1;\n    if (lo < 0)\n        lo = 0;\n    if (j >= lo",
-                                   "int64_t lo = i - window;\n    if (lo < 0)\n        lo = 0;\n    if (j >= lo"),
+    "window_holds_w_plus_1_keys": ("dist % dilation == 0 && dist / dilation < window",
+                                   "dist % dilation == 0 && dist / dilation <= window"),
     "stride_relative_to_query": ("stride > 0 && j <= i && j % stride == 0", "stride > 0 && j <= i && (i - j) % stride == 0"),
     "stride_ignores_causality": ("stride > 0 && j <= i && j % stride == 0", "stride > 0 && j % stride == 0"),
-    "gqa_interleaved_heads": ("h = bh % Hq, b = bh / Hq, g = h / G;\n        for (int64_t j = 0; j < N; ++j)\n            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride);\n        const float *qi",
-                              "h = bh % Hq, b = bh / Hq, g = h % Hkv;\n        for (int64_t j = 0; j < N; ++j)\n            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride);\n        const float *qi"),
+    "dilation_ignored": ("dist >= 0 && dist % dilation == 0 && dist / dilation < window",
+                         "dist >= 0 && dist < window"),
+    "dilation_span_not_stretched": ("dist >= 0 && dist % dilation == 0 && dist / dilation < window",
+                                    "dist >= 0 && dist % dilation == 0 && dist < window"),
+    "global_columns_dropped": ("(j < n_global || i < n_global)", "(i < n_global)"),
+    "global_ignores_causality": ("n_global > 0 && j <= i && (", "n_global > 0 && ("),
+    "tile_band_not_stretched_by_dilation": ("band += (j <= i && i - j <= span);",
+                                            "band += (j <= i && i - j < window);"),
+    "prefix_keys_miss_globals": ("prefix_keys[qt] += (j < n_global || (stride > 0 && j % stride == 0));",
+                                 "prefix_keys[qt] += (stride > 0 && j % stride == 0);"),
+    "gqa_interleaved_heads": ("h = bh % Hq, b = bh / Hq, g = h / G;\n        for (int64_t j = 0; j < N; ++j)\n            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride, dilation, n_global);\n        const float *qi",
+                              "h = bh % Hq, b = bh / Hq, g = h % Hkv;\n        for (int64_t j = 0; j < N; ++j)\n            mrow[j] = (uint8_t)orc_allowed(i, j, N, window, stride, dilation, n_global);\n        const float *qi"),
     "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
     "no_max_subtraction": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
     "value_transposed": ("out[c] += w * (double)V[j * v_stride + c];", "out[c] += w * (double)V[c * v_stride + j];"),
@@ -44,8 +54,16 @@ def all_pins():
         ("band_closed", lambda: pins.test_band_count_closed_form(33)),
         ("local_stride_closed", pins.test_local_stride_closed_form),
         ("tile_hand", lambda: pins.test_tile_list_hand_worked(GOLDEN)),
-        ("tile_blocks", lambda: pins.test_tile_list_against_block_sums(64, 16, 7, 16, 8)),
-        ("tile_blocks_full", lambda: pins.test_tile_list_against_block_sums(50, 50, 0, 16, 16)),
+        ("tile_blocks", lambda: pins.test_tile_list_against_block_sums(64, 16, 7, 16, 8, 1, 0)),
+        ("tile_blocks_full", lambda: pins.test_tile_list_against_block_sums(50, 50, 0, 16, 16, 1, 0)),
+        ("tile_blocks_dil_global", lambda: pins.test_tile_list_against_block_sums(70, 5, 4, 16, 8, 2, 11)),
+        ("tile_blocks_dilated", lambda: pins.test_tile_list_against_block_sums(90, 6, 5, 8, 8, 8, 0)),
+        ("tile_blocks_global_rows", lambda: pins.test_tile_list_against_block_sums(90, 7, 9, 8, 8, 1, 20)),
+        ("dilated_counts", pins.test_dilated_row_counts_closed_form),
+        ("dilated_residues", lambda: pins.test_dilated_window_is_plain_window_on_residue_classes(30, 4, 3)),
+        ("global_gather", lambda: pins.test_global_tokens_by_key_gather(30, 5, 9, 0)),
+        ("global_counts", pins.test_global_count_closed_form),
+        ("global_vs_sinks", lambda: pins.test_global_prefill_row_is_sink_decode(40, 8, 4)),
         ("attn_sdpa", lambda: pins.test_attention_matches_sdpa_with_pinned_mask(2, 4, 2, 33, 16, 8, 5, 4)),
         ("causal_sdpa", lambda: pins.test_window_ge_n_reduces_to_causal_sdpa(17, 17)),
         ("peaky", pins.test_peaky_scores_need_max_subtraction),

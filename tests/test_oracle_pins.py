@@ -162,7 +162,7 @@ def test_tile_list_hand_worked(golden_dir):
         a, b = t["row_ptr"][qt], t["row_ptr"][qt + 1]
         got = list(zip(t["kv_tile"][a:b].tolist(), t["kind"][a:b].tolist(), t["cells"][a:b].tolist()))
         assert got == entries, qt
-        assert t["stride_keys"][qt] == sk
+        assert t["prefix_keys"][qt] == sk
 
 
 def block_sums(mask, bm, bn):
@@ -173,20 +173,25 @@ def block_sums(mask, bm, bn):
     return pad.reshape(nq, bm, nk, bn).sum(axis=(1, 3))
 
 
-@pytest.mark.parametrize("n,w,s,bm,bn", [
-    (37, 5, 0, 8, 8), (37, 5, 3, 8, 4), (64, 16, 7, 16, 8), (50, 50, 0, 16, 16),
-    (50, 1, 0, 4, 8), (70, 9, 1, 8, 8), (129, 20, 11, 32, 16), (100, 300, 6, 16, 32)])
-def test_tile_list_against_block_sums(n, w, s, bm, bn):
+@pytest.mark.parametrize("n,w,s,bm,bn,dil,g", [
+    (37, 5, 0, 8, 8, 1, 0), (37, 5, 3, 8, 4, 1, 0), (64, 16, 7, 16, 8, 1, 0), (50, 50, 0, 16, 16, 1, 0),
+    (50, 1, 0, 4, 8, 1, 0), (70, 9, 1, 8, 8, 1, 0), (129, 20, 11, 32, 16, 1, 0),
+    (100, 300, 6, 16, 32, 1, 0),
+    (90, 6, 0, 16, 8, 3, 0), (90, 6, 5, 8, 8, 8, 0), (77, 4, 0, 16, 16, 16, 0),
+    (90, 7, 0, 16, 8, 1, 3), (90, 7, 9, 8, 8, 1, 20), (70, 5, 4, 16, 8, 2, 11),
+    (40, 3, 0, 8, 8, 1, 40)])
+def test_tile_list_against_block_sums(n, w, s, bm, bn, dil, g):
     """Per-tile cell counts equal numpy block sums of the (pinned) dense mask;
-    the kinds follow from the window/stride split of each block; the window
-    tiles of a query tile are one contiguous range with every stride-only tile
-    left of it; stride_keys counts the multiples of s below that range."""
-    mask = oracle.mask_dense(n, w, s)
+    the kinds follow from the band/prefix split of each block; the band tiles
+    of a query tile are one contiguous range (for dilation <= bn) with every
+    prefix-only tile left of it; prefix_keys counts the multiples of s and
+    the global columns below that range."""
+    mask = oracle.mask_dense(n, w, s, dil, g)
     ii, jj = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
-    band = ((jj <= ii) & (jj >= ii - w + 1)).astype(np.int64)
+    band = ((jj <= ii) & (ii - jj <= (w - 1) * dil)).astype(np.int64)
     sums = block_sums(mask, bm, bn)
     bsums = block_sums(band, bm, bn)
-    t = oracle.tile_list(n, w, s, bm, bn)
+    t = oracle.tile_list(n, w, s, bm, bn, dilation=dil, n_global=g)
     nq, nk = sums.shape
     assert t["nnz"] == int((sums > 0).sum())
     assert int(t["cells"].sum()) == int(mask.sum())
@@ -208,8 +213,8 @@ def test_tile_list_against_block_sums(n, w, s, bm, bn):
         assert np.all(kinds[: band_idx[0]] == 2) and np.all(kinds[band_idx[0]:] != 2)
         assert t["band_begin"][qt] == a + band_idx[0]
         lo_key = tiles[band_idx[0]] * bn
-        want_sk = len(range(0, lo_key, s)) if s > 0 else 0
-        assert t["stride_keys"][qt] == want_sk
+        want_pk = len([j for j in range(lo_key) if j < g or (s > 0 and j % s == 0)])
+        assert t["prefix_keys"][qt] == want_pk
 
 
 def test_stride_only_tiles_attended_by_every_row():
@@ -343,6 +348,100 @@ def test_diff_special_cases():
                                rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(oracle.diff_full(q1, k1, q1, k1, v, w, 0, 0.3, 0.5), 0.5 * single,
                                rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Longformer: dilated window and global tokens
+# --------------------------------------------------------------------------
+
+def test_dilated_row_counts_closed_form():
+    # "Learn: Sparse & Sliding-Window Attention" §3b: every dil-th key, the
+    # same budget of w keys: row i attends min(w, floor(i/dil) + 1) keys
+    for n in (1, 7, 40):
+        for w in (1, 3, 8):
+            for dil in (1, 2, 3, 7):
+                total, rows = oracle.count_nonmasked(n, w, 0, dil, 0)
+                want = [min(w, i // dil + 1) for i in range(n)]
+                np.testing.assert_array_equal(rows, want, err_msg=str((n, w, dil)))
+                assert total == sum(want)
+
+
+@pytest.mark.parametrize("N,w,dil", [(30, 4, 3), (41, 6, 2), (25, 30, 4), (33, 1, 5)])
+def test_dilated_window_is_plain_window_on_residue_classes(N, w, dil):
+    # rows i = r (mod dil) attend keys of the same residue class only, the w
+    # nearest: a plain window of w on the subsequence r, r+dil, r+2dil, ...
+    q, k, v = rand((1, 4, N, 8), 80), rand((1, 2, N, 8), 81), rand((1, 2, N, 8), 82)
+    got = oracle.attn_full(q, k, v, w, 0, 0.4, dilation=dil)
+    for r in range(dil):
+        qs, ks, vs = q[:, :, r::dil], k[:, :, r::dil], v[:, :, r::dil]
+        n = qs.shape[2]
+        band = np.tril(np.ones((n, n), dtype=np.uint8)) - np.tril(np.ones((n, n), dtype=np.uint8), -w)
+        want = sdpa64(qs, ks, vs, 0.4, mask=band)
+        np.testing.assert_allclose(got[:, :, r::dil], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,w,g,s", [(30, 5, 3, 0), (30, 5, 9, 0), (40, 6, 2, 7), (20, 3, 20, 0),
+                                     (26, 4, 1, 0)])
+def test_global_tokens_by_key_gather(N, w, g, s):
+    # §3b global tokens under the causal order: row i < g attends every j <= i;
+    # every other row attends the global keys j < g, its window, and (with a
+    # stride) the multiples of s -- checked row by row against SDPA over the
+    # explicitly gathered key set
+    B, Hq, Hkv, d = 1, 2, 1, 8
+    q, k, v = rand((B, Hq, N, d), 83), rand((B, Hkv, N, d), 84), rand((B, Hkv, N, d), 85)
+    got = oracle.attn_full(q, k, v, w, s, 0.3, n_global=g)
+    for i in range(N):
+        if i < g:
+            keep = list(range(i + 1))
+        else:
+            keep = sorted(set(range(g)) | set(range(max(0, i - w + 1), i + 1)) |
+                          (set(range(0, i + 1, s)) if s else set()))
+        want = sdpa64(q[:, :, i:i + 1], k[:, :, keep], v[:, :, keep], 0.3)[:, :, 0]
+        np.testing.assert_allclose(got[:, :, i], want, rtol=1e-12, atol=1e-12)
+
+
+def test_global_count_closed_form():
+    # g <= w: the global rows lie inside their own windows, and key j < g adds
+    # the rows i >= j + w that the window does not reach: N - j - w of them
+    for n in (5, 20, 64):
+        for w in (1, 4, 9):
+            for g in range(0, w + 1):
+                total, _ = oracle.count_nonmasked(n, w, 0, 1, g)
+                want = band_count(n, w) + sum(max(0, n - j - w) for j in range(g))
+                assert total == want, (n, w, g)
+    # g >= n: the full causal triangle
+    assert oracle.count_nonmasked(12, 2, 0, 1, 12)[0] == 12 * 13 // 2
+
+
+@pytest.mark.parametrize("L,W,S", [(40, 8, 4), (9, 8, 4), (30, 16, 2)])
+def test_global_prefill_row_is_sink_decode(L, W, S):
+    # the newest row of a prefill with S global tokens attends the same keys
+    # as a decode step with S sink slots and a ring of W ("Learn: Sparse &
+    # Sliding-Window Attention" §4): two separate paths of the oracle
+    B, Hq, Hkv, d = 1, 4, 2, 8
+    kseq, vseq = rand((B, Hkv, L, d), 86), rand((B, Hkv, L, d), 87)
+    qseq = rand((B, Hq, L, d), 88)
+    rows = [(b * Hq + h) * L + L - 1 for b in range(B) for h in range(Hq)]
+    pre = oracle.attn_rows(qseq, kseq, vseq, W, 0, 0.4, rows, n_global=S)
+    kr, vr = ring_from_sequence(kseq, vseq, L, W)
+    got = oracle.decode(qseq[:, :, L - 1], kr, vr, [L], 0.4, k_sink=kseq[:, :, :S].copy(),
+                        v_sink=vseq[:, :, :S].copy())
+    np.testing.assert_allclose(got.reshape(-1, d), pre, rtol=1e-12, atol=1e-12)
+
+
+def test_prefix_only_tiles_attended_by_every_row():
+    # stride and global columns in a prefix-only tile are open in every row
+    n, w, s, g, dil, bm, bn = 120, 6, 13, 5, 2, 16, 8
+    mask = oracle.mask_dense(n, w, s, dil, g)
+    t = oracle.tile_list(n, w, s, bm, bn, dilation=dil, n_global=g)
+    for qt in range(t["num_q_tiles"]):
+        for e in range(t["row_ptr"][qt], t["row_ptr"][qt + 1]):
+            if t["kind"][e] != 2:
+                continue
+            kt = t["kv_tile"][e]
+            cols = [j for j in range(kt * bn, min(n, (kt + 1) * bn)) if j < g or j % s == 0]
+            rows = range(qt * bm, min(n, (qt + 1) * bm))
+            assert cols and all(mask[i, j] for i in rows for j in cols)
 
 
 # --------------------------------------------------------------------------
