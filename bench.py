@@ -15,6 +15,8 @@ The same run also measures, each on its own seeded synthetic inputs:
   diff_decode  differential decode, 32 sequences x ring 4096, H=16, d=64 per
              map, dv=128 (both K rings and the one V ring, each read once)
   strided    local+strided prefill, B=2, H=16, N=16384, d=64, W=256, s=128
+  global     the prefill workload plus 64 global tokens (Longformer)
+  dilated    the prefill workload with 512 window keys at dilation 2
   diff       differential attention, B=1, H=16, N=4096, d=64/dv=128, W=1024
   tiny_f32   the small fp32 window problem (latency only)
   mask_build block-mask build for the prefill workload
@@ -56,6 +58,20 @@ def band_cells(n, w):
 def cells_of(cfg):
     """Attended cells per (batch, head) from the closed forms of the mask."""
     n, w, s = cfg["N"], cfg["window"], cfg["stride"]
+    dil, g = cfg.get("dilation", 1), cfg.get("n_global", 0)
+    if dil > 1 or g > 0:
+        # per row: the (dilated) window holds min(w, i // dil + 1) keys; the
+        # global columns add the keys j < g left of the window span
+        if s:
+            raise ValueError("no closed form here for a stride with dilation or global tokens")
+        i = np.arange(n, dtype=np.int64)
+        span = (w - 1) * dil
+        c = np.minimum(w, i // dil + 1)
+        if g > 0:
+            if dil > 1:
+                raise ValueError("no closed form here for dilation with global tokens")
+            c = c + np.maximum(0, np.minimum(g, i - span))
+        return int(c.sum())
     c = band_cells(n, w)
     if s > 0 and w < n:
         t = n - w
@@ -151,8 +167,8 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="minimum warm-up time per workload (0 for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "sink_decode", "diff_decode", "strided", "diff",
-                                       "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "sink_decode", "diff_decode", "strided",
+                                       "global", "dilated", "diff", "copy"], default=None,
                     help="time one workload only (for profiler runs); `copy` times a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -287,6 +303,26 @@ def main():
                               gbs=sbytes / (ev_ms * 1e-3) / 1e9, alg_flops=sflops, alg_bytes=sbytes)
         del sqd, skd, svd, sout
 
+    # ---- Longformer patterns: global tokens, dilated window ----------------------
+    for key, wl in (("global", "global_prefill_bf16"), ("dilated", "dilated_prefill_bf16")):
+        if args.only not in (None, key):
+            continue
+        xcfg = synth.workload(wl)
+        xq, xk, xv = synth.prefill_inputs(xcfg)
+        xqd, xkd, xvd = dev(xq, torch, bf16), dev(xk, torch, bf16), dev(xv, torch, bf16)
+        del xq, xk, xv
+        xmask = swa.swa_block_mask_build(xcfg["N"], xcfg["window"], 0, d=xcfg["d"],
+                                         dilation=xcfg.get("dilation", 1),
+                                         n_global=xcfg.get("n_global", 0))
+        xout = torch.empty_like(xqd)
+        fn = lambda i: swa.swa_attn_fwd(xqd, xkd, xvd, xcfg["window"], 0, xcfg["scale"], xmask, out=xout)
+        log(f"{wl}")
+        wall_ms, ev_ms = timed(fn, K, W, torch)
+        xcells = cells_of(xcfg) * xcfg["B"] * xcfg["Hq"]
+        res[key] = dict(event_ms=ev_ms, tflops=4.0 * xcfg["d"] * xcells / (ev_ms * 1e-3) / 1e12,
+                        workload=wl)
+        del xqd, xkd, xvd, xout
+
     # ---- differential attention ------------------------------------------------
     if args.only in (None, "diff"):
         fcfg = synth.workload("diff_bf16")
@@ -376,6 +412,12 @@ def main():
                            "gbs": round(s["gbs"], 1), "us": round(s["event_ms"] * 1e3, 2),
                            "roofline_frac": round(max(t_hbm, t_mfma) / (s["event_ms"] * 1e-3), 4),
                            "bound": "hbm" if t_hbm > t_mfma else "mfma"}
+    for key in ("global", "dilated"):
+        if key in res:
+            x = res[key]
+            line[key] = {"workload": x["workload"], "tflops": round(x["tflops"], 2),
+                         "us": round(x["event_ms"] * 1e3, 2), "bound": "mfma",
+                         "roofline_frac": round(x["tflops"] / PEAK_BF16_TFLOPS, 4)}
     if "diff" in res:
         f = res["diff"]
         line["diff"] = {"workload": "diff_bf16", "tflops": round(f["tflops"], 2),

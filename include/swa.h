@@ -5,12 +5,20 @@
  *
  *     A = softmax(Q K^T * scale + log M) V,   log M_ij in {0, -inf}
  *
- * with the mask M_ij = 1 iff  0 <= j <= i < N  and either
- *   (window)  i - window + 1 <= j            -- swa_mask(n, window) of
- *             "Attention Variants Compared"; exactly `window` keys per row
- *             once i >= window - 1, and window >= N gives full causal;
- *   (stride)  stride > 0 and j mod stride == 0  -- strided_mask(n, window,
- *             stride) of the same page, anchored at key 0.
+ * with the mask M_ij = 1 iff  0 <= j <= i < N  and at least one of
+ *   (window)  (i - j) mod dilation == 0 and (i - j) / dilation < window:
+ *             the `window` keys i, i - dilation, ..., i - (window-1)*dilation.
+ *             dilation = 1 is swa_mask(n, window) of "Attention Variants
+ *             Compared" (exactly `window` keys per row once i >= window-1;
+ *             window >= N gives full causal); dilation > 1 is Longformer's
+ *             dilated window (Learn: Sparse & Sliding-Window Attention, §3b).
+ *   (stride)  stride > 0 and j mod stride == 0 -- strided_mask(n, window,
+ *             stride) of "Attention Variants Compared", anchored at key 0.
+ *   (global)  j < n_global or i < n_global -- Longformer's global tokens
+ *             (same page, §3b), here the first n_global positions, kept
+ *             causal.  Since j <= i, a global row's keys are all global
+ *             columns: the global tokens act as key columns every later row
+ *             attends.
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte
@@ -66,33 +74,39 @@ typedef enum { SWA_OP_ATTN = 0, SWA_OP_DIFF = 1 } swa_op_t;
  * create_block_mask builds the per-block keep/skip map once, blocks with no
  * attended cell are skipped; it is then handed to the attention call).
  * Stored as a CSR over query tiles; within a query tile the key tiles are
- * ascending.  The mask depends only on (N, window, stride, bm, bn) and is
- * shared by every batch and head.
+ * ascending.  The mask depends only on (N, window, stride, dilation,
+ * n_global, bm, bn) and is shared by every batch and head.
+ *
+ * The "band" of query tile q is the key range max(0, r0 - (window-1) *
+ * dilation) .. r1 (r0, r1 its first and last row); every key left of the
+ * band that is a multiple of stride or a global column (a "prefix key") is
+ * attended by every row of the tile.
  *
  *   row_ptr[num_q_tiles + 1]   list of query tile q is [row_ptr[q], row_ptr[q+1])
  *   kv_tile[nnz]               key tile index
  *   kind[nnz]                  0 FULL: every in-range cell attends
  *                              1 PARTIAL: some cells attend (mask applied per cell)
- *                              2 STRIDE_ONLY: no cell lies in the window part;
- *                                only stride keys attend, and they attend
- *                                from every row of the query tile
+ *                              2 PREFIX_ONLY: the tile lies left of the band;
+ *                                only its prefix keys attend, from every row
  *   cells[nnz]                 attended cells of the tile (rows, keys < N)
- *   stride_keys[num_q_tiles]   stride keys inside the STRIDE_ONLY tiles of q;
- *                              they are keys 0, stride, 2*stride, ... in order
- *   band_begin[num_q_tiles]    index of the first non-STRIDE_ONLY entry of q
- *                              (STRIDE_ONLY entries come first)
+ *   prefix_keys[num_q_tiles]   prefix keys inside the PREFIX_ONLY tiles of q;
+ *                              in order they are 0 .. g'-1 (g' = min(n_global,
+ *                              prefix_keys[q])), then the multiples of stride
+ *                              from g' on
+ *   band_begin[num_q_tiles]    index of the first non-PREFIX_ONLY entry of q
+ *                              (PREFIX_ONLY entries come first)
  *
  * The caller allocates the five device arrays with the sizes that
  * swa_block_mask_query returns and fills the scalar fields.
  */
 typedef struct {
-    int32_t N, window, stride, bm, bn;
+    int32_t N, window, stride, dilation, n_global, bm, bn;
     int32_t num_q_tiles, nnz;
     int32_t *row_ptr;
     int32_t *kv_tile;
     uint8_t *kind;
     int32_t *cells;
-    int32_t *stride_keys;
+    int32_t *prefix_keys;
     int32_t *band_begin;
 } swa_block_mask_t;
 
@@ -103,10 +117,11 @@ typedef struct {
 int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn);
 
 /* Number of query tiles and list entries of the block mask of
- * (N, window, stride, bm, bn).  Host only, no HIP call.
+ * (N, window, stride, dilation, n_global, bm, bn).  Host only, no HIP call.
  * N in [1, SWA_MAX_N], window >= 1, stride >= 0 (0 = no stride pattern),
- * bm, bn in {16, 32, 64, 128, 256}. */
-int swa_block_mask_query(int N, int window, int stride, int bm, int bn,
+ * dilation in [1, bn] (so every tile of a band holds an attended cell),
+ * n_global in [0, SWA_MAX_N], bm, bn in {16, 32, 64, 128, 256}. */
+int swa_block_mask_query(int N, int window, int stride, int dilation, int n_global, int bm, int bn,
                          int32_t *num_q_tiles, int32_t *nnz);
 
 /* Fill the device arrays of *mask on `stream` from its scalar fields, which
@@ -116,7 +131,8 @@ int swa_block_mask_build(const swa_block_mask_t *mask, hipStream_t stream);
 
 /* Debug export of the dense mask: out[i*N + j] = 1 if query i attends key j,
  * else 0, for N <= 16384 (device array of N*N bytes). */
-int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream);
+int swa_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
+                   hipStream_t stream);
 
 /*
  * Masked attention forward (prefill) -- the §3 equation above over the block
@@ -126,14 +142,15 @@ int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stre
  *   lse            nullable; fp32 [B, Hq, N] natural-log sum of
  *                  exp(score * scale) over the attended keys
  *   d in {32, 64, 128} for SWA_BF16 and SWA_F32
- *   mask           built for (N, window, stride) and the tiles of
- *                  swa_tile_config(SWA_OP_ATTN, dt, d, d)
+ *   mask           built for (N, window, stride, dilation, n_global) and the
+ *                  tiles of swa_tile_config(SWA_OP_ATTN, dt, d, d)
  * Arithmetic: bf16 inputs, fp32 accumulation, output rounded to bf16
  * (SWA_BF16) or kept fp32 (SWA_F32).
  */
 int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                  swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
-                 float scale, const swa_block_mask_t *mask, hipStream_t stream);
+                 int dilation, int n_global, float scale, const swa_block_mask_t *mask,
+                 hipStream_t stream);
 
 /* Bytes of device workspace a decode call needs: op SWA_OP_ATTN for
  * swa_attn_decode and swa_attn_decode_sinks (dv = d), SWA_OP_DIFF for
@@ -218,13 +235,13 @@ int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const 
  *   q1, q2     [B, Hq, N, d]      k1, k2  [B, Hkv, N, d]
  *   v          [B, Hkv, N, dv]    out     [B, Hq, N, dv]
  *   d in {32, 64, 128}, dv in {32, 64, 128}; no normalisation follows the
- *   subtraction.  mask: built for the tiles of
- *   swa_tile_config(SWA_OP_DIFF, dt, d, dv).
+ *   subtraction.  mask: built for (N, window, stride, dilation, n_global)
+ *   and the tiles of swa_tile_config(SWA_OP_DIFF, dt, d, dv).
  */
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2,
                   const void *v, void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N,
-                  int d, int dv, int window, int stride, float scale, float lambda,
-                  const swa_block_mask_t *mask, hipStream_t stream);
+                  int d, int dv, int window, int stride, int dilation, int n_global, float scale,
+                  float lambda, const swa_block_mask_t *mask, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *swa_strerror(int status);

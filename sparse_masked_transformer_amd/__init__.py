@@ -33,22 +33,23 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 
 class swa_block_mask_t(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("window", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("dilation", ctypes.c_int32), ("n_global", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
                 ("num_q_tiles", ctypes.c_int32), ("nnz", ctypes.c_int32),
                 ("row_ptr", _p), ("kv_tile", _p), ("kind", _p), ("cells", _p),
-                ("stride_keys", _p), ("band_begin", _p)]
+                ("prefix_keys", _p), ("band_begin", _p)]
 
 
 _lib.swa_tile_config.restype = _i
 _lib.swa_tile_config.argtypes = [_i, _i, _i, _i, _i32p, _i32p]
 _lib.swa_block_mask_query.restype = _i
-_lib.swa_block_mask_query.argtypes = [_i, _i, _i, _i, _i, _i32p, _i32p]
+_lib.swa_block_mask_query.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i32p, _i32p]
 _lib.swa_block_mask_build.restype = _i
 _lib.swa_block_mask_build.argtypes = [ctypes.POINTER(swa_block_mask_t), _p]
 _lib.swa_mask_dense.restype = _i
-_lib.swa_mask_dense.argtypes = [_i, _i, _i, _p, _p]
+_lib.swa_mask_dense.argtypes = [_i, _i, _i, _i, _i, _p, _p]
 _lib.swa_attn_fwd.restype = _i
-_lib.swa_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+_lib.swa_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                               ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
 _lib.swa_attn_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.swa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
@@ -62,7 +63,7 @@ _lib.diff_attn_decode.restype = _i
 _lib.diff_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i,
                                   _i, _i, _i, _i, ctypes.c_float, ctypes.c_float, _p]
 _lib.diff_attn_fwd.restype = _i
-_lib.diff_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+_lib.diff_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                ctypes.c_float, ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
 _lib.swa_strerror.restype = ctypes.c_char_p
 _lib.swa_strerror.argtypes = [_i]
@@ -115,63 +116,68 @@ def swa_tile_config(dtype, d, dv=None, op=SWA_OP_ATTN):
     return bm.value, bn.value
 
 
-def swa_block_mask_query(N, window, stride, bm, bn):
-    """(num_q_tiles, nnz) of the block mask of (N, window, stride, bm, bn)."""
+def swa_block_mask_query(N, window, stride, bm, bn, dilation=1, n_global=0):
+    """(num_q_tiles, nnz) of the block mask of (N, window, stride, dilation,
+    n_global, bm, bn)."""
     nq, nnz = ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.swa_block_mask_query(N, window, stride, bm, bn, ctypes.byref(nq), ctypes.byref(nnz)),
-           "swa_block_mask_query")
+    _check(_lib.swa_block_mask_query(N, window, stride, dilation, n_global, bm, bn, ctypes.byref(nq),
+                                     ctypes.byref(nnz)), "swa_block_mask_query")
     return nq.value, nnz.value
 
 
 class BlockMask:
     """Device block mask (CSR over query tiles) plus its C struct."""
 
-    def __init__(self, N, window, stride, bm, bn, device):
-        nq, nnz = swa_block_mask_query(N, window, stride, bm, bn)
+    def __init__(self, N, window, stride, bm, bn, device, dilation=1, n_global=0):
+        nq, nnz = swa_block_mask_query(N, window, stride, bm, bn, dilation, n_global)
         i32 = dict(dtype=torch.int32, device=device)
         self.row_ptr = torch.empty(nq + 1, **i32)
         self.kv_tile = torch.empty(max(nnz, 1), **i32)
         self.kind = torch.empty(max(nnz, 1), dtype=torch.uint8, device=device)
         self.cells = torch.empty(max(nnz, 1), **i32)
-        self.stride_keys = torch.empty(nq, **i32)
+        self.prefix_keys = torch.empty(nq, **i32)
         self.band_begin = torch.empty(nq, **i32)
         self.N, self.window, self.stride, self.bm, self.bn = N, window, stride, bm, bn
+        self.dilation, self.n_global = dilation, n_global
         self.num_q_tiles, self.nnz = nq, nnz
-        self.c = swa_block_mask_t(N, window, stride, bm, bn, nq, nnz,
+        self.c = swa_block_mask_t(N, window, stride, dilation, n_global, bm, bn, nq, nnz,
                                   self.row_ptr.data_ptr(), self.kv_tile.data_ptr(),
                                   self.kind.data_ptr(), self.cells.data_ptr(),
-                                  self.stride_keys.data_ptr(), self.band_begin.data_ptr())
+                                  self.prefix_keys.data_ptr(), self.band_begin.data_ptr())
 
     def host(self):
         """Copy of the CSR arrays as numpy (synchronizes)."""
         n = self.nnz
         return dict(row_ptr=self.row_ptr.cpu().numpy(), kv_tile=self.kv_tile[:n].cpu().numpy(),
                     kind=self.kind[:n].cpu().numpy(), cells=self.cells[:n].cpu().numpy(),
-                    stride_keys=self.stride_keys.cpu().numpy(),
+                    prefix_keys=self.prefix_keys.cpu().numpy(),
                     band_begin=self.band_begin.cpu().numpy(), nnz=n, num_q_tiles=self.num_q_tiles)
 
 
 def swa_block_mask_build(N, window, stride=0, bm=None, bn=None, device="cuda",
-                         dtype=torch.bfloat16, d=128, dv=None, into=None, op=SWA_OP_ATTN):
+                         dtype=torch.bfloat16, d=128, dv=None, into=None, op=SWA_OP_ATTN,
+                         dilation=1, n_global=0):
     """Build the block mask on the GPU (asynchronous on the current stream),
     into a new BlockMask or into `into` (same sizes, arrays reused).  bm/bn
     default to the tile shape of the kernel serving (op, dtype)."""
     if bm is None or bn is None:
         bm, bn = swa_tile_config(dtype, d, dv, op)
+    key = (N, window, stride, dilation, n_global, bm, bn)
     if into is not None:
-        if (into.N, into.window, into.stride, into.bm, into.bn) != (N, window, stride, bm, bn):
+        if (into.N, into.window, into.stride, into.dilation, into.n_global, into.bm, into.bn) != key:
             raise ValueError("`into` was allocated for another mask")
         m = into
     else:
-        m = BlockMask(N, window, stride, bm, bn, torch.device(device))
+        m = BlockMask(N, window, stride, bm, bn, torch.device(device), dilation, n_global)
     _check(_lib.swa_block_mask_build(ctypes.byref(m.c), _stream(m.row_ptr)), "swa_block_mask_build")
     return m
 
 
-def swa_mask_dense(N, window, stride=0, device="cuda"):
+def swa_mask_dense(N, window, stride=0, device="cuda", dilation=1, n_global=0):
     """Dense uint8 [N, N] mask computed on the GPU (debug export)."""
     out = torch.empty((N, N), dtype=torch.uint8, device=device)
-    _check(_lib.swa_mask_dense(N, window, stride, _ptr(out), _stream(out)), "swa_mask_dense")
+    _check(_lib.swa_mask_dense(N, window, stride, dilation, n_global, _ptr(out), _stream(out)),
+           "swa_mask_dense")
     return out
 
 
@@ -184,8 +190,8 @@ def swa_attn_fwd(q, k, v, window, stride, scale, mask, out=None, lse=None):
     if out is None:
         out = torch.empty_like(q)
     _check(_lib.swa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
-                             Hkv, N, d, window, stride, float(scale), ctypes.byref(mask.c),
-                             _stream(q)), "swa_attn_fwd")
+                             Hkv, N, d, window, stride, mask.dilation, mask.n_global, float(scale),
+                             ctypes.byref(mask.c), _stream(q)), "swa_attn_fwd")
     return out
 
 
@@ -265,8 +271,9 @@ def diff_attn_fwd(q1, k1, q2, k2, v, window, stride, scale, lam, mask, out=None)
     if out is None:
         out = torch.empty((B, Hq, N, dv), dtype=q1.dtype, device=q1.device)
     _check(_lib.diff_attn_fwd(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out),
-                              _dtype_code(q1), B, Hq, Hkv, N, d, dv, window, stride, float(scale),
-                              float(lam), ctypes.byref(mask.c), _stream(q1)), "diff_attn_fwd")
+                              _dtype_code(q1), B, Hq, Hkv, N, d, dv, window, stride, mask.dilation,
+                              mask.n_global, float(scale), float(lam), ctypes.byref(mask.c),
+                              _stream(q1)), "diff_attn_fwd")
     return out
 
 

@@ -3,7 +3,7 @@
 // fp32 problems; they are simple rather than fast.
 //
 // Forward: one thread per query row of a 128-row query tile walks the tiles
-// the block mask lists (stride-prefix keys first, then window tiles), staging
+// the block mask lists (prefix keys first, then band tiles), staging
 // 16 keys at a time in LDS, with a per-key online softmax
 // (Attention Variants Compared, "Flash style softmax").
 // Decode: one thread per (sequence, query head) over the sink and ring slots.
@@ -19,8 +19,8 @@ __global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const
                                                       const float *q1p, const float *k1p,
                                                       const float *vp, float *out, float *lse,
                                                       MaskView mask, int Hq, int Hkv, int N,
-                                                      int window, int stride, float scale,
-                                                      float lambda) {
+                                                      int window, int stride, int dilation,
+                                                      int n_global, float scale, float lambda) {
     __shared__ float ks[NMAPS][kSub][D];
     __shared__ float vs[kSub][DV];
     const float *qp[2] = {q0p, q1p};
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const
         l[mp] = 0.f;
     }
 
-    const int sk = mask.stride_keys[qt];
+    const int sk = mask.prefix_keys[qt];
     const int n_pre = (sk + kBN - 1) / kBN;
     const int band0 = mask.band_begin[qt];
     const int n_items = n_pre + (mask.row_ptr[qt + 1] - band0);
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const
             for (int x = threadIdx.x; x < kSub * (NMAPS * D + DV); x += blockDim.x) {
                 int r = x % kSub, c = x / kSub;
                 int kk = sub * kSub + r;
-                int j = pre ? (it * kBN + kk < sk ? (it * kBN + kk) * stride : 0)
+                int j = pre ? (it * kBN + kk < sk ? prefix_key(it * kBN + kk, sk, stride, n_global) : 0)
                             : (key0 + kk < N ? key0 + kk : N - 1);
                 if (c < NMAPS * D)
                     ks[c / D][r][c % D] = kp[c / D][(kvh + j) * D + c % D];
@@ -73,9 +73,10 @@ __global__ __launch_bounds__(kF32BM) void fwd_f32_kernel(const float *q0p, const
                 if (pre) {
                     ok = it * kBN + kk < sk;
                 } else {
-                    int j = key0 + kk;
+                    const int j = key0 + kk, dist = i - j;
                     ok = j < N && j <= i &&
-                         (i - j < window || (stride > 0 && j % stride == 0));
+                         ((dist % dilation == 0 && dist / dilation < window) ||
+                          (stride > 0 && j % stride == 0) || j < n_global);
                 }
                 if (!ok)
                     continue;
@@ -166,7 +167,8 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
                        static_cast<const float *>(a.q[0]), static_cast<const float *>(a.k[0]),
                        static_cast<const float *>(a.q[1]), static_cast<const float *>(a.k[1]),
                        static_cast<const float *>(a.v), static_cast<float *>(a.out), a.lse, a.mask,
-                       a.Hq, a.Hkv, a.N, a.window, a.stride, a.scale, a.lambda);
+                       a.Hq, a.Hkv, a.N, a.window, a.stride, a.dilation, a.n_global, a.scale,
+                       a.lambda);
     return hipGetLastError();
 }
 

@@ -27,10 +27,16 @@
 //     of O^T += V^T P^T, so they never leave registers.  V stays row-major in
 //     LDS and its transposed A-operand fragments come from ds_read_b64_tr_b16.
 //   * Tiles a wave's rows cannot see are skipped by that wave; tiles entirely
-//     inside every row's window skip the per-cell mask.
-// Local+strided problems first visit a dense prefix of stride keys
-// (0, s, 2s, ... below the query tile's first window tile), which every row
-// of the tile attends, gathered 64 at a time, then the window tiles.
+//     inside every row's window (or made of global columns only) skip the
+//     per-cell mask.
+// Problems with a stride or global tokens first visit a dense prefix of the
+// keys left of the query tile's band that every row of the tile attends (the
+// global columns 0 .. g-1, then the stride keys s, 2s, ...), gathered 64 at a
+// time, then the band tiles.  In a band tile a cell attends if it lies on the
+// (dilated) window -- distance i - j a multiple of the dilation, at most
+// (window-1)*dilation -- or its key is a stride key or a global column
+// (Learn: Sparse & Sliding-Window Attention, §3b, for dilation and global
+// tokens).
 #include <type_traits>
 
 #include "swa_internal.h"
@@ -79,13 +85,17 @@ struct Params {
     __bf16 *out;
     float *lse;
     MaskView mask;
-    int B, Hq, Hkv, N, window, stride;
+    int B, Hq, Hkv, N, window, stride, dilation, n_global;
     float c;        // scale * log2(e)
     float lambda;
 };
 
-template <int D, int DV, int NMAPS, int RG>
+// EXT: the pattern may have a dilated window or global tokens; without it
+// both are compile-time absent and the plain window/stride code is unchanged.
+template <int D, int DV, int NMAPS, int RG, bool EXT>
 __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
+    const int dil = EXT ? p.dilation : 1;
+    const int n_glob = EXT ? p.n_global : 0;
     using C = Cfg<D, DV, NMAPS>;
     constexpr int BM = 128 * RG;       // query rows per workgroup
     constexpr int ROWS = 32 * RG;      // query rows per wave (RG groups of 32)
@@ -131,14 +141,25 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 qf[m][rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
     }
 
-    // ---- the walk: stride-prefix chunks, then window tiles ----------------
-    const int sk = p.mask.stride_keys[qt];
+    // ---- the walk: prefix chunks, then band tiles --------------------------
+    const int sk = p.mask.prefix_keys[qt];
+    // prefix key kn: kn itself below gp (global columns), then stride multiples
+    const int gp = n_glob < sk ? n_glob : sk;
+    const int s_first = p.stride > 0 ? (gp + p.stride - 1) / p.stride - gp : 0;
     const int n_pre = (sk + 63) >> 6;
     const int band0 = p.mask.band_begin[qt];
     const int n_items = n_pre + (p.mask.row_ptr[qt + 1] - band0);
     const int64_t kv_head = (int64_t)(b * p.Hkv + g) * p.N;
 
-    // first key of item it (window tiles only)
+    // window span in keys, and the dilation lattice: bit m set iff m is a
+    // multiple of the dilation (m < 64)
+    const int64_t span64 = static_cast<int64_t>(p.window - 1) * dil;
+    const int span = span64 < p.N ? static_cast<int>(span64) : p.N;  // distances are < N
+    uint64_t lattice = 0;
+    for (int m = 0; m < 64; m += dil)
+        lattice |= 1ull << m;
+
+    // first key of item it (band tiles only)
     auto item_key0 = [&](int it) -> int {
         return it >= n_pre ? p.mask.kv_tile[band0 + (it - n_pre)] * 64 : 0;
     };
@@ -175,12 +196,12 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                     vrs, v_goff, (key0 + u * C::vRowStep) * DV * 2, 0));
         } else {
-            // stride-prefix chunk: rows kn * stride for kn < sk (others read
+            // prefix chunk: key rows of prefix keys kn < sk (others read
             // past the end, i.e. zeros)
 #pragma unroll
             for (int u = 0; u < C::kPer; ++u) {
                 const int kn = it * 64 + kr0 + u * C::kRowStep;
-                const int row = kn < sk ? kn * p.stride : p.N;
+                const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
 #pragma unroll
                 for (int m = 0; m < NMAPS; ++m)
                     kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -189,7 +210,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 #pragma unroll
             for (int u = 0; u < C::vPer; ++u) {
                 const int kn = it * 64 + vr0 + u * C::vRowStep;
-                const int row = kn < sk ? kn * p.stride : p.N;
+                const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
                 vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                     vrs, (row * DV + vc * 8) * 2, 0, 0));
             }
@@ -241,12 +262,16 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
         // ---- classify this tile for each row group of this wave -------------
         const bool pre = it < n_pre;
         const int key0 = item_key0(it);
-        uint64_t smask = 0;  // stride keys of a window tile, bit per tile row
+        // column keys of a band tile (stride keys, global columns), one bit per
+        // key of the tile; every row at or after such a key attends it
+        uint64_t smask = 0;
         if (!pre && p.stride > 0) {
             const int f = ((key0 + p.stride - 1) / p.stride) * p.stride;
             for (int j = f; j < key0 + 64; j += p.stride)
                 smask |= 1ull << (j - key0);
         }
+        if (!pre && key0 < n_glob)
+            smask |= n_glob - key0 >= 64 ? ~0ull : (1ull << (n_glob - key0)) - 1;
         bool full[RG], any = false;
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
@@ -256,8 +281,9 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 empty = false;
                 full[rg] = (it + 1) * 64 <= sk;
             } else {
-                empty = key0 > r1 || (key0 + 63 < r0 - p.window + 1 && smask == 0);
-                full[rg] = !empty && key0 + 63 <= r0 && key0 >= r1 - p.window + 1 && key0 + 64 <= p.N;
+                empty = key0 > r1 || (key0 + 63 < r0 - span && smask == 0);
+                full[rg] = !empty && key0 + 63 <= r0 && key0 + 64 <= p.N &&
+                           ((dil == 1 && key0 >= r1 - p.window + 1) || key0 + 64 <= n_glob);
             }
             any = any || !empty;
         }
@@ -302,9 +328,10 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                     }
                 } else {
                     // dist = i - j = base - kc; window part iff 0 <= dist < W
+                    // (dilation 1), else dist <= span on the dilation lattice
                     const int base = my_row[rg] - key0 - kb * 32 - 4 * hl;
                     const unsigned W = (unsigned)p.window;
-                    if (smask == 0) {
+                    if (smask == 0 && dil == 1) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kcst = (r & 3) + 8 * (r >> 2);
@@ -313,7 +340,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             for (int m = 0; m < NMAPS; ++m)
                                 sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
                         }
-                    } else {
+                    } else if (dil == 1) {
                         const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
@@ -321,6 +348,22 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             const int dist = base - kcst;
                             // bitwise, not short-circuit: no per-cell branch
                             const bool ok = ((unsigned)dist < W) |
+                                            ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
+#pragma unroll
+                            for (int m = 0; m < NMAPS; ++m)
+                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
+                        }
+                    } else {
+                        const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
+                        // lattice bit kc set iff base - kc is a multiple of the dilation
+                        int res = base % dil;
+                        res += res < 0 ? dil : 0;
+                        const uint32_t lat = (uint32_t)(lattice << res);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kcst = (r & 3) + 8 * (r >> 2);
+                            const int dist = base - kcst;
+                            const bool ok = (((unsigned)dist <= (unsigned)span) & (((lat >> kcst) & 1u) != 0)) |
                                             ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
 #pragma unroll
                             for (int m = 0; m < NMAPS; ++m)
@@ -518,15 +561,15 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 // registers per lane, which lets two waves share each SIMD (one wave's
 // softmax overlaps the other's matrix work).  Two-map kernels need more
 // state and run one wave per SIMD.
-template <int D, int DV>
+template <int D, int DV, bool EXT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFwdRowGroups == 1 ? 2 : 1, 2)))
 void fwd_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 1, kFwdRowGroups>(p);
+    fwd_bf16_body<D, DV, 1, kFwdRowGroups, EXT>(p);
 }
 
-template <int D, int DV>
+template <int D, int DV, bool EXT>
 __global__ __launch_bounds__(kThreads) void diff_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 2, kDiffRowGroups>(p);
+    fwd_bf16_body<D, DV, 2, kDiffRowGroups, EXT>(p);
 }
 
 template <int D, int DV, int NMAPS>
@@ -546,13 +589,23 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     p.N = a.N;
     p.window = a.window;
     p.stride = a.stride;
+    p.dilation = a.dilation;
+    p.n_global = a.n_global;
     p.c = a.scale * kLog2e;
     p.lambda = a.lambda;
     unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
-    if constexpr (NMAPS == 1)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, DV>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((diff_bf16_kernel<D, DV>), dim3(grid), dim3(kThreads), 0, stream, p);
+    const bool ext = a.dilation != 1 || a.n_global != 0;
+    if constexpr (NMAPS == 1) {
+        if (ext)
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+        if (ext)
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -18,33 +18,44 @@ bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 bool tile_ok(int t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 256; }
 
-// List length of one query tile: the window tiles form one contiguous range
-// [t_lo, t_hi] covering keys max(0, r0 - window + 1) .. r1 (r0, r1 = first
-// and last row of the tile); every stride key left of that range is attended
-// by every row of the tile, and the tiles holding one are listed first.
-void q_tile_counts(int64_t q, int64_t N, int64_t window, int64_t stride, int64_t bm, int64_t bn,
-                   int64_t *n_band, int64_t *n_stride_only) {
+// List length of one query tile: the band tiles form one contiguous range
+// [t_lo, t_hi] covering keys max(0, r0 - (window-1)*dilation) .. r1 (r0, r1 =
+// first and last row of the tile; with dilation <= bn each of them holds an
+// attended cell); every prefix key (global column or multiple of stride) left
+// of that range is attended by every row of the tile, and the tiles holding
+// one are listed first.
+void q_tile_counts(int64_t q, int64_t N, int64_t window, int64_t stride, int64_t dilation,
+                   int64_t n_global, int64_t bm, int64_t bn, int64_t *n_band,
+                   int64_t *n_prefix_only) {
     int64_t r0 = q * bm;
     int64_t r1 = (r0 + bm < N ? r0 + bm : N) - 1;
-    int64_t lo = r0 - window + 1 > 0 ? r0 - window + 1 : 0;
+    int64_t span = (window - 1) * dilation;
+    int64_t lo = r0 - span > 0 ? r0 - span : 0;
     int64_t t_lo = lo / bn, t_hi = r1 / bn;
     *n_band = t_hi - t_lo + 1;
-    if (stride <= 0 || t_lo == 0)
-        *n_stride_only = 0;
-    else if (stride <= bn)
-        *n_stride_only = t_lo;  // every tile of bn >= stride keys holds a multiple
-    else
-        *n_stride_only = (t_lo * bn + stride - 1) / stride;  // one multiple per tile
+    // tiles [0, a) hold a global column; stride tiles are counted from a on
+    int64_t a = (n_global + bn - 1) / bn;
+    a = a < t_lo ? a : t_lo;
+    int64_t ns = 0;
+    if (stride > 0 && t_lo > a) {
+        if (stride <= bn)
+            ns = t_lo - a;  // every tile of bn >= stride keys holds a multiple
+        else                // one multiple per tile at most
+            ns = (t_lo * bn + stride - 1) / stride - (a * bn + stride - 1) / stride;
+    }
+    *n_prefix_only = a + ns;
 }
 
-int mask_query(int N, int window, int stride, int bm, int bn, int32_t *nq_out, int32_t *nnz_out) {
-    if (N < 1 || N > SWA_MAX_N || window < 1 || stride < 0 || !tile_ok(bm) || !tile_ok(bn))
+int mask_query(int N, int window, int stride, int dilation, int n_global, int bm, int bn,
+               int32_t *nq_out, int32_t *nnz_out) {
+    if (N < 1 || N > SWA_MAX_N || window < 1 || stride < 0 || !tile_ok(bm) || !tile_ok(bn) ||
+        dilation < 1 || dilation > bn || n_global < 0 || n_global > SWA_MAX_N)
         return SWA_ERR_INVALID_ARG;
     int64_t nq = (static_cast<int64_t>(N) + bm - 1) / bm, nnz = 0;
     for (int64_t q = 0; q < nq; ++q) {
-        int64_t nb, ns;
-        q_tile_counts(q, N, window, stride, bm, bn, &nb, &ns);
-        nnz += nb + ns;
+        int64_t nb, np;
+        q_tile_counts(q, N, window, stride, dilation, n_global, bm, bn, &nb, &np);
+        nnz += nb + np;
     }
     if (nnz > INT32_MAX)
         return SWA_ERR_UNSUPPORTED;
@@ -55,26 +66,31 @@ int mask_query(int N, int window, int stride, int bm, int bn, int32_t *nq_out, i
     return SWA_OK;
 }
 
+bool mask_arrays_ok(const swa_block_mask_t *m) {
+    return m->row_ptr && m->kv_tile && m->kind && m->cells && m->prefix_keys && m->band_begin;
+}
+
 // The mask must describe exactly this problem and the kernel's tiling.
-int check_mask(const swa_block_mask_t *m, int N, int window, int stride, int bm) {
+int check_mask(const swa_block_mask_t *m, int N, int window, int stride, int dilation,
+               int n_global, int bm) {
     if (m == nullptr)
         return SWA_ERR_INVALID_ARG;
-    if (m->N != N || m->window != window || m->stride != stride || m->bm != bm || m->bn != kBN)
+    if (m->N != N || m->window != window || m->stride != stride || m->dilation != dilation ||
+        m->n_global != n_global || m->bm != bm || m->bn != kBN)
         return SWA_ERR_INVALID_ARG;
     int32_t nq = 0, nnz = 0;
-    int st = mask_query(N, window, stride, bm, kBN, &nq, &nnz);
+    int st = mask_query(N, window, stride, dilation, n_global, bm, kBN, &nq, &nnz);
     if (st != SWA_OK)
         return st;
-    if (m->num_q_tiles != nq || m->nnz != nnz)
-        return SWA_ERR_INVALID_ARG;
-    if (!m->row_ptr || !m->kv_tile || !m->kind || !m->cells || !m->stride_keys || !m->band_begin)
+    if (m->num_q_tiles != nq || m->nnz != nnz || !mask_arrays_ok(m))
         return SWA_ERR_INVALID_ARG;
     return SWA_OK;
 }
 
-int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride) {
+int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride, int dilation,
+                int n_global) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || N > SWA_MAX_N || window < 1 ||
-        stride < 0)
+        stride < 0 || dilation < 1 || n_global < 0)
         return SWA_ERR_INVALID_ARG;
     // every flat row index (b*Hq + h)*N + i fits in int32
     if (static_cast<int64_t>(B) * Hq * N > INT32_MAX)
@@ -85,7 +101,7 @@ int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride) {
 int hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 
 swa::MaskView view_of(const swa_block_mask_t *m) {
-    return swa::MaskView{m->row_ptr, m->kv_tile, m->kind, m->stride_keys, m->band_begin,
+    return swa::MaskView{m->row_ptr, m->kv_tile, m->kind, m->prefix_keys, m->band_begin,
                          m->num_q_tiles};
 }
 
@@ -183,37 +199,38 @@ int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int
     return SWA_OK;
 }
 
-int swa_block_mask_query(int N, int window, int stride, int bm, int bn, int32_t *num_q_tiles,
-                         int32_t *nnz) {
+int swa_block_mask_query(int N, int window, int stride, int dilation, int n_global, int bm, int bn,
+                         int32_t *num_q_tiles, int32_t *nnz) {
     if (!num_q_tiles || !nnz)
         return SWA_ERR_INVALID_ARG;
-    return mask_query(N, window, stride, bm, bn, num_q_tiles, nnz);
+    return mask_query(N, window, stride, dilation, n_global, bm, bn, num_q_tiles, nnz);
 }
 
 int swa_block_mask_build(const swa_block_mask_t *mask, hipStream_t stream) {
     if (!mask)
         return SWA_ERR_INVALID_ARG;
     int32_t nq = 0, nnz = 0;
-    int st = mask_query(mask->N, mask->window, mask->stride, mask->bm, mask->bn, &nq, &nnz);
+    int st = mask_query(mask->N, mask->window, mask->stride, mask->dilation, mask->n_global,
+                        mask->bm, mask->bn, &nq, &nnz);
     if (st != SWA_OK)
         return st;
-    if (mask->num_q_tiles != nq || mask->nnz != nnz)
-        return SWA_ERR_INVALID_ARG;
-    if (!mask->row_ptr || !mask->kv_tile || !mask->kind || !mask->cells || !mask->stride_keys ||
-        !mask->band_begin)
+    if (mask->num_q_tiles != nq || mask->nnz != nnz || !mask_arrays_ok(mask))
         return SWA_ERR_INVALID_ARG;
     return hip_status(swa::launch_block_mask_build(*mask, stream));
 }
 
-int swa_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream) {
-    if (N < 1 || N > 16384 || window < 1 || stride < 0 || out == nullptr)
+int swa_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
+                   hipStream_t stream) {
+    if (N < 1 || N > 16384 || window < 1 || stride < 0 || dilation < 1 || n_global < 0 ||
+        out == nullptr)
         return SWA_ERR_INVALID_ARG;
-    return hip_status(swa::launch_mask_dense(N, window, stride, out, stream));
+    return hip_status(swa::launch_mask_dense(N, window, stride, dilation, n_global, out, stream));
 }
 
 int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                  swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
-                 float scale, const swa_block_mask_t *mask, hipStream_t stream) {
+                 int dilation, int n_global, float scale, const swa_block_mask_t *mask,
+                 hipStream_t stream) {
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return SWA_ERR_INVALID_ARG;
     if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
@@ -222,12 +239,12 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
         return SWA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f))
         return SWA_ERR_INVALID_ARG;
-    int st = check_sizes(B, Hq, Hkv, N, window, stride);
+    int st = check_sizes(B, Hq, Hkv, N, window, stride, dilation, n_global);
     if (st != SWA_OK)
         return st;
     if (!head_dim_ok(d))
         return SWA_ERR_UNSUPPORTED;
-    st = check_mask(mask, N, window, stride, swa::tile_rows(SWA_OP_ATTN, dt));
+    st = check_mask(mask, N, window, stride, dilation, n_global, swa::tile_rows(SWA_OP_ATTN, dt));
     if (st != SWA_OK)
         return st;
     swa::FwdArgs a{};
@@ -244,6 +261,8 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     a.dv = d;
     a.window = window;
     a.stride = stride;
+    a.dilation = dilation;
+    a.n_global = n_global;
     a.scale = scale;
     a.lambda = 0.f;
     a.nmaps = 1;
@@ -340,7 +359,7 @@ int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const 
 
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
                   void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int dv,
-                  int window, int stride, float scale, float lambda,
+                  int window, int stride, int dilation, int n_global, float scale, float lambda,
                   const swa_block_mask_t *mask, hipStream_t stream) {
     if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) ||
         !aligned16(out))
@@ -349,7 +368,7 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
         return SWA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(lambda))
         return SWA_ERR_INVALID_ARG;
-    int st = check_sizes(B, Hq, Hkv, N, window, stride);
+    int st = check_sizes(B, Hq, Hkv, N, window, stride, dilation, n_global);
     if (st != SWA_OK)
         return st;
     if (!head_dim_ok(d) || !head_dim_ok(dv))
@@ -357,7 +376,7 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
     // bf16: two K tiles and one V tile of 64 keys, double-buffered, in 64 KiB of LDS
     if (dt == SWA_BF16 && 2 * d + dv > 256)
         return SWA_ERR_UNSUPPORTED;
-    st = check_mask(mask, N, window, stride, swa::tile_rows(SWA_OP_DIFF, dt));
+    st = check_mask(mask, N, window, stride, dilation, n_global, swa::tile_rows(SWA_OP_DIFF, dt));
     if (st != SWA_OK)
         return st;
     swa::FwdArgs a{};
@@ -376,6 +395,8 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
     a.dv = dv;
     a.window = window;
     a.stride = stride;
+    a.dilation = dilation;
+    a.n_global = n_global;
     a.scale = scale;
     a.lambda = lambda;
     a.nmaps = 2;

@@ -30,7 +30,7 @@ struct MaskView {
     const int32_t *row_ptr;
     const int32_t *kv_tile;
     const uint8_t *kind;
-    const int32_t *stride_keys;
+    const int32_t *prefix_keys;
     const int32_t *band_begin;
     int32_t num_q_tiles;
 };
@@ -42,12 +42,23 @@ struct FwdArgs {
     const void *v;
     void *out;
     float *lse;
-    int B, Hq, Hkv, N, d, dv, window, stride;
+    int B, Hq, Hkv, N, d, dv, window, stride, dilation, n_global;
     float scale;
     float lambda;   // weight of the second map (two-map problems only)
     int nmaps;      // 1 or 2
     MaskView mask;
 };
+
+// k-th prefix key (0 <= k < count) of a query tile whose prefix-only tiles
+// hold `count` prefix keys: the global columns 0 .. g'-1 (g' = min(n_global,
+// count)), then the multiples of stride from g' on.
+__host__ __device__ inline int prefix_key(int k, int count, int stride, int n_global) {
+    const int gp = n_global < count ? n_global : count;
+    if (k < gp)
+        return k;
+    const int first = (gp + stride - 1) / stride;   // stride > 0 whenever k >= gp
+    return (first + (k - gp)) * stride;
+}
 
 // One decode step (one or two score maps, optional sink slots).
 struct DecodeArgs {
@@ -84,7 +95,8 @@ DecodePlan decode_plan(int B, int Hkv, int slots);
 inline int64_t decode_ws_ml_floats(int64_t parts) { return (parts * 2 + 3) / 4 * 4; }
 
 hipError_t launch_block_mask_build(const swa_block_mask_t &m, hipStream_t stream);
-hipError_t launch_mask_dense(int N, int window, int stride, uint8_t *out, hipStream_t stream);
+hipError_t launch_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
+                             hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);

@@ -23,6 +23,10 @@ sink_decode_bf16       window_decode_bf16 plus 4 sink slots (positions 0-3),
 diff_decode_bf16       32 sequences at position 131072, ring W=4096, H=16,
                        d=64 per map, dv=128, lambda 0.5, scale 1/8, bf16,
                        seed 7
+global_prefill_bf16    swa_prefill_bf16 plus 64 global tokens (positions
+                       0-63), seed 8
+dilated_prefill_bf16   swa_prefill_bf16 with a window of 512 keys at
+                       dilation 2 (the same 1023-token span), seed 9
 =====================  =====================================================
 """
 import math
@@ -46,6 +50,12 @@ WORKLOADS = {
                              scale=1.0 / math.sqrt(128), seed=6),
     "diff_decode_bf16": dict(kind="diff_decode", dtype="bf16", B=32, Hq=16, Hkv=16, window=4096,
                              d=64, dv=128, position=131072, scale=1.0 / 8, lam=0.5, seed=7),
+    "global_prefill_bf16": dict(kind="prefill", dtype="bf16", B=1, Hq=32, Hkv=8, N=8192, d=128,
+                                dv=128, window=1024, stride=0, n_global=64,
+                                scale=1.0 / math.sqrt(128), seed=8),
+    "dilated_prefill_bf16": dict(kind="prefill", dtype="bf16", B=1, Hq=32, Hkv=8, N=8192, d=128,
+                                 dv=128, window=512, stride=0, dilation=2,
+                                 scale=1.0 / math.sqrt(128), seed=9),
 }
 
 

@@ -85,36 +85,44 @@ def test_tile_config(swa):
     assert cfg(5, swa.SWA_BF16, 64, 64)[0] == swa.SWA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("N,W,s,bm,bn", [
-    (1, 1, 0, 128, 64), (37, 5, 3, 16, 16), (300, 64, 5, 128, 64), (511, 129, 64, 128, 64),
-    (1000, 50, 130, 128, 64), (777, 200, 1, 64, 32), (4096, 1024, 0, 128, 64),
-    (8192, 1024, 0, 128, 64), (16384, 256, 128, 128, 64), (640, 600, 700, 32, 128),
-    (999, 7, 65, 64, 64), (2000, 3000, 3, 256, 16)])
-def test_mask_query_matches_oracle(swa, N, W, s, bm, bn):
-    nq, nnz = swa.swa_block_mask_query(N, W, s, bm, bn)
-    t = oracle.tile_list(N, W, s, bm, bn)
+@pytest.mark.parametrize("N,W,s,bm,bn,dil,g", [
+    (1, 1, 0, 128, 64, 1, 0), (37, 5, 3, 16, 16, 1, 0), (300, 64, 5, 128, 64, 1, 0),
+    (511, 129, 64, 128, 64, 1, 0), (1000, 50, 130, 128, 64, 1, 0), (777, 200, 1, 64, 32, 1, 0),
+    (4096, 1024, 0, 128, 64, 1, 0), (8192, 1024, 0, 128, 64, 1, 0), (16384, 256, 128, 128, 64, 1, 0),
+    (640, 600, 700, 32, 128, 1, 0), (999, 7, 65, 64, 64, 1, 0), (2000, 3000, 3, 256, 16, 1, 0),
+    # dilated windows (dilation <= bn) and global tokens
+    (1000, 50, 0, 128, 64, 2, 0), (1000, 30, 0, 128, 64, 64, 0), (777, 40, 9, 64, 16, 16, 0),
+    (1000, 50, 0, 128, 64, 1, 64), (1000, 50, 130, 128, 64, 1, 300), (700, 20, 3, 32, 32, 5, 17),
+    (300, 4, 0, 128, 64, 3, 1000), (4096, 512, 0, 128, 64, 2, 64), (555, 8, 100, 16, 64, 7, 65)])
+def test_mask_query_matches_oracle(swa, N, W, s, bm, bn, dil, g):
+    nq, nnz = swa.swa_block_mask_query(N, W, s, bm, bn, dil, g)
+    t = oracle.tile_list(N, W, s, bm, bn, dilation=dil, n_global=g)
     assert (nq, nnz) == (t["num_q_tiles"], t["nnz"])
 
 
 def test_mask_query_rejects(swa):
     for args in [(0, 4, 0, 128, 64), (10, 0, 0, 128, 64), (10, 4, -1, 128, 64), (10, 4, 0, 100, 64),
-                 (10, 4, 0, 128, 8), (swa.SWA_MAX_N + 1, 4, 0, 128, 64)]:
+                 (10, 4, 0, 128, 8), (swa.SWA_MAX_N + 1, 4, 0, 128, 64),
+                 (10, 4, 0, 128, 64, 0, 0),        # dilation < 1
+                 (10, 4, 0, 128, 64, 65, 0),       # dilation > bn
+                 (10, 4, 0, 128, 16, 17, 0),
+                 (10, 4, 0, 128, 64, 1, -1)]:      # negative global count
         with pytest.raises(swa.SwaError) as e:
             swa.swa_block_mask_query(*args)
         assert e.value.status == swa.SWA_ERR_INVALID_ARG
 
 
-def fake_mask(swa, N, W, s, bm=128, bn=64, nq=None, nnz=None, null=False):
-    q, z = swa.swa_block_mask_query(N, W, s, bm, 64)
+def fake_mask(swa, N, W, s, bm=128, bn=64, nq=None, nnz=None, null=False, dil=1, g=0):
+    q, z = swa.swa_block_mask_query(N, W, s, bm, 64, dil, g)
     p = 0 if null else FAKE
-    return swa.swa_block_mask_t(N, W, s, bm, bn, q if nq is None else nq, z if nnz is None else nnz,
-                                p, p, p, p, p, p)
+    return swa.swa_block_mask_t(N, W, s, dil, g, bm, bn, q if nq is None else nq,
+                                z if nnz is None else nnz, p, p, p, p, p, p)
 
 
 def fwd(swa, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, dt=1, B=1, Hq=4, Hkv=2, N=256, d=64,
-        W=32, s=0, scale=0.125, mask=None):
+        W=32, s=0, scale=0.125, mask=None, dil=1, g=0):
     mask = fake_mask(swa, N, W, s) if mask is None else mask
-    return swa.lib.swa_attn_fwd(q, k, v, out, lse, dt, B, Hq, Hkv, N, d, W, s, scale,
+    return swa.lib.swa_attn_fwd(q, k, v, out, lse, dt, B, Hq, Hkv, N, d, W, s, dil, g, scale,
                                 ctypes.byref(mask), None)
 
 
@@ -139,7 +147,13 @@ def test_fwd_rejections(swa):
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, bm=256)) == E  # another tiling
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, nnz=1)) == E   # wrong size
     assert fwd(swa, mask=fake_mask(swa, 256, 32, 0, null=True)) == E
-    assert swa.lib.swa_attn_fwd(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 4, 2, 256, 64, 32, 0, 0.125,
+    assert fwd(swa, dil=0) == E
+    assert fwd(swa, g=-1) == E
+    assert fwd(swa, dil=2) == E                                     # mask built for dilation 1
+    assert fwd(swa, g=8) == E                                       # mask built without globals
+    assert fwd(swa, dil=2, g=8, mask=fake_mask(swa, 256, 32, 0, dil=2)) == E
+    assert fwd(swa, dil=2, mask=fake_mask(swa, 256, 32, 0, dil=2, g=8)) == E
+    assert swa.lib.swa_attn_fwd(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 4, 2, 256, 64, 32, 0, 1, 0, 0.125,
                                 None, None) == E
     assert fwd(swa, B=1 << 12, Hq=1 << 10, Hkv=1 << 10, N=1 << 12,
                mask=fake_mask(swa, 1 << 12, 32, 0)) == U   # flat row index beyond int32
@@ -230,16 +244,18 @@ def test_decode_workspace_bytes(swa):
 def test_diff_rejections(swa):
     E, U = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED
 
-    def call(d=64, dv=128, dt=1, lam=0.5, q2=FAKE, W=32, mask=None):
+    def call(d=64, dv=128, dt=1, lam=0.5, q2=FAKE, W=32, mask=None, dil=1, g=0):
         m = fake_mask(swa, 256, W, 0, bm=128) if mask is None else mask
         return swa.lib.diff_attn_fwd(FAKE, FAKE, q2, FAKE, FAKE, FAKE, dt, 1, 4, 4, 256, d, dv, W, 0,
-                                     0.125, lam, ctypes.byref(m), None)
+                                     dil, g, 0.125, lam, ctypes.byref(m), None)
     assert call(q2=0) == E
     assert call(lam=float("inf")) == E
     assert call(d=128, dv=128) == U              # bf16: 2d + dv > 256 does not fit LDS
     assert call(d=96) == U
     assert call(mask=fake_mask(swa, 256, 31, 0, bm=128)) == E
     assert call(mask=fake_mask(swa, 256, 32, 0, bm=64)) == E         # another tiling
+    assert call(dil=3) == E                                          # another dilation
+    assert call(g=1) == E                                            # another global count
 
 
 def test_block_mask_build_rejections(swa):
@@ -250,5 +266,7 @@ def test_block_mask_build_rejections(swa):
     assert swa.lib.swa_block_mask_build(ctypes.byref(m), None) == E
     m = fake_mask(swa, 300, 20, 0, null=True)
     assert swa.lib.swa_block_mask_build(ctypes.byref(m), None) == E
-    assert swa.lib.swa_mask_dense(20000, 4, 0, FAKE, None) == E
-    assert swa.lib.swa_mask_dense(20, 4, 0, None, None) == E
+    assert swa.lib.swa_mask_dense(20000, 4, 0, 1, 0, FAKE, None) == E
+    assert swa.lib.swa_mask_dense(20, 4, 0, 1, 0, None, None) == E
+    assert swa.lib.swa_mask_dense(20, 4, 0, 0, 0, FAKE, None) == E
+    assert swa.lib.swa_mask_dense(20, 4, 0, 1, -2, FAKE, None) == E

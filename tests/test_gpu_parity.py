@@ -63,15 +63,36 @@ def test_block_mask_bit_exact(swa, N, W, s, bm):
     got = m.host()
     want = oracle.tile_list(N, W, s, m.bm, m.bn)
     assert got["nnz"] == want["nnz"] and got["num_q_tiles"] == want["num_q_tiles"]
-    for key in ("row_ptr", "kv_tile", "kind", "cells", "stride_keys", "band_begin"):
+    for key in ("row_ptr", "kv_tile", "kind", "cells", "prefix_keys", "band_begin"):
         np.testing.assert_array_equal(got[key], want[key], err_msg=key)
 
 
-@pytest.mark.parametrize("N,W,s", [(1, 1, 0), (64, 5, 0), (257, 17, 7), (1024, 100, 64), (3000, 3000, 0)])
-def test_dense_mask_bit_exact(swa, N, W, s):
-    banner(f"dense mask N={N} W={W} s={s}")
-    got = swa.swa_mask_dense(N, W, s).cpu().numpy()
-    np.testing.assert_array_equal(got, oracle.mask_dense(N, W, s))
+MASK_EXT_CASES = [
+    # N, W, stride, dilation, n_global, bm, bn
+    (1000, 50, 0, 2, 0, 128, 64), (1000, 30, 0, 64, 0, 128, 64), (777, 40, 9, 16, 0, 64, 16),
+    (1000, 50, 0, 1, 64, 128, 64), (1000, 50, 130, 1, 300, 128, 64), (700, 20, 3, 5, 17, 32, 32),
+    (300, 4, 0, 3, 1000, 128, 64), (4096, 512, 0, 2, 64, 128, 64), (555, 8, 100, 7, 65, 16, 64),
+    (8192, 512, 0, 2, 0, 128, 64), (8192, 1024, 0, 1, 64, 128, 64)]
+
+
+@pytest.mark.parametrize("N,W,s,dil,g,bm,bn", MASK_EXT_CASES)
+def test_block_mask_dilated_global_bit_exact(swa, N, W, s, dil, g, bm, bn):
+    banner(f"block mask N={N} W={W} s={s} dilation={dil} globals={g} bm={bm} bn={bn}")
+    m = swa.swa_block_mask_build(N, W, s, bm=bm, bn=bn, dilation=dil, n_global=g)
+    got = m.host()
+    want = oracle.tile_list(N, W, s, bm, bn, dilation=dil, n_global=g)
+    assert got["nnz"] == want["nnz"] and got["num_q_tiles"] == want["num_q_tiles"]
+    for key in ("row_ptr", "kv_tile", "kind", "cells", "prefix_keys", "band_begin"):
+        np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+
+
+@pytest.mark.parametrize("N,W,s,dil,g", [(1, 1, 0, 1, 0), (64, 5, 0, 1, 0), (257, 17, 7, 1, 0),
+                                         (1024, 100, 64, 1, 0), (3000, 3000, 0, 1, 0),
+                                         (500, 20, 0, 3, 0), (500, 20, 33, 2, 9), (300, 4, 0, 1, 300)])
+def test_dense_mask_bit_exact(swa, N, W, s, dil, g):
+    banner(f"dense mask N={N} W={W} s={s} dilation={dil} globals={g}")
+    got = swa.swa_mask_dense(N, W, s, dilation=dil, n_global=g).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.mask_dense(N, W, s, dil, g))
 
 
 # --------------------------------------------------------------------------
@@ -81,7 +102,8 @@ def test_dense_mask_bit_exact(swa, N, W, s):
 def run_prefill(swa, cfg, q, k, v, with_lse=False):
     dt = cfg["dtype"]
     mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"],
-                                    dtype=torch.bfloat16 if dt == "bf16" else torch.float32, d=cfg["d"])
+                                    dtype=torch.bfloat16 if dt == "bf16" else torch.float32, d=cfg["d"],
+                                    dilation=cfg.get("dilation", 1), n_global=cfg.get("n_global", 0))
     qd, kd, vd = dev(q, dt), dev(k, dt), dev(v, dt)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda") if with_lse else None
     out = swa.swa_attn_fwd(qd, kd, vd, cfg["window"], cfg["stride"], cfg["scale"], mask, lse=lse)
@@ -119,6 +141,35 @@ def test_prefill_parity_small(swa, dtype, B, Hq, Hkv, N, d, W, s):
     assert max_err(lse, want_lse) <= (1e-3 if dtype == "bf16" else 1e-5)
 
 
+PREFILL_EXT_CASES = [
+    # B, Hq, Hkv, N, d, W, stride, dilation, n_global
+    (1, 2, 2, 300, 64, 20, 0, 2, 0),
+    (1, 4, 2, 517, 128, 64, 0, 3, 0),
+    (1, 2, 2, 450, 64, 40, 7, 4, 0),
+    (1, 2, 2, 700, 128, 16, 0, 64, 0),      # span 960 keys, one key in 64
+    (1, 2, 2, 600, 64, 50, 0, 1, 16),
+    (1, 2, 2, 600, 128, 50, 100, 1, 70),    # global columns and stride keys in the prefix
+    (2, 2, 1, 333, 64, 30, 0, 2, 5),
+    (1, 2, 2, 300, 32, 10, 0, 1, 300),      # every token global: full causal
+    (1, 4, 4, 1000, 64, 128, 64, 2, 64),
+    (1, 2, 2, 260, 32, 3, 5, 9, 130),       # global columns across whole tiles
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,W,s,dil,g", PREFILL_EXT_CASES)
+def test_prefill_dilated_global_parity(swa, dtype, B, Hq, Hkv, N, d, W, s, dil, g):
+    banner(f"prefill {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} W={W} s={s} dilation={dil} globals={g}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dv=d, window=W, stride=s, dilation=dil,
+               n_global=g, scale=1.0 / math.sqrt(d), seed=N + d + W + s + dil + g)
+    q, k, v = synth.prefill_inputs(cfg)
+    got, lse = run_prefill(swa, cfg, q, k, v, with_lse=True)
+    want, want_lse = oracle.attn_full(q, k, v, W, s, cfg["scale"], with_lse=True, dilation=dil,
+                                      n_global=g)
+    assert max_err(got, want) <= TOL[dtype]
+    assert max_err(lse, want_lse) <= (1e-3 if dtype == "bf16" else 1e-5)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_peaky_scores(swa, dtype):
     # query scaled by 8: near one-hot softmax rows, large score range
@@ -149,14 +200,16 @@ def boundary_rows(B, H, N, step, extra):
     return synth.sample_rows(B * H * N, extra, seed=step, must=must)
 
 
-@pytest.mark.parametrize("name", ["swa_prefill_bf16", "local_strided_bf16"])
+@pytest.mark.parametrize("name", ["swa_prefill_bf16", "local_strided_bf16", "global_prefill_bf16",
+                                  "dilated_prefill_bf16"])
 def test_prefill_workload_sampled(swa, name):
     cfg = synth.workload(name)
     banner(f"workload {name} (sampled rows)")
     q, k, v = synth.prefill_inputs(cfg)
     got = run_prefill(swa, cfg, q, k, v).reshape(-1, cfg["dv"])
     rows = boundary_rows(cfg["B"], cfg["Hq"], cfg["N"], 3, 768)
-    want = oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], rows)
+    want = oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], rows,
+                            dilation=cfg.get("dilation", 1), n_global=cfg.get("n_global", 0))
     assert max_err(got[rows], want) <= TOL["bf16"]
     assert np.all(np.isfinite(got))
 
@@ -179,7 +232,8 @@ def run_diff(swa, cfg, q1, k1, q2, k2, v):
     dt = cfg["dtype"]
     mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"],
                                     dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
-                                    d=cfg["d"], dv=cfg["dv"], op=swa.SWA_OP_DIFF)
+                                    d=cfg["d"], dv=cfg["dv"], op=swa.SWA_OP_DIFF,
+                                    dilation=cfg.get("dilation", 1), n_global=cfg.get("n_global", 0))
     out = swa.diff_attn_fwd(dev(q1, dt), dev(k1, dt), dev(q2, dt), dev(k2, dt), dev(v, dt),
                             cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], mask)
     torch.cuda.synchronize()
@@ -199,6 +253,19 @@ def test_diff_parity_small(swa, dtype, B, Hq, Hkv, N, d, dv, W, s):
     ins = synth.diff_inputs(cfg)
     got = run_diff(swa, cfg, *ins)
     want = oracle.diff_full(*ins, W, s, cfg["scale"], cfg["lam"])
+    assert max_err(got, want) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,d,dv,W,s,dil,g", [(300, 64, 128, 40, 0, 2, 8), (200, 32, 64, 30, 9, 3, 1),
+                                              (260, 64, 64, 20, 0, 1, 100)])
+def test_diff_dilated_global_parity(swa, dtype, N, d, dv, W, s, dil, g):
+    banner(f"diff {dtype} N={N} d={d} dv={dv} W={W} s={s} dilation={dil} globals={g}")
+    cfg = dict(dtype=dtype, B=1, Hq=2, Hkv=1, N=N, d=d, dv=dv, window=W, stride=s, dilation=dil,
+               n_global=g, scale=1.0 / 8, lam=0.5, seed=N + W + dil)
+    ins = synth.diff_inputs(cfg)
+    got = run_diff(swa, cfg, *ins)
+    want = oracle.diff_full(*ins, W, s, cfg["scale"], cfg["lam"], dilation=dil, n_global=g)
     assert max_err(got, want) <= TOL[dtype]
 
 
