@@ -60,9 +60,10 @@ struct Lay {
 };
 
 // Waves per SIMD: two, unless two register stages of two K rows and a V row
-// (2 d + dv > 192) no longer fit half the register file.
+// (2 d + dv > 192), or two maps' 128-wide outputs, no longer fit half the
+// register file.
 template <int D, int DV, int NMAPS>
-constexpr int occupancy() { return NMAPS == 2 && 2 * D + DV > 192 ? 1 : 2; }
+constexpr int occupancy() { return NMAPS == 2 && (2 * D + DV > 192 || DV == 128) ? 1 : 2; }
 
 // LDS bytes of a workgroup: the waves' tiles, or the merge area if larger.
 template <int D, int DV, int NMAPS>
@@ -95,7 +96,7 @@ void decode_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char dsm[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
     const int split = blockIdx.x % p.splits;
     const int bg = blockIdx.x / p.splits;
@@ -103,7 +104,10 @@ void decode_kernel(Params p) {
     const int G = p.Hq / p.Hkv;
 
     // ---- this wave's virtual slots -------------------------------------------
-    const int L = p.seq_len ? p.seq_len[b] : p.N;
+    // wave-uniform (one sequence per workgroup); made explicit so the step
+    // loop below compiles as a uniform loop, not an exec-masked one whose
+    // load waits fall back to waiting for every outstanding load
+    const int L = __builtin_amdgcn_readfirstlane(p.seq_len ? p.seq_len[b] : p.N);
     const int nvalid = L <= 0 ? 0 : (L < p.window ? L : p.window);
     const int first = L - p.window > 0 ? L - p.window : 0;   // oldest position in the ring
     const int s_eff = first < p.n_sink ? first : p.n_sink;   // sink slots not in the ring
@@ -132,7 +136,7 @@ void decode_kernel(Params p) {
 
     // A step's K and V rows, 16 bytes per lane per load, consecutive lanes
     // reading consecutive chunks of a row (coalesced); virtual slots past the
-    // end are clamped to the last one (and masked out below).  Addresses are
+    // wave's run are clamped to its last one (and masked out below).  Addresses are
     // built from wave-uniform byte bases: selecting between two pointers held
     // in the argument block would turn into a per-lane load of the pointer.
     uintptr_t kring_b[NMAPS], ksink_b[NMAPS];
@@ -150,7 +154,7 @@ void decode_kernel(Params p) {
         for (int u = 0; u < Y::kChunks; ++u) {
             const int x = lane + 64 * u;
             const int r = x / (D / 8), c = x % (D / 8);
-            const int vs = base + r < T ? base + r : T - 1;
+            const int vs = base + r < v1 ? base + r : v1 - 1;
             const bool in_sink = vs < s_eff;
             const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * D) + c * 16;
 #pragma unroll
@@ -161,7 +165,7 @@ void decode_kernel(Params p) {
         for (int u = 0; u < Y::vChunks; ++u) {
             const int x = lane + 64 * u;
             const int r = x / (DV / 8), c = x % (DV / 8);
-            const int vs = base + r < T ? base + r : T - 1;
+            const int vs = base + r < v1 ? base + r : v1 - 1;
             const bool in_sink = vs < s_eff;
             const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * DV) + c * 16;
             vst[reg][u] = load16((in_sink ? vsink_b : vring_b) + off);
@@ -264,20 +268,20 @@ void decode_kernel(Params p) {
         }
     };
 
-    // two register stages: steps st (even) and st+1 (odd) alternate
-    if (nsteps > 0)
+    // Two register stages: steps st (even) and st+1 (odd) alternate.  Every
+    // load is issued unconditionally (a step past the wave's run re-reads its
+    // last slot and is fully masked, so it adds nothing): conditional loads
+    // would make the compiler's load-counter waits assume the fewest loads in
+    // flight and wait for the other stage too.
+    if (nsteps > 0) {
         load(0, 0);
-    if (nsteps > 1)
         load(1, 1);
-    for (int st = 0; st < nsteps; st += 2) {
-        store(0);
-        if (st + 2 < nsteps)
+        for (int st = 0; st < nsteps; st += 2) {
+            store(0);
             load(st + 2, 0);
-        compute(st);
-        if (st + 1 < nsteps) {
+            compute(st);
             store(1);
-            if (st + 3 < nsteps)
-                load(st + 3, 1);
+            load(st + 3, 1);
             compute(st + 1);
         }
     }

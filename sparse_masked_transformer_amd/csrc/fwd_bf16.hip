@@ -140,6 +140,16 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             for (int ks = 0; ks < D / 16; ++ks)
                 qf[m][rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
     }
+    // Wait for Q here.  Left pending, its first use inside the tile loop gets
+    // a count-based wait on every iteration, and the load counter runs in
+    // issue order: that wait would also wait for the next tile's prefetch.
+#pragma unroll
+    for (int m = 0; m < NMAPS; ++m)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                asm volatile("" ::"v"(qf[m][rg][ks]));
 
     // ---- the walk: prefix chunks, then band tiles --------------------------
     const int sk = p.mask.prefix_keys[qt];
@@ -149,6 +159,11 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int n_pre = (sk + 63) >> 6;
     const int band0 = p.mask.band_begin[qt];
     const int n_items = n_pre + (p.mask.row_ptr[qt + 1] - band0);
+    // The band tiles of a query tile are one ascending run of consecutive key
+    // tiles, so only the first is read (once, here).  A per-tile read of the
+    // list inside the loop is a vector load whose wait also waits for the
+    // next tile's prefetch, which would serialise every tile behind it.
+    const int band_t0 = p.mask.kv_tile[band0];
     const int64_t kv_head = (int64_t)(b * p.Hkv + g) * p.N;
 
     // window span in keys, and the dilation lattice: bit m set iff m is a
@@ -161,7 +176,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 
     // first key of item it (band tiles only)
     auto item_key0 = [&](int it) -> int {
-        return it >= n_pre ? p.mask.kv_tile[band0 + (it - n_pre)] * 64 : 0;
+        return it >= n_pre ? (band_t0 + (it - n_pre)) * 64 : 0;
     };
 
     // per-thread staging: thread t owns chunk column t % (D/8) of rows
