@@ -58,6 +58,9 @@ constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = 256;
 // dword 3 of a raw (untyped) buffer descriptor on gfx950
 constexpr int kBufferDword3 = 0x00020000;
+// cache-policy bits of the band-tile loads: sc0 (measured ~1% faster than
+// the default on the window prefill; slc alone or with sc0 is slower)
+constexpr int kTileLoadPolicy = 1;
 
 template <int D, int DV, int NMAPS>
 struct Cfg {
@@ -205,11 +208,11 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 #pragma unroll
                 for (int u = 0; u < C::kPer; ++u)
                     kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        krs[m], k_goff, (key0 + u * C::kRowStep) * D * 2, 0));
+                        krs[m], k_goff, (key0 + u * C::kRowStep) * D * 2, kTileLoadPolicy));
 #pragma unroll
             for (int u = 0; u < C::vPer; ++u)
                 vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, v_goff, (key0 + u * C::vRowStep) * DV * 2, 0));
+                    vrs, v_goff, (key0 + u * C::vRowStep) * DV * 2, kTileLoadPolicy));
         } else {
             // prefix chunk: key rows of prefix keys kn < sk (others read
             // past the end, i.e. zeros)
