@@ -93,12 +93,21 @@ struct Params {
     float lambda;
 };
 
-// EXT: the pattern may have a dilated window or global tokens; without it
-// both are compile-time absent and the plain window/stride code is unchanged.
-template <int D, int DV, int NMAPS, int RG, bool EXT>
+// MODE 0: the window (and stride) pattern.  MODE 1: the pattern may also
+// have a dilated window or global tokens (tested per cell).  MODE 2: a
+// dilated window alone, computed as a plain window of `window` keys on each
+// residue class r, r + dil, r + 2 dil, ... of the sequence (Learn: Sparse &
+// Sliding-Window Attention, §3b: row i attends keys i - m dil; rows and keys
+// of one class form an ordinary sliding-window problem of length
+// ceil((N - r) / dil)), so no cell off the lattice is computed.  In MODE 2
+// the workgroup's class is part of its tile index, row and key indices are
+// class-local, and position = r + dil * index.
+template <int D, int DV, int NMAPS, int RG, int MODE>
 __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
+    constexpr bool EXT = MODE == 1;
     const int dil = EXT ? p.dilation : 1;
     const int n_glob = EXT ? p.n_global : 0;
+    const int rdil = MODE == 2 ? p.dilation : 1;   // position stride of the rows
     using C = Cfg<D, DV, NMAPS>;
     constexpr int BM = 128 * RG;       // query rows per workgroup
     constexpr int ROWS = 32 * RG;      // query rows per wave (RG groups of 32)
@@ -108,7 +117,10 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int hl = lane >> 5;          // which half of the wave
     const int col = lane & 31;         // query column within a row group
     const int G = p.Hq / p.Hkv;
-    const int nq = p.mask.num_q_tiles;
+    // query tiles per (batch, head): MODE 2 has rdil classes of up to
+    // ceil(N / rdil) rows each
+    const int nq_cls = ((p.N + rdil - 1) / rdil + BM - 1) / BM;
+    const int nq = MODE == 2 ? nq_cls * rdil : p.mask.num_q_tiles;
 
     // ---- workgroup -> (b, kv head, query tile, head in group) -------------
     // Consecutive workgroup ids go to the 8 XCDs in turn; remap so each XCD
@@ -119,8 +131,15 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
         lid = (pid & 7) * (total >> 3) + (pid >> 3);
     const int hg = lid % G;
     int rest = lid / G;
-    const int qt = nq - 1 - (rest % nq);  // long (late) query tiles first
+    const int qt_lin = nq - 1 - (rest % nq);  // long (late) query tiles first
     rest /= nq;
+    const int qt = MODE == 2 ? qt_lin / rdil : qt_lin;   // tile within the class
+    const int res = MODE == 2 ? qt_lin % rdil : 0;       // residue class
+    const int Nr = MODE == 2 ? (p.N - res + rdil - 1) / rdil : p.N;  // rows of the class
+    // MODE 2: classes differ in length by one row; a class may have no rows
+    // (N < dil) or none in its last tile -- nothing to do (uniform exit)
+    if (MODE == 2 && qt * BM >= Nr)
+        return;
     const int g = rest % p.Hkv;
     const int b = rest / p.Hkv;
     const int h = g * G + hg;
@@ -135,8 +154,8 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     bf16x8 qf[NMAPS][RG][D / 16];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        const int row = my_row[rg] < p.N ? my_row[rg] : p.N - 1;
-        const int64_t q_off = ((int64_t)(b * p.Hq + h) * p.N + row) * D;
+        const int row = my_row[rg] < Nr ? my_row[rg] : Nr - 1;
+        const int64_t q_off = ((int64_t)(b * p.Hq + h) * p.N + res + rdil * row) * D;
 #pragma unroll
         for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
@@ -155,18 +174,22 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 asm volatile("" ::"v"(qf[m][rg][ks]));
 
     // ---- the walk: prefix chunks, then band tiles --------------------------
-    const int sk = p.mask.prefix_keys[qt];
+    // (MODE 2: the band of the class-local rows in closed form, no prefix)
+    const int cls_r0 = qt * BM, cls_r1 = (cls_r0 + BM < Nr ? cls_r0 + BM : Nr) - 1;
+    const int cls_lo = cls_r0 - p.window + 1 > 0 ? cls_r0 - p.window + 1 : 0;
+    const int sk = MODE == 2 ? 0 : p.mask.prefix_keys[qt];
     // prefix key kn: kn itself below gp (global columns), then stride multiples
     const int gp = n_glob < sk ? n_glob : sk;
     const int s_first = p.stride > 0 ? (gp + p.stride - 1) / p.stride - gp : 0;
     const int n_pre = (sk + 63) >> 6;
-    const int band0 = p.mask.band_begin[qt];
-    const int n_items = n_pre + (p.mask.row_ptr[qt + 1] - band0);
+    const int band0 = MODE == 2 ? 0 : p.mask.band_begin[qt];
+    const int n_items = MODE == 2 ? cls_r1 / 64 - cls_lo / 64 + 1
+                                  : n_pre + (p.mask.row_ptr[qt + 1] - band0);
     // The band tiles of a query tile are one ascending run of consecutive key
     // tiles, so only the first is read (once, here).  A per-tile read of the
     // list inside the loop is a vector load whose wait also waits for the
     // next tile's prefetch, which would serialise every tile behind it.
-    const int band_t0 = p.mask.kv_tile[band0];
+    const int band_t0 = MODE == 2 ? cls_lo / 64 : p.mask.kv_tile[band0];
     const int64_t kv_head = (int64_t)(b * p.Hkv + g) * p.N;
 
     // window span in keys, and the dilation lattice: bit m set iff m is a
@@ -197,8 +220,9 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                                                    p.N * D * 2, kBufferDword3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + kv_head * DV), 0, p.N * DV * 2, kBufferDword3);
-    const int k_goff = (kr0 * D + kc * 8) * 2;
-    const int v_goff = (vr0 * DV + vc * 8) * 2;
+    // a key row at class-local index j sits at position res + rdil * j
+    const int k_goff = (rdil * kr0 * D + kc * 8) * 2;
+    const int v_goff = (rdil * vr0 * DV + vc * 8) * 2;
     auto load_stage = [&](int it) {
         if (it >= n_pre) {
             // window tile: rows key0 .. key0+63
@@ -208,11 +232,11 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 #pragma unroll
                 for (int u = 0; u < C::kPer; ++u)
                     kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        krs[m], k_goff, (key0 + u * C::kRowStep) * D * 2, kTileLoadPolicy));
+                        krs[m], k_goff, (res + rdil * (key0 + u * C::kRowStep)) * D * 2, kTileLoadPolicy));
 #pragma unroll
             for (int u = 0; u < C::vPer; ++u)
                 vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, v_goff, (key0 + u * C::vRowStep) * DV * 2, kTileLoadPolicy));
+                    vrs, v_goff, (res + rdil * (key0 + u * C::vRowStep)) * DV * 2, kTileLoadPolicy));
         } else {
             // prefix chunk: key rows of prefix keys kn < sk (others read
             // past the end, i.e. zeros)
@@ -300,7 +324,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 full[rg] = (it + 1) * 64 <= sk;
             } else {
                 empty = key0 > r1 || (key0 + 63 < r0 - span && smask == 0);
-                full[rg] = !empty && key0 + 63 <= r0 && key0 + 64 <= p.N &&
+                full[rg] = !empty && key0 + 63 <= r0 && key0 + 64 <= Nr &&
                            ((dil == 1 && key0 >= r1 - p.window + 1) || key0 + 64 <= n_glob);
             }
             any = any || !empty;
@@ -551,12 +575,12 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
         for (int m = 0; m < NMAPS; ++m) {
             const float lt = l_run[m][rg] + __shfl_xor(l_run[m][rg], 32);
             inv[m] = lt > 0.f ? 1.f / lt : 0.f;
-            if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row[rg] < p.N)
-                p.lse[(int64_t)(b * p.Hq + h) * p.N + my_row[rg]] =
+            if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row[rg] < Nr)
+                p.lse[(int64_t)(b * p.Hq + h) * p.N + res + rdil * my_row[rg]] =
                     lt > 0.f ? (m_run[m][rg] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
         }
-        if (my_row[rg] < p.N) {
-            __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + my_row[rg]) * DV;
+        if (my_row[rg] < Nr) {
+            __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + res + rdil * my_row[rg]) * DV;
 #pragma unroll
             for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -579,15 +603,15 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 // registers per lane, which lets two waves share each SIMD (one wave's
 // softmax overlaps the other's matrix work).  Two-map kernels need more
 // state and run one wave per SIMD.
-template <int D, int DV, bool EXT>
+template <int D, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFwdRowGroups == 1 ? 2 : 1, 2)))
 void fwd_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 1, kFwdRowGroups, EXT>(p);
+    fwd_bf16_body<D, DV, 1, kFwdRowGroups, MODE>(p);
 }
 
-template <int D, int DV, bool EXT>
+template <int D, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) void diff_bf16_kernel(Params p) {
-    fwd_bf16_body<D, DV, 2, kDiffRowGroups, EXT>(p);
+    fwd_bf16_body<D, DV, 2, kDiffRowGroups, MODE>(p);
 }
 
 template <int D, int DV, int NMAPS>
@@ -611,18 +635,28 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     p.n_global = a.n_global;
     p.c = a.scale * kLog2e;
     p.lambda = a.lambda;
-    unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
     const bool ext = a.dilation != 1 || a.n_global != 0;
     if constexpr (NMAPS == 1) {
+        if (a.dilation > 1 && a.stride == 0 && a.n_global == 0) {
+            // one workgroup per (batch, head, residue class, class-local tile)
+            constexpr int BM = 128 * kFwdRowGroups;
+            const int64_t nq = ((static_cast<int64_t>(a.N) + a.dilation - 1) / a.dilation + BM - 1) / BM;
+            const unsigned grid = static_cast<unsigned>(nq * a.dilation * a.Hq * a.B);
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
+    if constexpr (NMAPS == 1) {
         if (ext)
-            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
     } else {
         if (ext)
-            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -153,6 +153,11 @@ PREFILL_EXT_CASES = [
     (1, 2, 2, 300, 32, 10, 0, 1, 300),      # every token global: full causal
     (1, 4, 4, 1000, 64, 128, 64, 2, 64),
     (1, 2, 2, 260, 32, 3, 5, 9, 130),       # global columns across whole tiles
+    # dilation alone runs as plain windows on the residue classes
+    (1, 2, 2, 385, 64, 9, 0, 3, 0),         # classes of 129, 128, 128 rows: empty last tiles
+    (1, 2, 1, 40, 32, 3, 0, 64, 0),         # N < dilation: classes without rows
+    (2, 4, 1, 1000, 128, 100, 0, 7, 0),
+    (1, 2, 2, 300, 32, 1000, 0, 2, 0),      # window longer than every class
 ]
 
 
