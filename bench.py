@@ -379,7 +379,7 @@ def main():
         "config": {"workload": "swa_prefill_bf16", "B": cfg["B"], "Hq": cfg["Hq"], "Hkv": cfg["Hkv"],
                    "N": cfg["N"], "d": cfg["d"], "window": cfg["window"], "stride": cfg["stride"],
                    "attended_cells": cells, "gflop_per_step": round(flops / 1e9, 3)},
-        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,128,1>",
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,128,0>",
                      "achieved": round(p["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_us": round(p["event_ms"] * 1e3, 2),
@@ -392,7 +392,8 @@ def main():
         dsrc = os.path.join(ROOT, "sparse_masked_transformer_amd", "csrc", "decode_bf16.hip")
         line["decode"] = {"workload": "window_decode_bf16", "value": round(dd["gbs"], 1), "unit": "GB/s",
                           "kv_gbs": round(dd["kv_gbs"], 1), "us_per_step": round(dd["event_ms"] * 1e3, 2),
-                          "roofline": {"bound": "hbm", "achieved": round(dd["gbs"], 1),
+                          "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,1>",
+                                       "achieved": round(dd["gbs"], 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": round(dd["gbs"] / PEAK_HBM_GBS, 4),
                                        "traffic": traffic_record(dsrc, "decode_bf16_window")}}
