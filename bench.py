@@ -168,7 +168,7 @@ def main():
                     help="minimum warm-up time per workload (0 for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "sink_decode", "diff_decode", "strided",
-                                       "global", "dilated", "diff", "copy"], default=None,
+                                       "global", "dilated", "diff", "tiny", "copy"], default=None,
                     help="time one workload only (for profiler runs); `copy` times a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -341,7 +341,7 @@ def main():
         del fins, fout
 
     # ---- tiny fp32 --------------------------------------------------------------
-    if args.only is None:
+    if args.only in (None, "tiny"):
         tcfg = synth.workload("tiny_swa_f32")
         tq, tk, tv = (dev(x, torch, torch.float32) for x in synth.prefill_inputs(tcfg))
         tmask = swa.swa_block_mask_build(tcfg["N"], tcfg["window"], 0, dtype=torch.float32, d=tcfg["d"])

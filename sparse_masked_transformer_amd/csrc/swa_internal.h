@@ -12,11 +12,13 @@ namespace swa {
 // Key tile size every attention kernel walks.
 constexpr int kBN = 64;
 // bf16 kernels: 4 waves per workgroup, each owning this many groups of 32
-// query rows (single map: 2, i.e. 256-row query tiles; two maps: 1).
+// query rows (128-row query tiles for one map and for two).
 constexpr int kFwdRowGroups = 1;
 constexpr int kDiffRowGroups = 1;
-// fp32 kernels: one thread per row of a 128-row query tile.
-constexpr int kF32BM = 128;
+// fp32 kernels: 8 lanes per row of a 32-row query tile (256-lane
+// workgroups: one wave per SIMD, the full 256-VGPR budget per lane, and
+// small problems spread over many compute units).
+constexpr int kF32BM = 32;
 
 // Query tile rows of the kernel serving (op, dtype).
 inline int tile_rows(swa_op_t op, swa_dtype_t dt) {

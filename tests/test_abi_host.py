@@ -79,7 +79,8 @@ def test_tile_config(swa):
                                  bm.value, bn.value)
     assert cfg(swa.SWA_OP_ATTN, swa.SWA_BF16, 128, 128) == (0, 128, 64)
     assert cfg(swa.SWA_OP_DIFF, swa.SWA_BF16, 64, 128) == (0, 128, 64)    # 32 rows per wave
-    assert cfg(swa.SWA_OP_ATTN, swa.SWA_F32, 32, 32) == (0, 128, 64)
+    assert cfg(swa.SWA_OP_ATTN, swa.SWA_F32, 32, 32) == (0, 32, 64)
+    assert cfg(swa.SWA_OP_DIFF, swa.SWA_F32, 64, 128) == (0, 32, 64)
     assert cfg(swa.SWA_OP_ATTN, swa.SWA_BF16, 48, 48)[0] == swa.SWA_ERR_INVALID_ARG
     assert cfg(swa.SWA_OP_ATTN, 7, 64, 64)[0] == swa.SWA_ERR_INVALID_ARG
     assert cfg(5, swa.SWA_BF16, 64, 64)[0] == swa.SWA_ERR_INVALID_ARG

@@ -158,6 +158,9 @@ PREFILL_EXT_CASES = [
     (1, 2, 1, 40, 32, 3, 0, 64, 0),         # N < dilation: classes without rows
     (2, 4, 1, 1000, 128, 100, 0, 7, 0),
     (1, 2, 2, 300, 32, 1000, 0, 2, 0),      # window longer than every class
+    # (window - 1) * dilation beyond the int32 range: every earlier lattice key attends
+    (1, 2, 2, 200, 64, 2 ** 30, 0, 5, 0),
+    (1, 2, 2, 150, 32, 2 ** 30, 7, 3, 0),
 ]
 
 
