@@ -11,9 +11,9 @@
 //
 // Workgroup: 256 threads = 4 waves; wave w owns query rows q0 .. q0+31 of the
 // 128-row query tile.  Per 64-key tile:
-//   * K (and V) tiles are staged HBM -> VGPR -> LDS, double-buffered; the
-//     next tile's loads are in flight while the current tile is computed.
-//     LDS rows are padded by 32 bytes (bank spread).
+//   * K (and V) tiles go HBM -> LDS by LDS-DMA (buffer_load ... lds, no
+//     registers), double-buffered; the next tile's loads are in flight while
+//     the current tile is computed.  LDS rows are padded (bank spread).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand,
 //     Q^T held in registers as the B operand).  In the 32x32 accumulator
 //     layout lane l holds query column l%32 and keys (r%4) + 8(r/4) + 4(l/32)
@@ -75,10 +75,7 @@ struct Cfg {
     static constexpr int kTile = 64 * kRow;                   // one K tile
     static constexpr int vTile = 64 * vRow;                   // one V tile
     static constexpr int stage = NMAPS * kTile + vTile;       // one buffer
-    static constexpr int kPer = D / 32;                       // K chunks per thread
-    static constexpr int vPer = DV / 32;                      // V chunks per thread
-    static constexpr int kRowStep = kThreads / (D / 8);       // rows between a thread's chunks
-    static constexpr int vRowStep = kThreads / (DV / 8);
+    static_assert(kTile % 1024 == 0 && vTile % 1024 == 0, "tiles are whole 1 KiB DMA chunks");
 };
 
 struct Params {
@@ -205,11 +202,6 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
         return it >= n_pre ? (band_t0 + (it - n_pre)) * 64 : 0;
     };
 
-    // per-thread staging: thread t owns chunk column t % (D/8) of rows
-    // t / (D/8) + u * kRowStep (same for V with DV)
-    const int kc = tid % (D / 8), kr0 = tid / (D / 8);
-    const int vc = tid % (DV / 8), vr0 = tid / (DV / 8);
-    u32x4 kst[NMAPS][C::kPer], vst[C::vPer];
     // Buffer descriptors over this (b, kv head)'s K and V rows: N rows of D
     // (DV) bf16.  Reads at or past row N return zeros (no clamping needed);
     // the per-tile offset lives in a scalar register.
@@ -220,55 +212,75 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                                                    p.N * D * 2, kBufferDword3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + kv_head * DV), 0, p.N * DV * 2, kBufferDword3);
-    // a key row at class-local index j sits at position res + rdil * j
-    const int k_goff = (rdil * kr0 * D + kc * 8) * 2;
-    const int v_goff = (rdil * vr0 * DV + vc * 8) * 2;
-    auto load_stage = [&](int it) {
+    // LDS-DMA staging: buffer_load ... lds writes 16 bytes per lane straight
+    // into LDS, lane l at bytes 16 l .. 16 l + 15 of a wave-uniform 1 KiB
+    // chunk.  A tile of 64 padded rows is a whole number of chunks; wave w
+    // writes chunks w, w + 4, ...  Lane l of chunk ch covers tile byte
+    // 1024 ch + 16 l, i.e. a row and a column of the padded layout; lanes on
+    // padding fetch their row's first 16 bytes (padding is never read).
+    constexpr int kCh = C::kTile / 1024, vCh = C::vTile / 1024;
+    constexpr int kChW = (kCh + 3) / 4, vChW = (vCh + 3) / 4;   // chunks per wave, at most
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int dk_row[kChW], dk_col[kChW], dv_row[vChW], dv_col[vChW];
+#pragma unroll
+    for (int j = 0; j < kChW; ++j) {
+        const int pos = (wv + 4 * j) * 1024 + 16 * lane;
+        const int cb = pos % C::kRow;
+        dk_row[j] = pos / C::kRow;
+        dk_col[j] = cb < 2 * D ? cb : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < vChW; ++j) {
+        const int pos = (wv + 4 * j) * 1024 + 16 * lane;
+        const int cb = pos % C::vRow;
+        dv_row[j] = pos / C::vRow;
+        dv_col[j] = cb < 2 * DV ? cb : 0;
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto dma_stage = [&](int it, int buf) {
+        char *sb = smem + buf * C::stage;
         if (it >= n_pre) {
-            // window tile: rows key0 .. key0+63
+            // window tile: rows key0 .. key0+63 (the tile offset is scalar)
             const int key0 = item_key0(it);
+            const int kso = (res + rdil * key0) * D * 2, vso = (res + rdil * key0) * DV * 2;
 #pragma unroll
-            for (int m = 0; m < NMAPS; ++m)
+            for (int j = 0; j < kChW; ++j)
+                if (wv + 4 * j < kCh)
 #pragma unroll
-                for (int u = 0; u < C::kPer; ++u)
-                    kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        krs[m], k_goff, (res + rdil * (key0 + u * C::kRowStep)) * D * 2, kTileLoadPolicy));
+                    for (int m = 0; m < NMAPS; ++m)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + 4 * j) * 1024), 16,
+                            rdil * dk_row[j] * D * 2 + dk_col[j], kso, 0, kTileLoadPolicy);
 #pragma unroll
-            for (int u = 0; u < C::vPer; ++u)
-                vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, v_goff, (res + rdil * (key0 + u * C::vRowStep)) * DV * 2, kTileLoadPolicy));
+            for (int j = 0; j < vChW; ++j)
+                if (wv + 4 * j < vCh)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + 4 * j) * 1024), 16,
+                        rdil * dv_row[j] * DV * 2 + dv_col[j], vso, 0, kTileLoadPolicy);
         } else {
-            // prefix chunk: key rows of prefix keys kn < sk (others read
-            // past the end, i.e. zeros)
+            // prefix chunk: key rows of prefix keys kn < sk (others read past
+            // the end, i.e. zeros)
 #pragma unroll
-            for (int u = 0; u < C::kPer; ++u) {
-                const int kn = it * 64 + kr0 + u * C::kRowStep;
-                const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
+            for (int j = 0; j < kChW; ++j)
+                if (wv + 4 * j < kCh) {
+                    const int kn = it * 64 + dk_row[j];
+                    const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m)
-                    kst[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        krs[m], (row * D + kc * 8) * 2, 0, 0));
-            }
+                    for (int m = 0; m < NMAPS; ++m)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + 4 * j) * 1024), 16,
+                            row * D * 2 + dk_col[j], 0, 0, 0);
+                }
 #pragma unroll
-            for (int u = 0; u < C::vPer; ++u) {
-                const int kn = it * 64 + vr0 + u * C::vRowStep;
-                const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
-                vst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, (row * DV + vc * 8) * 2, 0, 0));
-            }
+            for (int j = 0; j < vChW; ++j)
+                if (wv + 4 * j < vCh) {
+                    const int kn = it * 64 + dv_row[j];
+                    const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + 4 * j) * 1024), 16,
+                        row * DV * 2 + dv_col[j], 0, 0, 0);
+                }
         }
-    };
-    auto store_stage = [&](int buf) {
-        char *kbase = smem + buf * C::stage + kr0 * C::kRow + kc * 16;
-        char *vbase = smem + buf * C::stage + NMAPS * C::kTile + vr0 * C::vRow + vc * 16;
-#pragma unroll
-        for (int u = 0; u < C::kPer; ++u)
-#pragma unroll
-            for (int m = 0; m < NMAPS; ++m)
-                *reinterpret_cast<u32x4 *>(kbase + m * C::kTile + u * C::kRowStep * C::kRow) = kst[m][u];
-#pragma unroll
-        for (int u = 0; u < C::vPer; ++u)
-            *reinterpret_cast<u32x4 *>(vbase + u * C::vRowStep * C::vRow) = vst[u];
     };
 
     // per-lane LDS read bases (everything else is a compile-time offset)
@@ -290,16 +302,16 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 o[m][rg][db] = f32x16{};
         }
 
-    if (n_items > 0) {
-        load_stage(0);
-        store_stage(0);
-    }
+    if (n_items > 0)
+        dma_stage(0, 0);
     __syncthreads();
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
-        // prefetch the next item (the last item re-reads itself; harmless)
-        load_stage(it + 1 < n_items ? it + 1 : it);
+        // prefetch the next item straight into the other buffer, whose last
+        // reads ended at the previous barrier
+        if (it + 1 < n_items)
+            dma_stage(it + 1, buf ^ 1);
 
         // ---- classify this tile for each row group of this wave -------------
         const bool pre = it < n_pre;
@@ -484,17 +496,22 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             };
             // V^T fragments of key half kb, shared by every row group
             bf16x8 va[2][DV / 32];
+            auto join = [](i16x4 t0, i16x4 t1) {
+                const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
+                const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
+                return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            };
+            // (the compiler waits for the outstanding LDS-DMA loads before
+            // these reads, as it cannot tell their buffers apart; the next
+            // tile's loads, issued at the top of the tile, have landed by then)
             auto read_v = [&](int kb) {
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db) {
                         const char *a = vb_base + (kb * 32 + hf * 16) * C::vRow + db * 64;
-                        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a);
-                        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 8 * C::vRow));
-                        const bf16x4 a0 = __builtin_bit_cast(bf16x4, t0);
-                        const bf16x4 a1 = __builtin_bit_cast(bf16x4, t1);
-                        va[hf][db] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        va[hf][db] = join(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a),
+                                          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 8 * C::vRow)));
                     }
             };
             // O^T += V^T P^T over the 32 keys of half kb
@@ -563,8 +580,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 pv(rg, 1);
         }
 
-        store_stage(buf ^ 1);
-        __syncthreads();
+        __syncthreads();   // preceded by a wait for this wave's DMA loads
     }
 
     // ---- epilogue: O / l -> bf16 ------------------------------------------
