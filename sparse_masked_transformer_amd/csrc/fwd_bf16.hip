@@ -58,8 +58,9 @@ constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = 256;
 // dword 3 of a raw (untyped) buffer descriptor on gfx950
 constexpr int kBufferDword3 = 0x00020000;
-// cache-policy bits of the band-tile loads: sc0 (measured ~1% faster than
-// the default on the window prefill; slc alone or with sc0 is slower)
+// cache-policy bits of the band-tile loads: sc0 (with LDS-DMA staging equal
+// to the default and to sc1 on the window prefill; nt, alone or with sc0, is
+// ~8% slower)
 constexpr int kTileLoadPolicy = 1;
 
 template <int D, int DV, int NMAPS>
