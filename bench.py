@@ -114,17 +114,25 @@ def dev(x, torch, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).cuda()
 
 
+def kernel_build_sha(kernel_src):
+    """Hash of a kernel's source together with the build script (its compiler
+    flags), the key under which its measured traffic is stored."""
+    h = hashlib.sha256()
+    for f in (kernel_src, os.path.join(ROOT, "sparse_masked_transformer_amd", "build.py")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(kernel_src, key):
-    """HBM traffic per launch measured with rocprofv3 counters, if the kernel
-    source has not changed since (null otherwise)."""
+    """HBM traffic per launch measured with rocprofv3 counters, if neither the
+    kernel source nor the build flags have changed since (null otherwise)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(key)
     if not rec:
         return None
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    return rec["bytes_per_launch"] if rec.get("kernel_sha256") == sha else None
+    return rec["bytes_per_launch"] if rec.get("kernel_sha256") == kernel_build_sha(kernel_src) else None
 
 
 def cpu_baseline(q, k, v, cfg, out_gpu, budget_s, threads):
