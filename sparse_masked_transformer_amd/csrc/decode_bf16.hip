@@ -59,9 +59,11 @@ struct Lay {
     static constexpr int vChunks = kDecodeStep * DV / 8 / 64;
 };
 
-// Waves per SIMD: two, unless two register stages of two K rows and a V row
-// (2 d + dv > 192), or two maps' 128-wide outputs, no longer fit half the
-// register file.
+// Waves per SIMD, at least: two, unless two register stages of two K rows
+// and a V row (2 d + dv > 192), or two maps' 128-wide outputs, no longer fit
+// half the register file.  (A minimum only: a maximum makes the compiler
+// declare extra registers to enforce it, which would keep small head sizes
+// from running more waves.)
 template <int D, int DV, int NMAPS>
 constexpr int occupancy() { return NMAPS == 2 && (2 * D + DV > 192 || DV == 128) ? 1 : 2; }
 
@@ -90,7 +92,7 @@ struct Params {
 
 template <int D, int DV, int NMAPS>
 __global__ __launch_bounds__(64 * kDecodeMaxWaves)
-__attribute__((amdgpu_waves_per_eu(occupancy<D, DV, NMAPS>(), occupancy<D, DV, NMAPS>())))
+__attribute__((amdgpu_waves_per_eu(occupancy<D, DV, NMAPS>())))
 void decode_kernel(Params p) {
     using Y = Lay<D, DV, NMAPS>;
     extern __shared__ __attribute__((aligned(16))) char dsm[];
