@@ -5,12 +5,13 @@
 // Three small integer kernels on the caller's stream:
 //   1. per query tile, the length of its list            (one thread / tile)
 //   2. exclusive scan of the lengths into row_ptr          (one workgroup)
-//   3. per list entry, its key tile, kind and cell count   (one wave / tile)
+//   3. per list entry, its key tile, kind and cell count   (one workgroup of
+//      four waves per query tile)
 // Cell counts of band tiles: for the plain window (+ stride) pattern a per-row
 // closed form (row i attends the keys max(0, i-window+1) .. i plus the
 // multiples of stride in 0 .. i-window, an interval and a progression clipped
 // to the key tile); with a dilated window or global tokens every cell of the
-// tile is tested.  Prefix-only tiles: every row attends every prefix key of
+// tile is tested, the wave's lanes splitting its rows.  Prefix-only tiles: every row attends every prefix key of
 // the tile, so their count is rows x prefix keys.
 #include "swa_internal.h"
 
@@ -28,6 +29,16 @@ __device__ bool allowed(const Pattern &p, int64_t i, int64_t j) {
     const int64_t dist = i - j;
     return (dist % p.dilation == 0 && dist / p.dilation < p.window) ||
            (p.stride > 0 && j % p.stride == 0) || j < p.n_global || i < p.n_global;
+}
+
+// The same predicate in 32-bit arithmetic for indices 0 <= i, j < N (N is at
+// most 2^22), the window span clamped to N: the per-cell counting loop.
+__device__ bool allowed32(int i, int j, int N, int span, int dil, int stride, int n_global) {
+    if (j > i || i >= N)
+        return false;
+    const int dist = i - j;
+    return (dist <= span && dist % dil == 0) || (stride > 0 && j % stride == 0) || j < n_global ||
+           i < n_global;
 }
 
 struct TileGeom {
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(1024) void mask_scan_kernel(int32_t *row_ptr, int n
     }
 }
 
-__global__ __launch_bounds__(64) void mask_fill_kernel(const int32_t *row_ptr, int32_t *kv_tile,
+__global__ __launch_bounds__(256) void mask_fill_kernel(const int32_t *row_ptr, int32_t *kv_tile,
                                                        uint8_t *kind, int32_t *cells,
                                                        int32_t *prefix_keys, int32_t *band_begin,
                                                        Pattern p) {
@@ -114,7 +125,33 @@ __global__ __launch_bounds__(64) void mask_fill_kernel(const int32_t *row_ptr, i
     const bool plain = p.dilation == 1 && p.n_global == 0;
     const int64_t i0 = q * p.bm, i1 = i0 + p.bm < p.N ? i0 + p.bm : p.N;
     const int64_t count = g.n_band + g.n_prefix;
-    for (int64_t e = threadIdx.x; e < count; e += blockDim.x) {
+    if (!plain) {
+        // dilated window or global tokens: each wave takes every fourth band
+        // tile, its lanes splitting the tile's rows (each lane tests its rows'
+        // cells), then a wave sum of the counts.  dist <= span with dist a
+        // multiple of the dilation is the window term of the predicate.
+        const int span = static_cast<int>((p.window - 1) * p.dilation < p.N ? (p.window - 1) * p.dilation : p.N);
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        for (int64_t e = g.n_prefix + wave; e < count; e += blockDim.x >> 6) {
+            const int64_t t = g.t_lo + (e - g.n_prefix);
+            const int j0 = static_cast<int>(t * p.bn), j1 = static_cast<int>(j0 + p.bn < p.N ? j0 + p.bn : p.N);
+            int c = 0;
+            for (int i = static_cast<int>(i0) + lane; i < i1; i += 64)
+                for (int j = j0; j < j1; ++j)
+                    c += allowed32(i, j, static_cast<int>(p.N), span, static_cast<int>(p.dilation),
+                                   static_cast<int>(p.stride), static_cast<int>(p.n_global));
+            for (int off = 32; off > 0; off >>= 1)
+                c += __shfl_xor(c, off);
+            if (lane == 0) {
+                kv_tile[base + e] = static_cast<int32_t>(t);
+                kind[base + e] = c == (i1 - i0) * (j1 - j0) ? 0 : 1;
+                cells[base + e] = static_cast<int32_t>(c);
+            }
+        }
+    }
+    // prefix-only tiles (closed form), and every tile of the plain pattern
+    const int64_t n_lane = plain ? count : g.n_prefix;
+    for (int64_t e = threadIdx.x; e < n_lane; e += blockDim.x) {
         int64_t t;
         if (e < g.a)
             t = e;  // holds a global column
@@ -135,22 +172,16 @@ __global__ __launch_bounds__(64) void mask_fill_kernel(const int32_t *row_ptr, i
             c = (i1 - i0) * (ng + nsk);
             k = 2;
         } else {
-            if (plain) {
-                for (int64_t i = i0; i < i1; ++i) {
-                    const int64_t lo = i - p.window + 1 > 0 ? i - p.window + 1 : 0;
-                    const int64_t a = lo > j0 ? lo : j0;
-                    const int64_t b = i < j1 - 1 ? i : j1 - 1;
-                    if (b >= a)
-                        c += b - a + 1;
-                    if (p.stride > 0) {
-                        const int64_t sb = j1 < lo ? j1 : lo;
-                        c += multiples_in(j0, sb, p.stride);
-                    }
+            for (int64_t i = i0; i < i1; ++i) {
+                const int64_t lo = i - p.window + 1 > 0 ? i - p.window + 1 : 0;
+                const int64_t a = lo > j0 ? lo : j0;
+                const int64_t b = i < j1 - 1 ? i : j1 - 1;
+                if (b >= a)
+                    c += b - a + 1;
+                if (p.stride > 0) {
+                    const int64_t sb = j1 < lo ? j1 : lo;
+                    c += multiples_in(j0, sb, p.stride);
                 }
-            } else {
-                for (int64_t i = i0; i < i1; ++i)
-                    for (int64_t j = j0; j < j1; ++j)
-                        c += allowed(p, i, j);
             }
             k = c == (i1 - i0) * (j1 - j0) ? 0 : 1;
         }
@@ -175,7 +206,7 @@ hipError_t launch_block_mask_build(const swa_block_mask_t &m, hipStream_t stream
     hipLaunchKernelGGL(mask_count_kernel, dim3((nq + 255) / 256), dim3(256), 0, stream, m.row_ptr,
                        nq, p);
     hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(1024), 0, stream, m.row_ptr, nq);
-    hipLaunchKernelGGL(mask_fill_kernel, dim3(nq), dim3(64), 0, stream, m.row_ptr, m.kv_tile,
+    hipLaunchKernelGGL(mask_fill_kernel, dim3(nq), dim3(256), 0, stream, m.row_ptr, m.kv_tile,
                        m.kind, m.cells, m.prefix_keys, m.band_begin, p);
     return hipGetLastError();
 }
