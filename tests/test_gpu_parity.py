@@ -222,6 +222,24 @@ def test_prefill_workload_sampled(swa, name):
     assert np.all(np.isfinite(got))
 
 
+def test_prefill_longest_sequence(swa):
+    # N at its maximum (2^22): the largest byte offsets the kernels form (row *
+    # d * 2 and the tile offsets, up to 1 GiB at d=128) and stride keys near
+    # the end of the sequence
+    N = swa.SWA_MAX_N
+    cfg = dict(dtype="bf16", B=1, Hq=1, Hkv=1, N=N, d=128, dv=128, window=128, stride=1 << 20,
+               scale=1.0 / math.sqrt(128), seed=21)
+    banner(f"prefill at N={N} (sampled rows)")
+    q, k, v = synth.prefill_inputs(cfg)
+    got = run_prefill(swa, cfg, q, k, v).reshape(-1, cfg["dv"])
+    rows = synth.sample_rows(N, 192, seed=22, must=[0, 63, 64, 127, 128, (1 << 20) - 1, 1 << 20,
+                                                   (1 << 20) + 1, 3 << 20, N - 129, N - 65, N - 2,
+                                                   N - 1])
+    want = oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], rows)
+    assert max_err(got[rows], want) <= TOL["bf16"]
+    assert np.all(np.isfinite(got[N - 4096:]))
+
+
 def test_prefill_deterministic(swa):
     cfg = dict(dtype="bf16", B=1, Hq=8, Hkv=2, N=1500, d=128, dv=128, window=300, stride=0,
                scale=1.0 / math.sqrt(128), seed=5)
