@@ -345,6 +345,20 @@ def test_decode_parity(swa, dtype, B, Hq, Hkv, W, d, lens):
     assert max_err(got, want) <= TOL[dtype]
 
 
+def test_decode_longest_ring(swa):
+    # a ring of 2^22 slots (the largest window the boundary accepts): split
+    # across workgroups, byte offsets up to 1 GiB per ring; one sequence
+    # past the ring's first wrap, one still filling it
+    W = swa.SWA_MAX_N
+    cfg = dict(dtype="bf16", B=2, Hq=4, Hkv=1, window=W, d=64, dv=64, position=0, n_sink=0,
+               scale=0.125, seed=23)
+    banner(f"decode with a ring of {W} slots")
+    ins = synth.decode_inputs(cfg, seq_len=[W + 1000, W // 2 + 3])
+    got = run_decode(swa, cfg, ins)
+    want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"])
+    assert max_err(got, want) <= TOL["bf16"]
+
+
 def test_decode_default_length(swa):
     cfg = dict(dtype="bf16", B=2, Hq=4, Hkv=1, window=128, d=64, dv=64, position=500, n_sink=0,
                scale=0.125, seed=3)
