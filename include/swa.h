@@ -33,6 +33,11 @@
  *   - Every argument is checked on the host BEFORE any HIP call; a rejected
  *     call launches nothing and returns a negative swa_status_t.  Launch
  *     failures return SWA_ERR_HIP.
+ *   - Each call launches its kernels as one-dimensional grids, and a dispatch
+ *     holds at most 2^32 - 1 work-items: a call that would need more returns
+ *     SWA_ERR_UNSUPPORTED.  Forward calls have 256 lanes per workgroup and
+ *     one workgroup per (batch, query head, query tile); the decode calls'
+ *     launches are sized by their own work split.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - No global mutable state: calls on different streams may overlap as
  *     long as their output buffers do not.
@@ -178,7 +183,8 @@ size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int 
  *              on entry do not matter.
  *   stride     must be 0: stride keys older than the window are not in the
  *              ring (SWA_ERR_UNSUPPORTED otherwise).
- * bf16 needs Hq / Hkv <= 16 (SWA_ERR_UNSUPPORTED otherwise).
+ * bf16 needs Hq / Hkv <= 16; B * Hq and B * Hkv * window must fit int32
+ * (SWA_ERR_UNSUPPORTED otherwise).
  */
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,

@@ -19,9 +19,8 @@ namespace swa {
 namespace {
 
 constexpr int kSub = 16;   // keys staged per LDS step
-constexpr int kTPR = 8;    // lanes per query row
-
-constexpr int kF32Threads = kF32BM * kTPR;   // lanes per forward workgroup
+constexpr int kTPR = kF32TPR;            // lanes per query row
+constexpr int kF32Threads = kFwdThreads;   // lanes per forward workgroup
 
 __device__ inline float dot4(float4 a, float4 b, float acc) {
     acc = fmaf(a.x, b.x, acc);
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 
 template <int D, int DV, int NMAPS>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
-    unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
+    const unsigned grid = static_cast<unsigned>(fwd_workgroups(a, SWA_F32));
     hipLaunchKernelGGL((fwd_f32_kernel<D, DV, NMAPS>), dim3(grid), dim3(kF32Threads), 0, stream,
                        static_cast<const float *>(a.q[0]), static_cast<const float *>(a.k[0]),
                        static_cast<const float *>(a.q[1]), static_cast<const float *>(a.k[1]),

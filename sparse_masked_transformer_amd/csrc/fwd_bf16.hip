@@ -54,7 +54,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;       // log2 units the running maximum may lag
 constexpr float kNegBig = -1e30f;    // running maximum before any key
-constexpr int kThreads = 256;
+constexpr int kThreads = kFwdThreads;
 // dword 3 of a raw (untyped) buffer descriptor on gfx950
 constexpr int kBufferDword3 = 0x00020000;
 // cache-policy bits of the band-tile loads: sc0 (with LDS-DMA staging equal
@@ -655,17 +655,13 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     p.lambda = a.lambda;
     const bool ext = a.dilation != 1 || a.n_global != 0;
+    const unsigned grid = static_cast<unsigned>(fwd_workgroups(a, SWA_BF16));
     if constexpr (NMAPS == 1) {
-        if (a.dilation > 1 && a.stride == 0 && a.n_global == 0) {
-            // one workgroup per (batch, head, residue class, class-local tile)
-            constexpr int BM = 128 * kFwdRowGroups;
-            const int64_t nq = ((static_cast<int64_t>(a.N) + a.dilation - 1) / a.dilation + BM - 1) / BM;
-            const unsigned grid = static_cast<unsigned>(nq * a.dilation * a.Hq * a.B);
+        if (fwd_by_residue_class(a, SWA_BF16)) {
             hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
             return hipGetLastError();
         }
     }
-    unsigned grid = static_cast<unsigned>(a.mask.num_q_tiles) * a.Hq * a.B;
     if constexpr (NMAPS == 1) {
         if (ext)
             hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 1>), dim3(grid), dim3(kThreads), 0, stream, p);

@@ -100,6 +100,12 @@ int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride, int dilat
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 
+int fwd_run(const swa::FwdArgs &a, swa_dtype_t dt, hipStream_t stream) {
+    if (swa::fwd_workgroups(a, dt) * swa::kFwdThreads > swa::kMaxGridItems)
+        return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
+    return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
+}
+
 swa::MaskView view_of(const swa_block_mask_t *m) {
     return swa::MaskView{m->row_ptr, m->kv_tile, m->kind, m->prefix_keys, m->band_begin,
                          m->num_q_tiles};
@@ -122,6 +128,20 @@ DecodePlan decode_plan(int B, int Hkv, int slots) {
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     const int64_t spw = (steps + splits * waves - 1) / (splits * waves);
     return DecodePlan{static_cast<int>(waves), static_cast<int>(splits), static_cast<int>(spw)};
+}
+
+int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt) {
+    const int64_t rows = static_cast<int64_t>(a.B) * a.Hq;   // (sequence, query head) pairs
+    if (dt == SWA_F32) {
+        // 64-lane workgroups of 64 / kF32TPR rows
+        const int64_t per_wg = 64 / kF32TPR;
+        return (rows + per_wg - 1) / per_wg * 64;
+    }
+    const DecodePlan plan = decode_plan(a.B, a.Hkv, a.window + a.n_sink);
+    const int64_t main_items = static_cast<int64_t>(a.B) * a.Hkv * plan.splits * 64 * plan.waves;
+    // the combine kernel: 256-lane workgroups of 4 rows
+    const int64_t combine_items = plan.splits > 1 ? (rows + 3) / 4 * 256 : 0;
+    return main_items > combine_items ? main_items : combine_items;
 }
 }  // namespace swa
 
@@ -162,7 +182,8 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         return SWA_ERR_INVALID_ARG;
     if (dt == SWA_BF16 && a.Hq / a.Hkv > 16)
         return SWA_ERR_UNSUPPORTED;  // the query heads of a group share one 16-column tile
-    if (static_cast<int64_t>(a.B) * a.Hkv * (a.window + a.n_sink) > INT32_MAX)
+    if (static_cast<int64_t>(a.B) * a.Hkv * (a.window + a.n_sink) > INT32_MAX ||
+        static_cast<int64_t>(a.B) * a.Hq > INT32_MAX)
         return SWA_ERR_UNSUPPORTED;
     if (!head_dim_ok(a.d) || !head_dim_ok(a.dv))
         return SWA_ERR_UNSUPPORTED;
@@ -171,6 +192,8 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         return SWA_ERR_UNSUPPORTED;
     if (stride != 0)
         return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
+    if (swa::decode_launch_items(a, dt) > swa::kMaxGridItems)
+        return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
     const size_t need = decode_ws_bytes(a.nmaps, a.B, a.Hq, a.Hkv, a.dv, a.window, a.n_sink);
     if (need > 0 && (a.workspace == nullptr || !aligned16(a.workspace) || workspace_bytes < need))
         return SWA_ERR_WORKSPACE;
@@ -267,7 +290,7 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     a.lambda = 0.f;
     a.nmaps = 1;
     a.mask = view_of(mask);
-    return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
+    return fwd_run(a, dt, stream);
 }
 
 size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int dv, int window,
@@ -401,7 +424,7 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
     a.lambda = lambda;
     a.nmaps = 2;
     a.mask = view_of(mask);
-    return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
+    return fwd_run(a, dt, stream);
 }
 
 const char *swa_strerror(int status) {

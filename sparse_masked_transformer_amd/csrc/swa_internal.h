@@ -19,6 +19,13 @@ constexpr int kDiffRowGroups = 1;
 // workgroups: one wave per SIMD, the full 256-VGPR budget per lane, and
 // small problems spread over many compute units).
 constexpr int kF32BM = 32;
+constexpr int kF32TPR = 8;   // lanes per query row (fp32 forward and decode)
+// Lanes per workgroup of every forward kernel.
+constexpr int kFwdThreads = 256;
+static_assert(kF32BM * kF32TPR == kFwdThreads, "fp32 forward tile = one 256-lane workgroup");
+// A dispatch holds at most 2^32 - 1 work-items per grid dimension; every
+// launch here uses one dimension.
+constexpr int64_t kMaxGridItems = 0xffffffffLL;
 
 // Query tile rows of the kernel serving (op, dtype).
 inline int tile_rows(swa_op_t op, swa_dtype_t dt) {
@@ -50,6 +57,25 @@ struct FwdArgs {
     int nmaps;      // 1 or 2
     MaskView mask;
 };
+
+// The bf16 single-map forward over a dilated window alone (no stride, no
+// global tokens) walks each residue class of the rows mod dilation as a dense
+// band: one workgroup per (batch, head, residue class, class-local tile).
+// Every other forward has one workgroup per (batch, head, query tile).
+inline bool fwd_by_residue_class(const FwdArgs &a, swa_dtype_t dt) {
+    return dt == SWA_BF16 && a.nmaps == 1 && a.dilation > 1 && a.stride == 0 && a.n_global == 0;
+}
+
+// Workgroups of the forward launch for (a, dt).
+inline int64_t fwd_workgroups(const FwdArgs &a, swa_dtype_t dt) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.Hq;
+    if (fwd_by_residue_class(a, dt)) {
+        const int64_t bm = 128 * kFwdRowGroups;
+        const int64_t rows = (static_cast<int64_t>(a.N) + a.dilation - 1) / a.dilation;
+        return (rows + bm - 1) / bm * a.dilation * heads;
+    }
+    return static_cast<int64_t>(a.mask.num_q_tiles) * heads;
+}
 
 // k-th prefix key (0 <= k < count) of a query tile whose prefix-only tiles
 // hold `count` prefix keys: the global columns 0 .. g'-1 (g' = min(n_global,
@@ -92,6 +118,8 @@ struct DecodePlan {
 // Plan for B*Hkv (sequence, key/value head) pairs and at most `slots` cache
 // slots (window + sink slots) per pair.
 DecodePlan decode_plan(int B, int Hkv, int slots);
+// Work-items of the largest dispatch one decode call makes.
+int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt);
 // fp32 count of the (max, sum) section of the decode workspace for `parts`
 // partial results, padded so the output section starts 16-byte aligned.
 inline int64_t decode_ws_ml_floats(int64_t parts) { return (parts * 2 + 3) / 4 * 4; }

@@ -160,6 +160,21 @@ def test_fwd_rejections(swa):
                mask=fake_mask(swa, 1 << 12, 32, 0)) == U   # flat row index beyond int32
 
 
+def test_fwd_rejects_grids_beyond_one_dispatch(swa):
+    """Row indices fit int32 but the launch would need 2^32 or more work-items
+    (256 lanes per workgroup): rejected on the host, nothing launched."""
+    U = swa.SWA_ERR_UNSUPPORTED
+    # bf16, ragged N = 130: 2 query tiles of 128 rows for each of 2^23 heads
+    assert fwd(swa, B=1 << 10, Hq=1 << 13, Hkv=1 << 13, N=130,
+               mask=fake_mask(swa, 130, 32, 0)) == U
+    # fp32 (32-row tiles of 256 lanes): 2^30 rows -> 2^33 work-items
+    assert fwd(swa, dt=0, B=1, Hq=1 << 9, Hkv=1, N=1 << 21,
+               mask=fake_mask(swa, 1 << 21, 32, 0, bm=32)) == U
+    m = fake_mask(swa, 1 << 21, 32, 0, bm=32)
+    assert swa.lib.diff_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1 << 9, 1, 1 << 21, 64,
+                                 64, 32, 0, 1, 0, 0.125, 0.5, ctypes.byref(m), None) == U
+
+
 def dec(swa, q=FAKE, kr=FAKE, vr=FAKE, out=FAKE, sl=None, ws=FAKE, wsb=None, dt=1, B=2, Hq=8,
         Hkv=2, N=10, d=128, W=64, s=0, scale=0.1):
     if wsb is None:
@@ -183,6 +198,17 @@ def test_decode_rejections(swa):
     assert dec(swa, ws=0) == WS
     assert dec(swa, wsb=swa.swa_attn_decode_workspace_bytes(2, 8, 2, 128, 64) - 4) == WS
     assert dec(swa, ws=FAKE + 8) == WS
+
+
+def test_decode_rejects_grids_beyond_one_dispatch(swa):
+    U = swa.SWA_ERR_UNSUPPORTED
+    # a one-slot window gives one 64-lane workgroup per (sequence, key/value
+    # head): 2^30 pairs -> 2^36 work-items
+    assert dec(swa, B=1 << 15, Hq=1 << 15, Hkv=1 << 15, W=1, d=64, wsb=0) == U
+    # fp32: 8 lanes per (sequence, query head), 2^29 of them -> 2^32 work-items
+    assert dec(swa, dt=0, B=1 << 15, Hq=1 << 14, Hkv=1 << 14, W=1, d=64, wsb=0) == U
+    # B * Hq beyond int32 (B * Hkv * window fits)
+    assert dec(swa, B=1 << 16, Hq=1 << 16, Hkv=1 << 12, W=1, d=64, wsb=0) == U
 
 
 def test_decode_sinks_rejections(swa):
