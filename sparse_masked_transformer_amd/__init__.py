@@ -99,8 +99,45 @@ def _ptr(t):
 
 
 def _need(t, name):
-    if not (t.is_cuda and t.is_contiguous()):
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous tensor on the GPU")
+
+
+def _dims(t, name, n):
+    _need(t, name)
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _expect(t, name, shape, dtype, device):
+    """The kernels index every buffer from the sizes passed with it: a buffer
+    of another shape, dtype or device would be read or written out of
+    bounds, so it is rejected here, before the call."""
+    _need(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_mask(mask, device):
+    if mask.row_ptr.device != device:
+        raise ValueError(f"block mask is on {mask.row_ptr.device}, expected {device}")
+
+
+def _expect_seq_len(seq_len, B, device):
+    if seq_len is not None:
+        _expect(seq_len, "seq_len", (B,), torch.int32, device)
+
+
+def _expect_workspace(workspace, device):
+    if workspace is not None:
+        _need(workspace, "workspace")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
 
 
 def swa_strerror(status):
@@ -183,12 +220,17 @@ def swa_mask_dense(N, window, stride=0, device="cuda", dilation=1, n_global=0):
 
 def swa_attn_fwd(q, k, v, window, stride, scale, mask, out=None, lse=None):
     """Masked attention forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d]; returns out."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _expect(t, n, (B, Hkv, N, d), q.dtype, dev)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", (B, Hq, N, d), q.dtype, dev)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq, N), torch.float32, dev)
+    _expect_mask(mask, dev)
     _check(_lib.swa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
                              Hkv, N, d, window, stride, mask.dilation, mask.n_global, float(scale),
                              ctypes.byref(mask.c), _stream(q)), "swa_attn_fwd")
@@ -209,13 +251,17 @@ def _workspace(workspace, nbytes, device):
 def swa_attn_decode(q, k_ring, v_ring, seq_len, scale, workspace=None, out=None, N=0, stride=0):
     """One decode step.  q [B,Hq,d]; k_ring/v_ring [B,Hkv,W,d]; seq_len int32
     [B] on the GPU (or None: every sequence at length N); returns out."""
-    for t, n in ((q, "q"), (k_ring, "k_ring"), (v_ring, "v_ring")):
-        _need(t, n)
-    B, Hq, d = q.shape
-    Hkv, W = k_ring.shape[1], k_ring.shape[2]
-    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W), q.device)
+    B, Hq, d = _dims(q, "q", 3)
+    _, Hkv, W, _ = _dims(k_ring, "k_ring", 4)
+    dev = q.device
+    for t, n in ((k_ring, "k_ring"), (v_ring, "v_ring")):
+        _expect(t, n, (B, Hkv, W, d), q.dtype, dev)
+    _expect_seq_len(seq_len, B, dev)
+    _expect_workspace(workspace, dev)
+    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W), dev)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", (B, Hq, d), q.dtype, dev)
     _check(_lib.swa_attn_decode(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(out), _ptr(seq_len),
                                 _ptr(ws), ws_bytes, _dtype_code(q), B, Hq, Hkv, N, d, W, stride,
                                 float(scale), _stream(q)), "swa_attn_decode")
@@ -226,15 +272,20 @@ def swa_attn_decode_sinks(q, k_sink, v_sink, k_ring, v_ring, seq_len, scale, wor
                           out=None, N=0):
     """Decode step with sink slots.  k_sink/v_sink [B,Hkv,S,d] hold positions
     0..S-1; k_ring/v_ring [B,Hkv,W,d]; returns out [B,Hq,d]."""
-    for t, n in ((q, "q"), (k_sink, "k_sink"), (v_sink, "v_sink"), (k_ring, "k_ring"),
-                 (v_ring, "v_ring")):
-        _need(t, n)
-    B, Hq, d = q.shape
-    Hkv, S, W = k_ring.shape[1], k_sink.shape[2], k_ring.shape[2]
-    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W, S),
-                              q.device)
+    B, Hq, d = _dims(q, "q", 3)
+    _, Hkv, W, _ = _dims(k_ring, "k_ring", 4)
+    S = _dims(k_sink, "k_sink", 4)[2]
+    dev = q.device
+    for t, n in ((k_ring, "k_ring"), (v_ring, "v_ring")):
+        _expect(t, n, (B, Hkv, W, d), q.dtype, dev)
+    for t, n in ((k_sink, "k_sink"), (v_sink, "v_sink")):
+        _expect(t, n, (B, Hkv, S, d), q.dtype, dev)
+    _expect_seq_len(seq_len, B, dev)
+    _expect_workspace(workspace, dev)
+    ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, W, S), dev)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", (B, Hq, d), q.dtype, dev)
     _check(_lib.swa_attn_decode_sinks(_ptr(q), _ptr(k_sink), _ptr(v_sink), S, _ptr(k_ring),
                                       _ptr(v_ring), _ptr(out), _ptr(seq_len), _ptr(ws), ws_bytes,
                                       _dtype_code(q), B, Hq, Hkv, N, d, W, float(scale), _stream(q)),
@@ -246,15 +297,20 @@ def diff_attn_decode(q1, k1_ring, q2, k2_ring, v_ring, seq_len, scale, lam, work
                      out=None, N=0):
     """Differential decode step.  q1/q2 [B,Hq,d]; k1_ring/k2_ring [B,Hkv,W,d];
     v_ring [B,Hkv,W,dv]; returns out [B,Hq,dv]."""
-    for t, n in ((q1, "q1"), (k1_ring, "k1_ring"), (q2, "q2"), (k2_ring, "k2_ring"),
-                 (v_ring, "v_ring")):
-        _need(t, n)
-    B, Hq, d = q1.shape
-    Hkv, W, dv = v_ring.shape[1], v_ring.shape[2], v_ring.shape[3]
+    B, Hq, d = _dims(q1, "q1", 3)
+    _, Hkv, W, dv = _dims(v_ring, "v_ring", 4)
+    dev, dt = q1.device, q1.dtype
+    _expect(q2, "q2", (B, Hq, d), dt, dev)
+    for t, n in ((k1_ring, "k1_ring"), (k2_ring, "k2_ring")):
+        _expect(t, n, (B, Hkv, W, d), dt, dev)
+    _expect(v_ring, "v_ring", (B, Hkv, W, dv), dt, dev)
+    _expect_seq_len(seq_len, B, dev)
+    _expect_workspace(workspace, dev)
     ws, ws_bytes = _workspace(workspace, swa_attn_decode_workspace_bytes(B, Hq, Hkv, dv, W, 0,
-                                                                         SWA_OP_DIFF), q1.device)
+                                                                         SWA_OP_DIFF), dev)
     if out is None:
-        out = torch.empty((B, Hq, dv), dtype=q1.dtype, device=q1.device)
+        out = torch.empty((B, Hq, dv), dtype=dt, device=dev)
+    _expect(out, "out", (B, Hq, dv), dt, dev)
     _check(_lib.diff_attn_decode(_ptr(q1), _ptr(k1_ring), _ptr(q2), _ptr(k2_ring), _ptr(v_ring),
                                  _ptr(out), _ptr(seq_len), _ptr(ws), ws_bytes, _dtype_code(q1), B,
                                  Hq, Hkv, N, d, dv, W, float(scale), float(lam), _stream(q1)),
@@ -264,12 +320,18 @@ def diff_attn_decode(q1, k1_ring, q2, k2_ring, v_ring, seq_len, scale, lam, work
 
 def diff_attn_fwd(q1, k1, q2, k2, v, window, stride, scale, lam, mask, out=None):
     """Differential attention: (softmax(q1 k1^T s + log M) - lam softmax(q2 k2^T s + log M)) v."""
-    for t, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")):
-        _need(t, n)
-    B, Hq, N, d = q1.shape
-    Hkv, dv = k1.shape[1], v.shape[3]
+    B, Hq, N, d = _dims(q1, "q1", 4)
+    Hkv = _dims(k1, "k1", 4)[1]
+    dv = _dims(v, "v", 4)[3]
+    dev, dt = q1.device, q1.dtype
+    _expect(q2, "q2", (B, Hq, N, d), dt, dev)
+    for t, n in ((k1, "k1"), (k2, "k2")):
+        _expect(t, n, (B, Hkv, N, d), dt, dev)
+    _expect(v, "v", (B, Hkv, N, dv), dt, dev)
     if out is None:
-        out = torch.empty((B, Hq, N, dv), dtype=q1.dtype, device=q1.device)
+        out = torch.empty((B, Hq, N, dv), dtype=dt, device=dev)
+    _expect(out, "out", (B, Hq, N, dv), dt, dev)
+    _expect_mask(mask, dev)
     _check(_lib.diff_attn_fwd(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out),
                               _dtype_code(q1), B, Hq, Hkv, N, d, dv, window, stride, mask.dilation,
                               mask.n_global, float(scale), float(lam), ctypes.byref(mask.c),
