@@ -159,16 +159,6 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             for (int ks = 0; ks < D / 16; ++ks)
                 qf[m][rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
     }
-    // Wait for Q here.  Left pending, its first use inside the tile loop gets
-    // a count-based wait on every iteration, and the load counter runs in
-    // issue order: that wait would also wait for the next tile's prefetch.
-#pragma unroll
-    for (int m = 0; m < NMAPS; ++m)
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                asm volatile("" ::"v"(qf[m][rg][ks]));
 
     // ---- the walk: prefix chunks, then band tiles --------------------------
     // (MODE 2: the band of the class-local rows in closed form, no prefix)
@@ -305,6 +295,18 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     if (n_items > 0)
         dma_stage(0, 0);
     __syncthreads();
+    // Wait for Q here, after the first tile's staging, so that its loads
+    // overlap the block-mask reads and the first tile's loads.  Left pending
+    // into the loop, its first use there gets a count-based wait on every
+    // iteration, and as the load counter runs in issue order that wait would
+    // also wait for the next tile's prefetch.
+#pragma unroll
+    for (int m = 0; m < NMAPS; ++m)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                asm volatile("" ::"v"(qf[m][rg][ks]));
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
