@@ -9,20 +9,28 @@
 // is the sum of the 8 lanes' partial dot products (xor shuffles).
 //
 // Forward: a 32-row query tile (256 lanes) walks the tiles the block mask
-// lists (prefix keys first, then band tiles), staging 16 keys at a time in LDS
-// with the next 16 keys' loads in flight, and updates an online softmax once
-// per 16-key block (Attention Variants Compared, "Flash style softmax").
+// lists (prefix keys first, then band tiles), staging 16 to 64 keys at a time
+// in LDS (more for smaller heads) with the next step's loads in flight, and
+// updates an online softmax once per block of 16 keys (8 with two maps)
+// (Attention Variants Compared, "Flash style softmax").
 // Decode: one row per (sequence, query head) over the sink and ring slots.
 #include "swa_internal.h"
 
 namespace swa {
 namespace {
 
-constexpr int kSub = 16;   // keys staged per LDS step
+// Keys staged per LDS step, for kw float4 groups of K and V per key: at most
+// 16 KiB per step, so that small heads walk a key tile in few steps (each
+// step costs a barrier and a load latency).
+constexpr int sub_keys(int kw) { return kw <= 16 ? 64 : (kw <= 32 ? 32 : 16); }
+// 16 bytes as a native vector (arrays of HIP's float4 struct are kept in
+// scratch memory rather than in registers)
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 constexpr int kTPR = kF32TPR;            // lanes per query row
 constexpr int kF32Threads = kFwdThreads;   // lanes per forward workgroup
 
-__device__ inline float dot4(float4 a, float4 b, float acc) {
+__device__ inline float dot4(f32x4v a, f32x4v b, float acc) {
     acc = fmaf(a.x, b.x, acc);
     acc = fmaf(a.y, b.y, acc);
     acc = fmaf(a.z, b.z, acc);
@@ -45,11 +53,52 @@ __device__ inline float row_sum(float x) {
     return x;
 }
 
-__device__ inline void fma4(float4 &acc, float e, float4 v) {
+__device__ inline void fma4(f32x4v &acc, float e, f32x4v v) {
     acc.x = fmaf(e, v.x, acc.x);
     acc.y = fmaf(e, v.y, acc.y);
     acc.z = fmaf(e, v.z, acc.z);
     acc.w = fmaf(e, v.w, acc.w);
+}
+
+// Staging of the forward kernel's K and V rows, one step of kSub keys at a
+// time.  A step's kSub * KW float4 groups are spread over the workgroup:
+// group c of a key is K of map c / (D/4) below NMAPS * D/4, else V.  Slot u
+// of a lane holds group x = lane + u * threads; where a step is not a whole
+// number of workgroup rows, the lanes past its end repeat its last group
+// (same value, same LDS address).  Plain functions rather than lambdas that
+// capture one another: through a chain of captured closures the compiler
+// kept the staged registers in scratch memory.
+template <int kSub, int KW>
+__device__ __forceinline__ int stage_slot(int u) {
+    const int x = static_cast<int>(threadIdx.x) + u * kF32Threads;
+    return (kSub * KW) % kF32Threads == 0 || x < kSub * KW ? x : kSub * KW - 1;
+}
+
+// First key of step s (prefix items count their keys from 0).
+template <int kSub>
+__device__ __forceinline__ int step_key0(int s, int n_pre, const int32_t *kv_tile, int band0) {
+    const int it = s / (kBN / kSub), sub = s % (kBN / kSub);
+    return it < n_pre ? it * kBN + sub * kSub : kv_tile[band0 + it - n_pre] * kBN + sub * kSub;
+}
+
+// Loads of one step's groups into registers, one load per slot through a
+// selected row pointer (no branch on the group's kind).
+template <int D, int DV, int NMAPS, int kSub, int KW, int PER>
+__device__ __forceinline__ void fetch_step(f32x4v (&stage)[PER], int key0, bool pre, int sk, int stride,
+                                           int n_global, int N, int64_t kvh, const float *k0p,
+                                           const float *k1p, const float *vp) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int x = stage_slot<kSub, KW>(u);
+        const int r = x / KW, c = x % KW;
+        const int kk = key0 + r;
+        const int j = pre ? (kk < sk ? prefix_key(kk, sk, stride, n_global) : 0) : (kk < N ? kk : N - 1);
+        const bool is_k = c < NMAPS * D / 4;
+        const float *base = is_k ? (c < D / 4 ? k0p : k1p) : vp;
+        const int width = is_k ? D : DV;
+        const int col = is_k ? c % (D / 4) : c - NMAPS * D / 4;
+        stage[u] = reinterpret_cast<const f32x4v *>(base + (kvh + j) * width)[col];
+    }
 }
 
 template <int D, int DV, int NMAPS>
@@ -62,9 +111,11 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float *q0p, 
     static_assert(D % (4 * kTPR) == 0 && DV % (4 * kTPR) == 0, "head sizes are multiples of 32");
     constexpr int QG = D / 4 / kTPR, VG = DV / 4 / kTPR;   // float4 groups per lane
     constexpr int KW = NMAPS * D / 4 + DV / 4;             // float4 groups per staged key
+    constexpr int kSub = sub_keys(KW);                     // keys per LDS step
+    static_assert(kBN % kSub == 0, "steps tile a key tile");
     constexpr int PER = (kSub * KW + kF32Threads - 1) / kF32Threads;
-    __shared__ float4 ks[NMAPS][kSub][D / 4];
-    __shared__ float4 vs[kSub][DV / 4];
+    __shared__ f32x4v ks[NMAPS][kSub][D / 4];
+    __shared__ f32x4v vs[kSub][DV / 4];
 
     const int nq = mask.num_q_tiles;
     const int qt = blockIdx.x % nq;
@@ -78,17 +129,17 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float *q0p, 
     const int64_t lo64 = static_cast<int64_t>(i) - static_cast<int64_t>(window - 1) * dilation;
     const int lo = lo64 > -1 ? static_cast<int>(lo64) : -1;
 
-    float4 qr[NMAPS][QG], o[NMAPS][VG];
+    f32x4v qr[NMAPS][QG], o[NMAPS][VG];
     float m[NMAPS], l[NMAPS];
 #pragma unroll
     for (int mp = 0; mp < NMAPS; ++mp) {
-        const float4 *src = reinterpret_cast<const float4 *>((mp == 0 ? q0p : q1p) + ((int64_t)bh * N + irow) * D);
+        const f32x4v *src = reinterpret_cast<const f32x4v *>((mp == 0 ? q0p : q1p) + ((int64_t)bh * N + irow) * D);
 #pragma unroll
         for (int k = 0; k < QG; ++k)
             qr[mp][k] = src[t + kTPR * k];
 #pragma unroll
         for (int k = 0; k < VG; ++k)
-            o[mp][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            o[mp][k] = f32x4v{0.f, 0.f, 0.f, 0.f};
         m[mp] = -__builtin_inff();
         l[mp] = 0.f;
     }
@@ -100,54 +151,32 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float *q0p, 
     const int n_steps = n_items * (kBN / kSub);
     const int64_t kvh = (int64_t)(b * Hkv + g) * N;
 
-    // first key of step s's 16-key block (prefix items count their keys from 0)
-    auto block_key0 = [&](int s) {
-        const int it = s / (kBN / kSub), sub = s % (kBN / kSub);
-        return it < n_pre ? it * kBN + sub * kSub : mask.kv_tile[band0 + it - n_pre] * kBN + sub * kSub;
+    f32x4v stage[PER];
+    auto fetch = [&](int s) {   // loads of step s, in flight until the next store
+        fetch_step<D, DV, NMAPS, kSub, KW, PER>(stage, step_key0<kSub>(s, n_pre, mask.kv_tile, band0),
+                                                 s / (kBN / kSub) < n_pre, sk, stride, n_global, N,
+                                                 kvh, k0p, k1p, vp);
     };
-    // loads of step s's staged float4 groups into registers
-    float4 stage[PER];
-    auto fetch = [&](int s) {
-        const bool pre = s / (kBN / kSub) < n_pre;
-        const int key0 = block_key0(s);
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int x = threadIdx.x + u * kF32Threads;
-            if (x < kSub * KW) {
-                const int r = x / KW, c = x % KW;
-                const int kk = key0 + r;
-                const int j = pre ? (kk < sk ? prefix_key(kk, sk, stride, n_global) : 0)
-                                  : (kk < N ? kk : N - 1);
-                if (c < NMAPS * D / 4)
-                    stage[u] = reinterpret_cast<const float4 *>((c < D / 4 ? k0p : k1p) + (kvh + j) * D)[c % (D / 4)];
-                else
-                    stage[u] = reinterpret_cast<const float4 *>(vp + (kvh + j) * DV)[c - NMAPS * D / 4];
-            }
-        }
-    };
-
     if (n_steps > 0)
         fetch(0);
     for (int s = 0; s < n_steps; ++s) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int x = threadIdx.x + u * kF32Threads;
-            if (x < kSub * KW) {
-                const int r = x / KW, c = x % KW;
-                if (c < NMAPS * D / 4)
-                    ks[c / (D / 4)][r][c % (D / 4)] = stage[u];
-                else
-                    vs[r][c - NMAPS * D / 4] = stage[u];
-            }
+            const int x = stage_slot<kSub, KW>(u);
+            const int r = x / KW, c = x % KW;
+            const bool is_k = c < NMAPS * D / 4;
+            const int ck = is_k ? c : 0, cv = is_k ? 0 : c - NMAPS * D / 4;
+            f32x4v *dst = is_k ? &ks[ck / (D / 4)][r][ck % (D / 4)] : &vs[r][cv];
+            *dst = stage[u];
         }
         __syncthreads();
         const bool pre = s / (kBN / kSub) < n_pre;
-        const int key0 = block_key0(s);
+        const int key0 = step_key0<kSub>(s, n_pre, mask.kv_tile, band0);
         if (s + 1 < n_steps)
             fetch(s + 1);   // in flight while this block is processed
 
         // softmax blocks of KB keys (8 with two maps, to bound live registers)
-        constexpr int KB = NMAPS == 2 ? kSub / 2 : kSub;
+        constexpr int KB = NMAPS == 2 ? 8 : 16;
 #pragma unroll 1
         for (int hb = 0; hb < kSub; hb += KB) {
             // the mask of the KB keys.  Band keys: j <= i, and j in the dilated
@@ -215,11 +244,11 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float *q0p, 
     }
     if (i >= N)
         return;
-    float4 *dst = reinterpret_cast<float4 *>(out + ((int64_t)bh * N + i) * DV);
+    f32x4v *dst = reinterpret_cast<f32x4v *>(out + ((int64_t)bh * N + i) * DV);
 #pragma unroll
     for (int k = 0; k < VG; ++k) {
         const float r0 = 1.f / l[0];
-        float4 x = make_float4(o[0][k].x * r0, o[0][k].y * r0, o[0][k].z * r0, o[0][k].w * r0);
+        f32x4v x = f32x4v{o[0][k].x * r0, o[0][k].y * r0, o[0][k].z * r0, o[0][k].w * r0};
         if (NMAPS == 2) {
             const float r1 = lambda / l[NMAPS - 1];
             x.x -= o[NMAPS - 1][k].x * r1;
@@ -249,26 +278,26 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     const int first = L - a.window > 0 ? L - a.window : 0;
     const int s_eff = first < a.n_sink ? first : a.n_sink;
     const int64_t kv = static_cast<int64_t>(b) * a.Hkv + g;
-    float4 qr[NMAPS][QG], o[NMAPS][VG];
+    f32x4v qr[NMAPS][QG], o[NMAPS][VG];
     float m[NMAPS], l[NMAPS];
     for (int mp = 0; mp < NMAPS; ++mp) {
-        const float4 *qv = static_cast<const float4 *>(a.q[mp]) + static_cast<int64_t>(row) * (D / 4);
+        const f32x4v *qv = static_cast<const f32x4v *>(a.q[mp]) + static_cast<int64_t>(row) * (D / 4);
 #pragma unroll
         for (int k = 0; k < QG; ++k)
             qr[mp][k] = qv[t + kTPR * k];
 #pragma unroll
         for (int k = 0; k < VG; ++k)
-            o[mp][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            o[mp][k] = f32x4v{0.f, 0.f, 0.f, 0.f};
         m[mp] = -__builtin_inff();
         l[mp] = 0.f;
     }
     for (int s = 0; s < s_eff + nvalid; ++s) {
         const bool in_sink = s < s_eff;
         const int64_t r = in_sink ? kv * a.n_sink + s : kv * a.window + (s - s_eff);
-        const float4 *vrow = static_cast<const float4 *>(in_sink ? a.v_sink : a.v_ring) + r * (DV / 4);
+        const f32x4v *vrow = static_cast<const f32x4v *>(in_sink ? a.v_sink : a.v_ring) + r * (DV / 4);
         for (int mp = 0; mp < NMAPS; ++mp) {
-            const float4 *krow =
-                static_cast<const float4 *>(in_sink ? a.k_sink[mp] : a.k_ring[mp]) + r * (D / 4);
+            const f32x4v *krow =
+                static_cast<const f32x4v *>(in_sink ? a.k_sink[mp] : a.k_ring[mp]) + r * (D / 4);
             float x = 0.f;
 #pragma unroll
             for (int k = 0; k < QG; ++k)
@@ -280,7 +309,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             l[mp] = l[mp] * alpha + e;
 #pragma unroll
             for (int k = 0; k < VG; ++k) {
-                const float4 v = vrow[t + kTPR * k];
+                const f32x4v v = vrow[t + kTPR * k];
                 o[mp][k].x = fmaf(o[mp][k].x, alpha, e * v.x);
                 o[mp][k].y = fmaf(o[mp][k].y, alpha, e * v.y);
                 o[mp][k].z = fmaf(o[mp][k].z, alpha, e * v.z);
@@ -291,11 +320,11 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     }
     if (!live)
         return;
-    float4 *dst = static_cast<float4 *>(a.out) + static_cast<int64_t>(row) * (DV / 4);
+    f32x4v *dst = static_cast<f32x4v *>(a.out) + static_cast<int64_t>(row) * (DV / 4);
 #pragma unroll
     for (int k = 0; k < VG; ++k) {
         const float r0 = l[0] > 0.f ? 1.f / l[0] : 0.f;
-        float4 x = make_float4(o[0][k].x * r0, o[0][k].y * r0, o[0][k].z * r0, o[0][k].w * r0);
+        f32x4v x = f32x4v{o[0][k].x * r0, o[0][k].y * r0, o[0][k].z * r0, o[0][k].w * r0};
         if (NMAPS == 2) {
             const float r1 = l[NMAPS - 1] > 0.f ? a.lambda / l[NMAPS - 1] : 0.f;
             x.x -= o[NMAPS - 1][k].x * r1;
