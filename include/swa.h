@@ -35,9 +35,9 @@
  *     failures return SWA_ERR_HIP.
  *   - Each call launches its kernels as one-dimensional grids, and a dispatch
  *     holds at most 2^32 - 1 work-items: a call that would need more returns
- *     SWA_ERR_UNSUPPORTED.  Forward calls have 256 lanes per workgroup and
- *     one workgroup per (batch, query head, query tile); the decode calls'
- *     launches are sized by their own work split.
+ *     SWA_ERR_UNSUPPORTED.  Forward calls have one workgroup per (batch,
+ *     query head, query tile) of 256 lanes (512 for diff_attn_fwd in bf16);
+ *     the decode calls' launches are sized by their own work split.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - No global mutable state: calls on different streams may overlap as
  *     long as their output buffers do not.

@@ -9,8 +9,12 @@
 // running weighted sum for its 128 query rows while it walks the key tiles
 // the block mask lists.
 //
-// Workgroup: 256 threads = 4 waves; wave w owns query rows q0 .. q0+31 of the
-// 128-row query tile.  Per 64-key tile:
+// Workgroup: 4 waves per score map; wave w of a map owns query rows
+// q0 + 32 w .. q0 + 32 w + 31 of the 128-row query tile.  With two maps
+// (differential attention) waves 0-3 compute the first map and waves 4-7 the
+// second, on the same rows and the same staged K and V tiles; at the end the
+// second map's waves hand lambda * O2 / l2 to the first's through LDS.  Per
+// 64-key tile:
 //   * K (and V) tiles go HBM -> LDS by LDS-DMA (buffer_load ... lds, no
 //     registers), double-buffered; the next tile's loads are in flight while
 //     the current tile is computed.  LDS rows are padded (bank spread).
@@ -55,6 +59,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;       // log2 units the running maximum may lag
 constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = kFwdThreads;
+constexpr int kDiffThreads = kDiffFwdThreads;
 // dword 3 of a raw (untyped) buffer descriptor on gfx950
 constexpr int kBufferDword3 = 0x00020000;
 // cache-policy bits of the band-tile loads: sc0 (with LDS-DMA staging equal
@@ -101,6 +106,7 @@ struct Params {
 // class-local, and position = r + dil * index.
 template <int D, int DV, int NMAPS, int RG, int MODE>
 __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
+    constexpr int WAVES = 4 * NMAPS;   // waves per workgroup: 4 per score map
     constexpr bool EXT = MODE == 1;
     const int dil = EXT ? p.dilation : 1;
     const int n_glob = EXT ? p.n_global : 0;
@@ -108,9 +114,13 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     using C = Cfg<D, DV, NMAPS>;
     constexpr int BM = 128 * RG;       // query rows per workgroup
     constexpr int ROWS = 32 * RG;      // query rows per wave (RG groups of 32)
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::stage];
+    // two K/V stages; with two maps also the second map's output at the end
+    constexpr int kXo = NMAPS == 2 ? 4 * RG * (DV / 32) * 16 * 64 * 4 : 0;
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::stage > kXo ? 2 * C::stage : kXo];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave_id = tid >> 6;
+    const int wmap = wave_id >> 2;     // score map of this wave
+    const int wave = wave_id & 3;      // its rows within the query tile
     const int hl = lane >> 5;          // which half of the wave
     const int col = lane & 31;         // query column within a row group
     const int G = p.Hq / p.Hkv;
@@ -148,16 +158,14 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
         my_row[rg] = q0 + 32 * rg + col;
 
     // ---- Q^T fragments (B operand), one per 16-channel step ----------------
-    bf16x8 qf[NMAPS][RG][D / 16];
+    bf16x8 qf[RG][D / 16];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const int row = my_row[rg] < Nr ? my_row[rg] : Nr - 1;
         const int64_t q_off = ((int64_t)(b * p.Hq + h) * p.N + res + rdil * row) * D;
 #pragma unroll
-        for (int m = 0; m < NMAPS; ++m)
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                qf[m][rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[m] + q_off + ks * 16 + hl * 8);
+        for (int ks = 0; ks < D / 16; ++ks)
+            qf[rg][ks] = *reinterpret_cast<const bf16x8 *>(p.q[wmap] + q_off + ks * 16 + hl * 8);
     }
 
     // ---- the walk: prefix chunks, then band tiles --------------------------
@@ -209,19 +217,19 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     // 1024 ch + 16 l, i.e. a row and a column of the padded layout; lanes on
     // padding fetch their row's first 16 bytes (padding is never read).
     constexpr int kCh = C::kTile / 1024, vCh = C::vTile / 1024;
-    constexpr int kChW = (kCh + 3) / 4, vChW = (vCh + 3) / 4;   // chunks per wave, at most
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int kChW = (kCh + WAVES - 1) / WAVES, vChW = (vCh + WAVES - 1) / WAVES;   // chunks per wave, at most
+    const int wv = __builtin_amdgcn_readfirstlane(wave_id);
     int dk_row[kChW], dk_col[kChW], dv_row[vChW], dv_col[vChW];
 #pragma unroll
     for (int j = 0; j < kChW; ++j) {
-        const int pos = (wv + 4 * j) * 1024 + 16 * lane;
+        const int pos = (wv + WAVES * j) * 1024 + 16 * lane;
         const int cb = pos % C::kRow;
         dk_row[j] = pos / C::kRow;
         dk_col[j] = cb < 2 * D ? cb : 0;
     }
 #pragma unroll
     for (int j = 0; j < vChW; ++j) {
-        const int pos = (wv + 4 * j) * 1024 + 16 * lane;
+        const int pos = (wv + WAVES * j) * 1024 + 16 * lane;
         const int cb = pos % C::vRow;
         dv_row[j] = pos / C::vRow;
         dv_col[j] = cb < 2 * DV ? cb : 0;
@@ -235,39 +243,39 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             const int kso = (res + rdil * key0) * D * 2, vso = (res + rdil * key0) * DV * 2;
 #pragma unroll
             for (int j = 0; j < kChW; ++j)
-                if (wv + 4 * j < kCh)
+                if (wv + WAVES * j < kCh)
 #pragma unroll
                     for (int m = 0; m < NMAPS; ++m)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + 4 * j) * 1024), 16,
+                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + WAVES * j) * 1024), 16,
                             rdil * dk_row[j] * D * 2 + dk_col[j], kso, 0, kTileLoadPolicy);
 #pragma unroll
             for (int j = 0; j < vChW; ++j)
-                if (wv + 4 * j < vCh)
+                if (wv + WAVES * j < vCh)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + 4 * j) * 1024), 16,
+                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + WAVES * j) * 1024), 16,
                         rdil * dv_row[j] * DV * 2 + dv_col[j], vso, 0, kTileLoadPolicy);
         } else {
             // prefix chunk: key rows of prefix keys kn < sk (others read past
             // the end, i.e. zeros)
 #pragma unroll
             for (int j = 0; j < kChW; ++j)
-                if (wv + 4 * j < kCh) {
+                if (wv + WAVES * j < kCh) {
                     const int kn = it * 64 + dk_row[j];
                     const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
 #pragma unroll
                     for (int m = 0; m < NMAPS; ++m)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + 4 * j) * 1024), 16,
+                            krs[m], (lds_void *)(sb + m * C::kTile + (wv + WAVES * j) * 1024), 16,
                             row * D * 2 + dk_col[j], 0, 0, 0);
                 }
 #pragma unroll
             for (int j = 0; j < vChW; ++j)
-                if (wv + 4 * j < vCh) {
+                if (wv + WAVES * j < vCh) {
                     const int kn = it * 64 + dv_row[j];
                     const int row = kn < gp ? kn : (kn < sk ? (s_first + kn) * p.stride : p.N);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + 4 * j) * 1024), 16,
+                        vrs, (lds_void *)(sb + NMAPS * C::kTile + (wv + WAVES * j) * 1024), 16,
                         row * DV * 2 + dv_col[j], 0, 0, 0);
                 }
         }
@@ -279,18 +287,16 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * C::vRow + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
     // ---- running state (per map, per row group) --------------------------------
-    f32x16 o[NMAPS][RG][DV / 32];
-    float m_run[NMAPS][RG], l_run[NMAPS][RG];
+    f32x16 o[RG][DV / 32];
+    float m_run[RG], l_run[RG];
 #pragma unroll
-    for (int m = 0; m < NMAPS; ++m)
+    for (int rg = 0; rg < RG; ++rg) {
+        m_run[rg] = kNegBig;
+        l_run[rg] = 0.f;
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            m_run[m][rg] = kNegBig;
-            l_run[m][rg] = 0.f;
-#pragma unroll
-            for (int db = 0; db < DV / 32; ++db)
-                o[m][rg][db] = f32x16{};
-        }
+        for (int db = 0; db < DV / 32; ++db)
+            o[rg][db] = f32x16{};
+    }
 
     if (n_items > 0)
         dma_stage(0, 0);
@@ -301,12 +307,10 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     // iteration, and as the load counter runs in issue order that wait would
     // also wait for the next tile's prefetch.
 #pragma unroll
-    for (int m = 0; m < NMAPS; ++m)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                asm volatile("" ::"v"(qf[m][rg][ks]));
+        for (int ks = 0; ks < D / 16; ++ks)
+            asm volatile("" ::"v"(qf[rg][ks]));
 
     for (int it = 0; it < n_items; ++it) {
         const int buf = it & 1;
@@ -349,25 +353,20 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             const char *vb_base = smem + buf * C::stage + NMAPS * C::kTile + v_lane;
 
             // Scores of row group rg, key half kb (32 keys): S^T = K Q^T.
-            f32x16 sh[RG][2][NMAPS];
-            bf16x8 ka[NMAPS][D / 16];
+            f32x16 sh[RG][2];
+            bf16x8 ka[D / 16];
             auto read_k = [&](int kb) {
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m)
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks)
-                        ka[m][ks] = *reinterpret_cast<const bf16x8 *>(
-                            kb_base + m * C::kTile + kb * 32 * C::kRow + ks * 32);
+                for (int ks = 0; ks < D / 16; ++ks)
+                    ka[ks] = *reinterpret_cast<const bf16x8 *>(
+                        kb_base + wmap * C::kTile + kb * 32 * C::kRow + ks * 32);
             };
             auto qk = [&](int rg, int kb) {
+                f32x16 acc = f32x16{};
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m) {
-                    f32x16 acc = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[m][ks], qf[m][rg][ks], acc, 0, 0, 0);
-                    sh[rg][kb][m] = acc;
-                }
+                for (int ks = 0; ks < D / 16; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[rg][ks], acc, 0, 0, 0);
+                sh[rg][kb] = acc;
             };
             // per-cell mask (branch-free selects); lane key kk = kb*32 + kc +
             // 4*hl with kc a compile-time constant
@@ -378,9 +377,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kcst = (r & 3) + 8 * (r >> 2);
-#pragma unroll
-                        for (int m = 0; m < NMAPS; ++m)
-                            sh[rg][kb][m][r] = kcst < lim ? sh[rg][kb][m][r] : ninf;
+                        sh[rg][kb][r] = kcst < lim ? sh[rg][kb][r] : ninf;
                     }
                 } else {
                     // dist = i - j = base - kc; window part iff 0 <= dist < W
@@ -392,9 +389,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                         for (int r = 0; r < 16; ++r) {
                             const int kcst = (r & 3) + 8 * (r >> 2);
                             const bool ok = (unsigned)(base - kcst) < W;
-#pragma unroll
-                            for (int m = 0; m < NMAPS; ++m)
-                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
+                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
                         }
                     } else if (dil == 1) {
                         const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
@@ -405,9 +400,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             // bitwise, not short-circuit: no per-cell branch
                             const bool ok = ((unsigned)dist < W) |
                                             ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
-#pragma unroll
-                            for (int m = 0; m < NMAPS; ++m)
-                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
+                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
                         }
                     } else {
                         const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
@@ -421,9 +414,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                             const int dist = base - kcst;
                             const bool ok = (((unsigned)dist <= (unsigned)span) & (((lat >> kcst) & 1u) != 0)) |
                                             ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
-#pragma unroll
-                            for (int m = 0; m < NMAPS; ++m)
-                                sh[rg][kb][m][r] = ok ? sh[rg][kb][m][r] : ninf;
+                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
                         }
                     }
                 }
@@ -433,68 +424,58 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
             // (branch-free, so the scheduler can interleave them with MFMAs).
             // l is rescaled here, O by rescale_o once every PV product that
             // used the old maximum has been accumulated.
-            float alpha[NMAPS][RG];
+            float alpha[RG];
             auto softmax_max = [&](int rg, int kb) -> bool {
                 bool moved = false;
-#pragma unroll
-                for (int m = 0; m < NMAPS; ++m) {
-                    const f32x16 &sv = sh[rg][kb][m];
-                    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-                    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                                         fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-                    // row maximum across the two lane halves holding the row
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                                     __builtin_bit_cast(unsigned, mx),
-                                                                     false, false);
-                    mx = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]),
-                               __builtin_bit_cast(float, (unsigned)sw[1]));
-                    const float mxs = mx * p.c;
-                    alpha[m][rg] = 1.f;
-                    if (__builtin_amdgcn_ballot_w64(mxs > m_run[m][rg] + kSlack) != 0) {
-                        const float m_new = fmaxf(m_run[m][rg], mxs);
-                        alpha[m][rg] = __builtin_amdgcn_exp2f(m_run[m][rg] - m_new);
-                        l_run[m][rg] *= alpha[m][rg];
-                        m_run[m][rg] = m_new;
-                        moved = true;
-                    }
+                const f32x16 &sv = sh[rg][kb];
+                float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+                mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                                     fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+                // row maximum across the two lane halves holding the row
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                                 __builtin_bit_cast(unsigned, mx),
+                                                                 false, false);
+                mx = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]),
+                           __builtin_bit_cast(float, (unsigned)sw[1]));
+                const float mxs = mx * p.c;
+                alpha[rg] = 1.f;
+                if (__builtin_amdgcn_ballot_w64(mxs > m_run[rg] + kSlack) != 0) {
+                    const float m_new = fmaxf(m_run[rg], mxs);
+                    alpha[rg] = __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+                    l_run[rg] *= alpha[rg];
+                    m_run[rg] = m_new;
+                    moved = true;
                 }
                 return moved;
             };
             auto rescale_o = [&](int rg) {
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m)
-#pragma unroll
-                    for (int db = 0; db < DV / 32; ++db)
-                        o[m][rg][db] *= alpha[m][rg];
+                for (int db = 0; db < DV / 32; ++db)
+                    o[rg][db] *= alpha[rg];
             };
-            bf16x8 pf[RG][2][NMAPS][2];
+            bf16x8 pf[RG][2][2];
             auto softmax_exp = [&](int rg, int kb) {
+                const f32x16 &sv = sh[rg][kb];
+                const float nm = -m_run[rg];
+                float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
-                for (int m = 0; m < NMAPS; ++m) {
-                    const f32x16 &sv = sh[rg][kb][m];
-                    const float nm = -m_run[m][rg];
-                    float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
+                for (int hf = 0; hf < 2; ++hf) {
+                    bf16x8 v8;
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        bf16x8 v8;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float pv = __builtin_amdgcn_exp2f(fmaf(sv[hf * 8 + e], p.c, nm));
-                            lsum[e & 3] += pv;
-                            v8[e] = (__bf16)pv;
-                        }
-                        pf[rg][kb][m][hf] = v8;
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[hf * 8 + e], p.c, nm));
+                        lsum[e & 3] += pv;
+                        v8[e] = (__bf16)pv;
                     }
-                    l_run[m][rg] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+                    pf[rg][kb][hf] = v8;
                 }
+                l_run[rg] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
             };
             // keep a block's exponentials in that block (otherwise they are
             // sunk past the next branch, next to their use)
             auto pin = [&](int rg, int kb) {
-#pragma unroll
-                for (int m = 0; m < NMAPS; ++m)
-                    asm volatile("" ::"v"(pf[rg][kb][m][0]), "v"(pf[rg][kb][m][1]), "v"(l_run[m][rg]));
+                asm volatile("" ::"v"(pf[rg][kb][0]), "v"(pf[rg][kb][1]), "v"(l_run[rg]));
             };
             // V^T fragments of key half kb, shared by every row group
             bf16x8 va[2][DV / 32];
@@ -522,10 +503,8 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-                        for (int m = 0; m < NMAPS; ++m)
-                            o[m][rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                va[hf][db], pf[rg][kb][m][hf], o[m][rg][db], 0, 0, 0);
+                        o[rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            va[hf][db], pf[rg][kb][hf], o[rg][db], 0, 0, 0);
             };
             // scheduling hint for one branch-free block: alternate one MFMA
             // with a few VALU instructions
@@ -536,8 +515,8 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
                 }
             };
-            using QkMfma = std::integral_constant<int, NMAPS * D / 16>;
-            using PvMfma = std::integral_constant<int, NMAPS * 2 * (DV / 32)>;
+            using QkMfma = std::integral_constant<int, D / 16>;
+            using PvMfma = std::integral_constant<int, 2 * (DV / 32)>;
 
             // ---- the tile, software-pipelined over (row group, key half) ----
             read_k(0);
@@ -586,17 +565,38 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     }
 
     // ---- epilogue: O / l -> bf16 ------------------------------------------
+    // Two maps: the second map's waves hand lambda * O2 / l2 to the first
+    // map's waves through LDS (the stages are free after the last barrier),
+    // in register order, lane-major; those store O1 / l1 minus it.
+    static_assert(kXo <= sizeof(smem), "the second map's output fits the LDS array");
+    float *xo = reinterpret_cast<float *>(smem);
+    auto xo_at = [&](int rg, int db, int r) -> float & {
+        return xo[(((wave * RG + rg) * (DV / 32) + db) * 16 + r) * 64 + lane];
+    };
+    if constexpr (NMAPS == 2) {
+        if (wmap == 1) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const float lt = l_run[rg] + __shfl_xor(l_run[rg], 32);
+                const float sc = lt > 0.f ? p.lambda / lt : 0.f;
+#pragma unroll
+                for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        xo_at(rg, db, r) = o[rg][db][r] * sc;
+            }
+        }
+        __syncthreads();
+        if (wmap == 1)
+            return;
+    }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        float inv[NMAPS];
-#pragma unroll
-        for (int m = 0; m < NMAPS; ++m) {
-            const float lt = l_run[m][rg] + __shfl_xor(l_run[m][rg], 32);
-            inv[m] = lt > 0.f ? 1.f / lt : 0.f;
-            if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row[rg] < Nr)
-                p.lse[(int64_t)(b * p.Hq + h) * p.N + res + rdil * my_row[rg]] =
-                    lt > 0.f ? (m_run[m][rg] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
-        }
+        const float lt = l_run[rg] + __shfl_xor(l_run[rg], 32);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (NMAPS == 1 && p.lse != nullptr && hl == 0 && my_row[rg] < Nr)
+            p.lse[(int64_t)(b * p.Hq + h) * p.N + res + rdil * my_row[rg]] =
+                lt > 0.f ? (m_run[rg] + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
         if (my_row[rg] < Nr) {
             __bf16 *dst = p.out + ((int64_t)(b * p.Hq + h) * p.N + res + rdil * my_row[rg]) * DV;
 #pragma unroll
@@ -606,9 +606,9 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                     bf16x4 v4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float x = o[0][rg][db][r4 * 4 + i] * inv[0];
+                        float x = o[rg][db][r4 * 4 + i] * inv;
                         if (NMAPS == 2)
-                            x -= p.lambda * (o[NMAPS - 1][rg][db][r4 * 4 + i] * inv[NMAPS - 1]);
+                            x -= xo_at(rg, db, r4 * 4 + i);
                         v4[i] = (__bf16)x;
                     }
                     *reinterpret_cast<bf16x4 *>(dst + db * 32 + 8 * r4 + 4 * hl) = v4;
@@ -622,16 +622,20 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
 // softmax overlaps another's matrix work).  Only the minimum is given: a
 // maximum of two makes the compiler declare extra registers to enforce it,
 // and at d=64 (143 registers, 42 KiB LDS) a third workgroup per CU runs the
-// local+strided workload 17% faster.  Two-map kernels need more state and
-// run one wave per SIMD.
+// local+strided workload 17% faster.
 template <int D, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFwdRowGroups == 1 ? 2 : 1)))
 void fwd_bf16_kernel(Params p) {
     fwd_bf16_body<D, DV, 1, kFwdRowGroups, MODE>(p);
 }
 
+// Two maps on separate waves (8 per workgroup, two per SIMD): a wave holds one
+// map's state (191 registers at d=64, dv=128).  Both maps in every wave need
+// ~316 registers, one wave per SIMD, and run the differential workload 13%
+// slower.
 template <int D, int DV, int MODE>
-__global__ __launch_bounds__(kThreads) void diff_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kDiffThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void diff_bf16_kernel(Params p) {
     fwd_bf16_body<D, DV, 2, kDiffRowGroups, MODE>(p);
 }
 
@@ -671,9 +675,9 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
     } else {
         if (ext)
-            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 1>), dim3(grid), dim3(kDiffThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((diff_bf16_kernel<D, DV, 0>), dim3(grid), dim3(kDiffThreads), 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -101,7 +101,7 @@ int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride, int dilat
 int hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 
 int fwd_run(const swa::FwdArgs &a, swa_dtype_t dt, hipStream_t stream) {
-    if (swa::fwd_workgroups(a, dt) * swa::kFwdThreads > swa::kMaxGridItems)
+    if (swa::fwd_workgroups(a, dt) * swa::fwd_threads(a, dt) > swa::kMaxGridItems)
         return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
     return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
 }

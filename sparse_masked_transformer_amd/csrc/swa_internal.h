@@ -20,8 +20,10 @@ constexpr int kDiffRowGroups = 1;
 // small problems spread over many compute units).
 constexpr int kF32BM = 32;
 constexpr int kF32TPR = 8;   // lanes per query row (fp32 forward and decode)
-// Lanes per workgroup of every forward kernel.
+// Lanes per workgroup of the forward kernels: 256, except the bf16
+// two-map kernel (its maps run on separate waves).
 constexpr int kFwdThreads = 256;
+constexpr int kDiffFwdThreads = 512;
 static_assert(kF32BM * kF32TPR == kFwdThreads, "fp32 forward tile = one 256-lane workgroup");
 // A dispatch holds at most 2^32 - 1 work-items per grid dimension; every
 // launch here uses one dimension.
@@ -64,6 +66,11 @@ struct FwdArgs {
 // Every other forward has one workgroup per (batch, head, query tile).
 inline bool fwd_by_residue_class(const FwdArgs &a, swa_dtype_t dt) {
     return dt == SWA_BF16 && a.nmaps == 1 && a.dilation > 1 && a.stride == 0 && a.n_global == 0;
+}
+
+// Lanes per workgroup of the forward launch for (a, dt).
+inline int fwd_threads(const FwdArgs &a, swa_dtype_t dt) {
+    return dt == SWA_BF16 && a.nmaps == 2 ? kDiffFwdThreads : kFwdThreads;
 }
 
 // Workgroups of the forward launch for (a, dt).

@@ -161,8 +161,8 @@ def test_fwd_rejections(swa):
 
 
 def test_fwd_rejects_grids_beyond_one_dispatch(swa):
-    """Row indices fit int32 but the launch would need 2^32 or more work-items
-    (256 lanes per workgroup): rejected on the host, nothing launched."""
+    """Row indices fit int32 but the launch would need 2^32 or more work-items:
+    rejected on the host, nothing launched."""
     U = swa.SWA_ERR_UNSUPPORTED
     # bf16, ragged N = 130: 2 query tiles of 128 rows for each of 2^23 heads
     assert fwd(swa, B=1 << 10, Hq=1 << 13, Hkv=1 << 13, N=130,
@@ -173,6 +173,11 @@ def test_fwd_rejects_grids_beyond_one_dispatch(swa):
     m = fake_mask(swa, 1 << 21, 32, 0, bm=32)
     assert swa.lib.diff_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1 << 9, 1, 1 << 21, 64,
                                  64, 32, 0, 1, 0, 0.125, 0.5, ctypes.byref(m), None) == U
+    # bf16 differential attention: 512 lanes per workgroup (one wave group per
+    # map), 2 query tiles for each of 2^22 heads -> 2^32 work-items
+    m = fake_mask(swa, 130, 32, 0, bm=128)
+    assert swa.lib.diff_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 9, 1 << 13, 1 << 13, 130,
+                                 64, 64, 32, 0, 1, 0, 0.125, 0.5, ctypes.byref(m), None) == U
 
 
 def dec(swa, q=FAKE, kr=FAKE, vr=FAKE, out=FAKE, sl=None, ws=FAKE, wsb=None, dt=1, B=2, Hq=8,
