@@ -213,7 +213,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     // LDS-DMA staging: buffer_load ... lds writes 16 bytes per lane straight
     // into LDS, lane l at bytes 16 l .. 16 l + 15 of a wave-uniform 1 KiB
     // chunk.  A tile of 64 padded rows is a whole number of chunks; wave w
-    // writes chunks w, w + 4, ...  Lane l of chunk ch covers tile byte
+    // writes chunks w, w + WAVES, ...  Lane l of chunk ch covers tile byte
     // 1024 ch + 16 l, i.e. a row and a column of the padded layout; lanes on
     // padding fetch their row's first 16 bytes (padding is never read).
     constexpr int kCh = C::kTile / 1024, vCh = C::vTile / 1024;

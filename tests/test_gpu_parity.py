@@ -266,8 +266,10 @@ def run_diff(swa, cfg, q1, k1, q2, k2, v):
     return host(out)
 
 
+# every bf16 head-size pair (d, dv) the two-map kernel instantiates
 DIFF_CASES = [(1, 2, 2, 300, 64, 128, 70, 0), (1, 4, 2, 257, 64, 64, 300, 0),
-              (2, 2, 2, 200, 32, 128, 50, 9), (1, 2, 1, 130, 32, 32, 1, 0)]
+              (2, 2, 2, 200, 32, 128, 50, 9), (1, 2, 1, 130, 32, 32, 1, 0),
+              (1, 4, 2, 190, 32, 64, 40, 0), (1, 2, 2, 150, 64, 32, 100, 7)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
