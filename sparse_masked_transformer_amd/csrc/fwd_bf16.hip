@@ -700,6 +700,9 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
         SWA_DIFF_CASE(64, 32)
         SWA_DIFF_CASE(64, 64)
         SWA_DIFF_CASE(64, 128)
+        SWA_DIFF_CASE(128, 32)
+        SWA_DIFF_CASE(128, 64)
+        SWA_DIFF_CASE(128, 128)
 #undef SWA_DIFF_CASE
     }
     return hipErrorInvalidValue;

@@ -396,9 +396,6 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
         return st;
     if (!head_dim_ok(d) || !head_dim_ok(dv))
         return SWA_ERR_UNSUPPORTED;
-    // bf16: two K tiles and one V tile of 64 keys, double-buffered, in 64 KiB of LDS
-    if (dt == SWA_BF16 && 2 * d + dv > 256)
-        return SWA_ERR_UNSUPPORTED;
     st = check_mask(mask, N, window, stride, dilation, n_global, swa::tile_rows(SWA_OP_DIFF, dt));
     if (st != SWA_OK)
         return st;

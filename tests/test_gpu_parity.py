@@ -269,7 +269,9 @@ def run_diff(swa, cfg, q1, k1, q2, k2, v):
 # every bf16 head-size pair (d, dv) the two-map kernel instantiates
 DIFF_CASES = [(1, 2, 2, 300, 64, 128, 70, 0), (1, 4, 2, 257, 64, 64, 300, 0),
               (2, 2, 2, 200, 32, 128, 50, 9), (1, 2, 1, 130, 32, 32, 1, 0),
-              (1, 4, 2, 190, 32, 64, 40, 0), (1, 2, 2, 150, 64, 32, 100, 7)]
+              (1, 4, 2, 190, 32, 64, 40, 0), (1, 2, 2, 150, 64, 32, 100, 7),
+              (1, 2, 2, 200, 128, 128, 64, 0), (1, 4, 2, 170, 128, 64, 90, 5),
+              (1, 2, 1, 140, 128, 32, 30, 0)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
