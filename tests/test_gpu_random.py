@@ -1,0 +1,192 @@
+"""Seeded random sweep of the GPU path against the fp64 oracle.
+
+The hand-picked parity cases pin the edges one at a time; this sweep draws
+combinations of them (sequence length, window, stride, dilation, global
+tokens, head sizes, grouped heads, batch, dtype, decode lengths and sink
+slots) from a fixed seed, so every run checks the same configurations.
+Tolerances are the parity bar: max-abs 2e-2 for bf16 inputs, 1e-5 for fp32.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def swa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_masked_transformer_amd as m
+    return m
+
+
+def dev(x, dt):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16 if dt == "bf16" else torch.float32)
+    return t.cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def max_err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def tdtype(dt):
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def mask_pattern(rng, N):
+    """(window, stride, dilation, n_global): each part on or off at random."""
+    W = int(rng.integers(1, N + 41))
+    s = 0 if rng.random() < 0.5 else int(rng.integers(1, N + 6))
+    dil = 1 if rng.random() < 0.5 else int(rng.integers(2, 7))
+    g = 0 if rng.random() < 0.6 else int(rng.integers(1, N + 4))
+    return W, s, dil, g
+
+
+def heads(rng, max_group=4):
+    Hkv = int(rng.integers(1, 3))
+    return Hkv * int(rng.choice([1, 2, max_group])), Hkv
+
+
+def prefill_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 601))
+        W, s, dil, g = mask_pattern(rng, N)
+        Hq, Hkv = heads(rng)
+        d = int(rng.choice([32, 64, 128]))
+        out.append(dict(dtype="bf16" if i % 2 == 0 else "f32", B=int(rng.integers(1, 3)), Hq=Hq,
+                        Hkv=Hkv, N=N, d=d, dv=d, window=W, stride=s, dilation=dil, n_global=g,
+                        scale=1.0 / math.sqrt(d), seed=1000 + i))
+    return out
+
+
+def diff_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 401))
+        W, s, dil, g = mask_pattern(rng, N)
+        Hq, Hkv = heads(rng)
+        out.append(dict(dtype="bf16" if i % 2 == 0 else "f32", B=1, Hq=Hq, Hkv=Hkv, N=N,
+                        d=int(rng.choice([32, 64, 128])), dv=int(rng.choice([32, 64, 128])),
+                        window=W, stride=s, dilation=dil, n_global=g, scale=0.125,
+                        lam=float(rng.uniform(0.0, 1.0)), seed=2000 + i))
+    return out
+
+
+def decode_configs(n, seed, sinks):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        W = int(rng.integers(1, 301))
+        B = int(rng.integers(1, 6))
+        Hq, Hkv = heads(rng, max_group=8)
+        d = int(rng.choice([32, 64, 128]))
+        lens = [int(x) for x in rng.integers(0, 3 * W + 10, size=B)]
+        out.append(dict(dtype="bf16" if i % 2 == 0 else "f32", B=B, Hq=Hq, Hkv=Hkv, window=W, d=d,
+                        dv=d, position=0, n_sink=int(rng.integers(1, 9)) if sinks else 0,
+                        scale=1.0 / math.sqrt(d), seed=3000 + i + (100 if sinks else 0), lens=lens))
+    return out
+
+
+def diff_decode_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = "bf16" if i % 2 == 0 else "f32"
+        # bf16 two-map decode holds two K rows and a V row per slot: 2 d + dv <= 256
+        pairs = [(32, 32), (32, 64), (32, 128), (64, 32), (64, 64), (64, 128)]
+        if dt == "f32":
+            pairs += [(128, 32), (128, 64), (128, 128)]
+        d, dv = pairs[int(rng.integers(0, len(pairs)))]
+        W = int(rng.integers(1, 301))
+        B = int(rng.integers(1, 5))
+        Hq, Hkv = heads(rng, max_group=8)
+        lens = [int(x) for x in rng.integers(0, 3 * W + 10, size=B)]
+        out.append(dict(dtype=dt, B=B, Hq=Hq, Hkv=Hkv, window=W, d=d, dv=dv, position=0,
+                        scale=0.125, lam=float(rng.uniform(0.0, 1.0)), seed=4000 + i, lens=lens))
+    return out
+
+
+def label(c):
+    keys = ("dtype", "B", "Hq", "Hkv", "N", "d", "dv", "window", "stride", "dilation", "n_global",
+            "n_sink")
+    return " ".join(f"{k}={c[k]}" for k in keys if k in c)
+
+
+def banner(c):
+    print(f"[case] {label(c)}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", prefill_configs(16, 11), ids=label)
+def test_random_prefill(swa, cfg):
+    banner(cfg)
+    dt = cfg["dtype"]
+    q, k, v = synth.prefill_inputs(cfg)
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"], dtype=tdtype(dt),
+                                    d=cfg["d"], dilation=cfg["dilation"], n_global=cfg["n_global"])
+    out = swa.swa_attn_fwd(dev(q, dt), dev(k, dt), dev(v, dt), cfg["window"], cfg["stride"],
+                           cfg["scale"], mask)
+    want = oracle.attn_full(q, k, v, cfg["window"], cfg["stride"], cfg["scale"],
+                            dilation=cfg["dilation"], n_global=cfg["n_global"])
+    assert max_err(host(out), want) <= TOL[dt]
+
+
+@pytest.mark.parametrize("cfg", diff_configs(10, 12), ids=label)
+def test_random_diff(swa, cfg):
+    banner(cfg)
+    dt = cfg["dtype"]
+    ins = synth.diff_inputs(cfg)
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"], dtype=tdtype(dt),
+                                    d=cfg["d"], dv=cfg["dv"], op=swa.SWA_OP_DIFF,
+                                    dilation=cfg["dilation"], n_global=cfg["n_global"])
+    out = swa.diff_attn_fwd(*(dev(x, dt) for x in ins), cfg["window"], cfg["stride"], cfg["scale"],
+                            cfg["lam"], mask)
+    want = oracle.diff_full(*ins, cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"],
+                            dilation=cfg["dilation"], n_global=cfg["n_global"])
+    assert max_err(host(out), want) <= TOL[dt]
+
+
+@pytest.mark.parametrize("cfg", decode_configs(8, 13, sinks=False) + decode_configs(6, 14, sinks=True),
+                         ids=label)
+def test_random_decode(swa, cfg):
+    banner(cfg)
+    dt = cfg["dtype"]
+    ins = synth.decode_inputs(cfg, seq_len=cfg["lens"])
+    sl = torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda()
+    if cfg["n_sink"] == 0:
+        out = swa.swa_attn_decode(dev(ins["q"], dt), dev(ins["k_ring"], dt), dev(ins["v_ring"], dt), sl,
+                                  cfg["scale"])
+        want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"])
+    else:
+        out = swa.swa_attn_decode_sinks(dev(ins["q"], dt), dev(ins["k_sink"], dt), dev(ins["v_sink"], dt),
+                                        dev(ins["k_ring"], dt), dev(ins["v_ring"], dt), sl, cfg["scale"])
+        want = oracle.decode(ins["q"], ins["k_ring"], ins["v_ring"], ins["seq_len"], cfg["scale"],
+                             k_sink=ins["k_sink"], v_sink=ins["v_sink"])
+    assert max_err(host(out), want) <= TOL[dt]
+
+
+@pytest.mark.parametrize("cfg", diff_decode_configs(8, 15), ids=label)
+def test_random_diff_decode(swa, cfg):
+    banner(cfg)
+    dt = cfg["dtype"]
+    ins = synth.diff_decode_inputs(cfg, seq_len=cfg["lens"])
+    sl = torch.from_numpy(ins["seq_len"].astype(np.int32)).cuda()
+    out = swa.diff_attn_decode(*(dev(ins[x], dt) for x in ("q1", "k1_ring", "q2", "k2_ring", "v_ring")),
+                               sl, cfg["scale"], cfg["lam"])
+    want = oracle.diff_decode(ins["q1"], ins["k1_ring"], ins["q2"], ins["k2_ring"], ins["v_ring"],
+                              ins["seq_len"], cfg["scale"], cfg["lam"])
+    assert max_err(host(out), want) <= TOL[dt]
