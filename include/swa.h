@@ -221,7 +221,7 @@ int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink,
  * over the window positions of swa_attn_decode.
  *   q1, q2          [B, Hq, d]            k1_ring, k2_ring  [B, Hkv, window, d]
  *   v_ring          [B, Hkv, window, dv]  out               [B, Hq, dv]
- * d, dv in {32, 64, 128}; bf16 also needs 2 d + dv <= 256.
+ * d, dv in {32, 64, 128}.
  * workspace: swa_attn_decode_workspace_bytes(SWA_OP_DIFF, B, Hq, Hkv, dv,
  * window, 0) bytes.
  */

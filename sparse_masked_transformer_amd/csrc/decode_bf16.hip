@@ -16,8 +16,9 @@
 // Workgroup: `waves` waves for one (sequence, key/value head, split of the
 // virtual slots); each wave takes a contiguous run of whole 32-slot steps.
 //   * A wave streams its slots 32 at a time: coalesced 16-byte loads into
-//     registers two steps ahead (two register stages), then into its own LDS
-//     area, rows padded (K +16 bytes, V +64 bytes) against bank conflicts.
+//     registers two steps ahead (two register stages; one for two maps with
+//     2 d + dv > 256), then into its own LDS area, rows padded (K +16 bytes,
+//     V +64 bytes) against bank conflicts.
 //   * The G query heads sharing the key/value head form the 16 columns of a
 //     v_mfma_f32_16x16x32_bf16 (unused columns are zero): S^T = K Q^T with K
 //     from LDS as the A operand; lane l holds head l%16 and keys 4(l/16)+i.
@@ -58,6 +59,12 @@ struct Lay {
     static constexpr int kChunks = kDecodeStep * D / 8 / 64;   // 16-byte chunks per lane
     static constexpr int vChunks = kDecodeStep * DV / 8 / 64;
 };
+
+// Register stages of a wave's step loads: two (the next two steps in flight),
+// or one where two stages would not fit the register file -- two maps whose
+// K rows and V row span more than 256 channels (2 d + dv > 256).
+template <int D, int DV, int NMAPS>
+constexpr int reg_stages() { return NMAPS * D + DV > 256 ? 1 : 2; }
 
 // Waves per SIMD, at least: two, unless two register stages of two K rows
 // and a V row (2 d + dv > 192), or two maps' 128-wide outputs, no longer fit
@@ -161,7 +168,8 @@ void decode_kernel(Params p) {
     }
     const uintptr_t vring_b = reinterpret_cast<uintptr_t>(p.v) + static_cast<uintptr_t>(ring) * (2 * DV);
     const uintptr_t vsink_b = reinterpret_cast<uintptr_t>(p.vs) + static_cast<uintptr_t>(sink) * (2 * DV);
-    u32x4 kst[2][NMAPS][Y::kChunks], vst[2][Y::vChunks];
+    constexpr int S = reg_stages<D, DV, NMAPS>();
+    u32x4 kst[S][NMAPS][Y::kChunks], vst[S][Y::vChunks];
     auto load = [&](int st, int reg) {
         const int base = v0 + run_step(st) * kDecodeStep;
 #pragma unroll
@@ -286,17 +294,28 @@ void decode_kernel(Params p) {
     // load is issued unconditionally (a step past the wave's run re-reads its
     // last slot and is fully masked, so it adds nothing): conditional loads
     // would make the compiler's load-counter waits assume the fewest loads in
-    // flight and wait for the other stage too.
+    // flight and wait for the other stage too.  With one stage the next
+    // step's loads are in flight while the current step, already in LDS, is
+    // computed.
     if (nsteps > 0) {
-        load(0, 0);
-        load(1, 1);
-        for (int st = 0; st < nsteps; st += 2) {
-            store(0);
-            load(st + 2, 0);
-            compute(st);
-            store(1);
-            load(st + 3, 1);
-            compute(st + 1);
+        if constexpr (S == 2) {
+            load(0, 0);
+            load(1, 1);
+            for (int st = 0; st < nsteps; st += 2) {
+                store(0);
+                load(st + 2, 0);
+                compute(st);
+                store(1);
+                load(st + 3, 1);
+                compute(st + 1);
+            }
+        } else {
+            load(0, 0);
+            for (int st = 0; st < nsteps; ++st) {
+                store(0);
+                load(st + 1, 0);
+                compute(st);
+            }
         }
     }
 
@@ -473,7 +492,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
             return launch<128, 128, 1>(a, stream);
         return hipErrorInvalidValue;
     }
-    // two maps: 2 d + dv <= 256 (the register stages hold two K rows and a V row)
+    // two maps: every (d, dv); wide pairs take one register stage
     if (a.d == 32 && a.dv == 32)
         return launch<32, 32, 2>(a, stream);
     if (a.d == 32 && a.dv == 64)
@@ -486,6 +505,12 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
         return launch<64, 64, 2>(a, stream);
     if (a.d == 64 && a.dv == 128)
         return launch<64, 128, 2>(a, stream);
+    if (a.d == 128 && a.dv == 32)
+        return launch<128, 32, 2>(a, stream);
+    if (a.d == 128 && a.dv == 64)
+        return launch<128, 64, 2>(a, stream);
+    if (a.d == 128 && a.dv == 128)
+        return launch<128, 128, 2>(a, stream);
     return hipErrorInvalidValue;
 }
 

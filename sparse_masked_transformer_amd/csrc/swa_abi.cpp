@@ -187,9 +187,6 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         return SWA_ERR_UNSUPPORTED;
     if (!head_dim_ok(a.d) || !head_dim_ok(a.dv))
         return SWA_ERR_UNSUPPORTED;
-    // bf16, two maps: two K rows and a V row per slot in the register stages
-    if (dt == SWA_BF16 && a.nmaps == 2 && 2 * a.d + a.dv > 256)
-        return SWA_ERR_UNSUPPORTED;
     if (stride != 0)
         return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
     if (swa::decode_launch_items(a, dt) > swa::kMaxGridItems)

@@ -422,6 +422,10 @@ DIFF_DECODE_CASES = [
     (1, 8, 1, 129, 32, 128, [129]),
     (2, 4, 4, 96, 64, 64, [50, 97]),
     (16, 16, 16, 1000, 64, 128, LENS16),
+    # 2 d + dv > 256: one register stage in bf16
+    (2, 4, 2, 100, 128, 128, [50, 300]),
+    (1, 8, 2, 70, 128, 64, [140]),
+    (3, 4, 4, 64, 128, 32, [1, 64, 65]),
 ]
 
 

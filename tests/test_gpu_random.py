@@ -107,11 +107,7 @@ def diff_decode_configs(n, seed):
     out = []
     for i in range(n):
         dt = "bf16" if i % 2 == 0 else "f32"
-        # bf16 two-map decode holds two K rows and a V row per slot: 2 d + dv <= 256
-        pairs = [(32, 32), (32, 64), (32, 128), (64, 32), (64, 64), (64, 128)]
-        if dt == "f32":
-            pairs += [(128, 32), (128, 64), (128, 128)]
-        d, dv = pairs[int(rng.integers(0, len(pairs)))]
+        d, dv = int(rng.choice([32, 64, 128])), int(rng.choice([32, 64, 128]))
         W = int(rng.integers(1, 301))
         B = int(rng.integers(1, 5))
         Hq, Hkv = heads(rng, max_group=8)
