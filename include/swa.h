@@ -183,8 +183,8 @@ size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int 
  *              on entry do not matter.
  *   stride     must be 0: stride keys older than the window are not in the
  *              ring (SWA_ERR_UNSUPPORTED otherwise).
- * bf16 needs Hq / Hkv <= 16; B * Hq and B * Hkv * window must fit int32
- * (SWA_ERR_UNSUPPORTED otherwise).
+ * B * Hq and B * Hkv * window must fit int32 (SWA_ERR_UNSUPPORTED
+ * otherwise).
  */
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,

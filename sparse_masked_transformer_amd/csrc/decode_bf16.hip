@@ -14,7 +14,11 @@
 // (attention does not depend on key order).
 //
 // Workgroup: `waves` waves for one (sequence, key/value head, split of the
-// virtual slots); each wave takes a contiguous run of whole 32-slot steps.
+// virtual slots) and one block of up to 16 of the head's query heads (grid
+// dimension y); each wave takes a contiguous run of whole 32-slot steps.
+// (With more than 16 query heads per key/value head, each block of 16 reads
+// the head's keys and values again; the blocks run side by side, so the
+// repeats mostly hit L2.)
 //   * A wave streams its slots 32 at a time: coalesced 16-byte loads into
 //     registers two steps ahead (two register stages; one for two maps with
 //     2 d + dv > 256), then into its own LDS area, rows padded (K +16 bytes,
@@ -110,7 +114,9 @@ void decode_kernel(Params p) {
     const int split = blockIdx.x % p.splits;
     const int bg = blockIdx.x / p.splits;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
-    const int G = p.Hq / p.Hkv;
+    const int G = p.Hq / p.Hkv;                   // query heads per key/value head
+    const int h0 = 16 * blockIdx.y;               // this block of up to 16 of them
+    const int Gb = G - h0 < 16 ? G - h0 : 16;
 
     // ---- this wave's virtual slots -------------------------------------------
     // wave-uniform (one sequence per workgroup); made explicit so the step
@@ -148,9 +154,9 @@ void decode_kernel(Params p) {
     for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-            if (colq < G)
+            if (colq < Gb)
                 qf[m][ks] = *reinterpret_cast<const bf16x8 *>(
-                    p.q[m] + (kv * G + colq) * D + ks * 32 + grp * 8);
+                    p.q[m] + (kv * G + h0 + colq) * D + ks * 32 + grp * 8);
             else
                 qf[m][ks] = bf16x8{};
         }
@@ -329,7 +335,7 @@ void decode_kernel(Params p) {
     __syncthreads();  // every wave is done with its tiles
     float *mw = reinterpret_cast<float *>(dsm);   // [waves][NMAPS][16]
     float *lw = mw + waves * NMAPS * 16;          // [waves][NMAPS][16]
-    float *ow = lw + waves * NMAPS * 16;          // [waves][NMAPS][G][DV]
+    float *ow = lw + waves * NMAPS * 16;          // [waves][NMAPS][Gb][DV]
     if (grp == 0) {
 #pragma unroll
         for (int m = 0; m < NMAPS; ++m) {
@@ -337,18 +343,18 @@ void decode_kernel(Params p) {
             lw[(wave * NMAPS + m) * 16 + colq] = lt[m];
         }
     }
-    if (colq < G) {
+    if (colq < Gb) {
 #pragma unroll
         for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
             for (int db = 0; db < DV / 16; ++db)
-                *reinterpret_cast<f32x4 *>(ow + ((wave * NMAPS + m) * G + colq) * DV + db * 16 + grp * 4) =
+                *reinterpret_cast<f32x4 *>(ow + ((wave * NMAPS + m) * Gb + colq) * DV + db * 16 + grp * 4) =
                     o[m][db];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < G * DV; e += blockDim.x) {
+    for (int e = threadIdx.x; e < Gb * DV; e += blockDim.x) {
         const int col = e / DV, dd = e % DV;
-        const int64_t head = kv * G + col;   // b * Hq + query head
+        const int64_t head = kv * G + h0 + col;   // b * Hq + query head
         float res = 0.f;
 #pragma unroll
         for (int m = 0; m < NMAPS; ++m) {
@@ -359,7 +365,7 @@ void decode_kernel(Params p) {
             for (int w = 0; w < waves; ++w) {
                 const float wgt = __builtin_amdgcn_exp2f(mw[(w * NMAPS + m) * 16 + col] - mstar);
                 l += wgt * lw[(w * NMAPS + m) * 16 + col];
-                acc += wgt * ow[((w * NMAPS + m) * G + col) * DV + dd];
+                acc += wgt * ow[((w * NMAPS + m) * Gb + col) * DV + dd];
             }
             if (p.splits == 1) {
                 const float r = l > 0.f ? acc / l : 0.f;
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_ml,
 
 template <int D, int DV, int NMAPS>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
-    const DecodePlan plan = decode_plan(a.B, a.Hkv, a.window + a.n_sink);
+    const DecodePlan plan = decode_plan_for(a);
     Params p;
     for (int m = 0; m < 2; ++m) {
         p.q[m] = static_cast<const __bf16 *>(a.q[m]);
@@ -459,7 +465,8 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     p.lambda = a.lambda;
 
-    const size_t lds = lds_bytes<D, DV, NMAPS>(plan.waves, a.Hq / a.Hkv);
+    const int group = a.Hq / a.Hkv;
+    const size_t lds = lds_bytes<D, DV, NMAPS>(plan.waves, group < 16 ? group : 16);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, NMAPS>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -468,7 +475,8 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
             return e;
     }
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * plan.splits);
-    hipLaunchKernelGGL((decode_kernel<D, DV, NMAPS>), dim3(grid), dim3(64 * plan.waves),
+    const unsigned blocks = static_cast<unsigned>(decode_head_blocks(a.Hq, a.Hkv));
+    hipLaunchKernelGGL((decode_kernel<D, DV, NMAPS>), dim3(grid, blocks), dim3(64 * plan.waves),
                        static_cast<unsigned>(lds), stream, p);
     if (plan.splits > 1)
         hipLaunchKernelGGL((decode_combine_kernel<DV, NMAPS>), dim3(static_cast<unsigned>((rows + 3) / 4)),

@@ -137,7 +137,8 @@ int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt) {
         const int64_t per_wg = 64 / kF32TPR;
         return (rows + per_wg - 1) / per_wg * 64;
     }
-    const DecodePlan plan = decode_plan(a.B, a.Hkv, a.window + a.n_sink);
+    const DecodePlan plan = decode_plan_for(a);
+    // grid x: (sequence, key/value head, split); y: blocks of 16 query heads
     const int64_t main_items = static_cast<int64_t>(a.B) * a.Hkv * plan.splits * 64 * plan.waves;
     // the combine kernel: 256-lane workgroups of 4 rows
     const int64_t combine_items = plan.splits > 1 ? (rows + 3) / 4 * 256 : 0;
@@ -151,7 +152,7 @@ size_t decode_ws_bytes(int nmaps, int B, int Hq, int Hkv, int dv, int window, in
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(dv) || window < 1 ||
         window > SWA_MAX_N || n_sink < 0 || n_sink > SWA_MAX_N)
         return 0;
-    const swa::DecodePlan plan = swa::decode_plan(B, Hkv, window + n_sink);
+    const swa::DecodePlan plan = swa::decode_plan(B, Hkv * swa::decode_head_blocks(Hq, Hkv), window + n_sink);
     if (plan.splits == 1)
         return 0;  // the workgroups write the output directly
     // per (sequence, query head, split, map): running max and sum (section
@@ -180,8 +181,6 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         a.window > SWA_MAX_N || a.n_sink < 0 || a.n_sink > SWA_MAX_N || stride < 0 ||
         (a.seq_len == nullptr && a.N < 0))
         return SWA_ERR_INVALID_ARG;
-    if (dt == SWA_BF16 && a.Hq / a.Hkv > 16)
-        return SWA_ERR_UNSUPPORTED;  // the query heads of a group share one 16-column tile
     if (static_cast<int64_t>(a.B) * a.Hkv * (a.window + a.n_sink) > INT32_MAX ||
         static_cast<int64_t>(a.B) * a.Hq > INT32_MAX)
         return SWA_ERR_UNSUPPORTED;
@@ -191,6 +190,8 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         return SWA_ERR_UNSUPPORTED;  // stride keys older than the window are not in the ring
     if (swa::decode_launch_items(a, dt) > swa::kMaxGridItems)
         return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
+    if (dt == SWA_BF16 && swa::decode_head_blocks(a.Hq, a.Hkv) > 65535)
+        return SWA_ERR_UNSUPPORTED;  // blocks of 16 query heads fill the grid's y dimension
     const size_t need = decode_ws_bytes(a.nmaps, a.B, a.Hq, a.Hkv, a.dv, a.window, a.n_sink);
     if (need > 0 && (a.workspace == nullptr || !aligned16(a.workspace) || workspace_bytes < need))
         return SWA_ERR_WORKSPACE;

@@ -125,6 +125,13 @@ struct DecodePlan {
 // Plan for B*Hkv (sequence, key/value head) pairs and at most `slots` cache
 // slots (window + sink slots) per pair.
 DecodePlan decode_plan(int B, int Hkv, int slots);
+// The bf16 decode kernel takes the query heads of a key/value head 16 at a
+// time (the columns of one MFMA tile): blocks per key/value head.
+inline int decode_head_blocks(int Hq, int Hkv) { return (Hq / Hkv + 15) / 16; }
+// The plan of a decode call: each block of query heads counts as a pair.
+inline DecodePlan decode_plan_for(const DecodeArgs &a) {
+    return decode_plan(a.B, a.Hkv * decode_head_blocks(a.Hq, a.Hkv), a.window + a.n_sink);
+}
 // Work-items of the largest dispatch one decode call makes.
 int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt);
 // fp32 count of the (max, sum) section of the decode workspace for `parts`

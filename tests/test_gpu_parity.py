@@ -326,6 +326,8 @@ LENS16 = [(i * 397) % 2100 for i in range(16)]   # 0 .. 2099, below, at and abov
 
 DECODE_CASES = [
     # B, Hq, Hkv, W, d, lengths   (bf16 work split: workgroups of 1-4 waves; splits)
+    (2, 32, 1, 200, 64, [150, 900]),           # one key/value head for 32 query heads
+    (1, 34, 2, 70, 128, [70]),                 # 17 per group: a second block of one head
     (3, 4, 1, 64, 64, [1, 30, 64]),            # 1 wave, 2 splits
     (2, 8, 2, 300, 128, [299, 1000]),          # 2 waves, 5 splits
     (4, 4, 4, 1000, 32, [0, 5, 999, 1001]),    # 4 waves, 8 splits
@@ -384,6 +386,7 @@ def run_decode_sinks(swa, cfg, ins):
 
 SINK_CASES = [
     # B, Hq, Hkv, W, n_sink, d, lengths
+    (2, 48, 2, 80, 4, 64, [30, 400]),          # 24 query heads per key/value head
     (2, 8, 2, 64, 4, 128, [3, 200]),           # no sink yet outside the ring; 4 sinks
     (3, 4, 1, 100, 4, 64, [102, 104, 5000]),   # sinks partly still in the ring
     (1, 2, 2, 31, 1, 32, [40]),                # sink + ring = exactly one 32-slot step
@@ -422,6 +425,7 @@ DIFF_DECODE_CASES = [
     (1, 8, 1, 129, 32, 128, [129]),
     (2, 4, 4, 96, 64, 64, [50, 97]),
     (16, 16, 16, 1000, 64, 128, LENS16),
+    (2, 40, 2, 90, 64, 128, [91, 20]),         # 20 query heads per key/value head
     # 2 d + dv > 256: one register stage in bf16
     (2, 4, 2, 100, 128, 128, [50, 300]),
     (1, 8, 2, 70, 128, 64, [140]),

@@ -93,7 +93,7 @@ def decode_configs(n, seed, sinks):
     for i in range(n):
         W = int(rng.integers(1, 301))
         B = int(rng.integers(1, 6))
-        Hq, Hkv = heads(rng, max_group=8)
+        Hq, Hkv = heads(rng, max_group=int(rng.choice([8, 20, 33])))
         d = int(rng.choice([32, 64, 128]))
         lens = [int(x) for x in rng.integers(0, 3 * W + 10, size=B)]
         out.append(dict(dtype="bf16" if i % 2 == 0 else "f32", B=B, Hq=Hq, Hkv=Hkv, window=W, d=d,
