@@ -286,7 +286,7 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     const int k_lane = col * C::kRow + hl * 16;
     const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * C::vRow + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
-    // ---- running state (per map, per row group) --------------------------------
+    // ---- running state of this wave's map, per row group ---------------------
     f32x16 o[RG][DV / 32];
     float m_run[RG], l_run[RG];
 #pragma unroll
