@@ -5,8 +5,11 @@ combinations of them (sequence length, window, stride, dilation, global
 tokens, head sizes, grouped heads, batch, dtype, decode lengths and sink
 slots) from a fixed seed, so every run checks the same configurations.
 Tolerances are the parity bar: max-abs 2e-2 for bf16 inputs, 1e-5 for fp32.
+SWA_RANDOM_SCALE=k multiplies the number of drawn configurations by k (the
+default run draws 48; k = 150 draws about 7,000, about a minute on one GPU).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -18,6 +21,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
+SCALE = max(1, int(os.environ.get("SWA_RANDOM_SCALE", "1")))
 
 
 @pytest.fixture(scope="module")
@@ -127,7 +131,7 @@ def banner(c):
     print(f"[case] {label(c)}", flush=True)
 
 
-@pytest.mark.parametrize("cfg", prefill_configs(16, 11), ids=label)
+@pytest.mark.parametrize("cfg", prefill_configs(16 * SCALE, 11), ids=label)
 def test_random_prefill(swa, cfg):
     banner(cfg)
     dt = cfg["dtype"]
@@ -141,7 +145,7 @@ def test_random_prefill(swa, cfg):
     assert max_err(host(out), want) <= TOL[dt]
 
 
-@pytest.mark.parametrize("cfg", diff_configs(10, 12), ids=label)
+@pytest.mark.parametrize("cfg", diff_configs(10 * SCALE, 12), ids=label)
 def test_random_diff(swa, cfg):
     banner(cfg)
     dt = cfg["dtype"]
@@ -156,7 +160,8 @@ def test_random_diff(swa, cfg):
     assert max_err(host(out), want) <= TOL[dt]
 
 
-@pytest.mark.parametrize("cfg", decode_configs(8, 13, sinks=False) + decode_configs(6, 14, sinks=True),
+@pytest.mark.parametrize("cfg", decode_configs(8 * SCALE, 13, sinks=False) +
+                         decode_configs(6 * SCALE, 14, sinks=True),
                          ids=label)
 def test_random_decode(swa, cfg):
     banner(cfg)
@@ -175,7 +180,7 @@ def test_random_decode(swa, cfg):
     assert max_err(host(out), want) <= TOL[dt]
 
 
-@pytest.mark.parametrize("cfg", diff_decode_configs(8, 15), ids=label)
+@pytest.mark.parametrize("cfg", diff_decode_configs(8 * SCALE, 15), ids=label)
 def test_random_diff_decode(swa, cfg):
     banner(cfg)
     dt = cfg["dtype"]
