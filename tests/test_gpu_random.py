@@ -121,9 +121,31 @@ def diff_decode_configs(n, seed):
     return out
 
 
+def long_configs(n, seed):
+    """Long sequences (1,000-30,000 tokens), checked on sampled rows: windows
+    up to 4,096 keys or wider than the sequence, stride, dilation up to the
+    key-tile size, global tokens, one or two maps."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1000, 30001))
+        two = rng.random() < 0.3
+        d = int(rng.choice([32, 64, 128]))
+        out.append(dict(dtype="bf16" if rng.random() < 0.75 else "f32", B=1,
+                        Hq=int(rng.choice([1, 2, 4])), Hkv=1, N=N, d=d,
+                        dv=int(rng.choice([32, 64, 128])) if two else d,
+                        window=int(rng.integers(1, 4097)) if rng.random() < 0.9 else N + 5,
+                        stride=0 if rng.random() < 0.5 else int(rng.integers(1, 3000)),
+                        dilation=1 if rng.random() < 0.6 else int(rng.integers(2, 65)),
+                        n_global=0 if rng.random() < 0.7 else int(rng.integers(1, 300)),
+                        two=two, scale=1.0 / math.sqrt(d), lam=float(rng.uniform(0, 1)),
+                        seed=10000 + i))
+    return out
+
+
 def label(c):
     keys = ("dtype", "B", "Hq", "Hkv", "N", "d", "dv", "window", "stride", "dilation", "n_global",
-            "n_sink")
+            "n_sink", "two")
     return " ".join(f"{k}={c[k]}" for k in keys if k in c)
 
 
@@ -191,3 +213,26 @@ def test_random_diff_decode(swa, cfg):
     want = oracle.diff_decode(ins["q1"], ins["k1_ring"], ins["q2"], ins["k2_ring"], ins["v_ring"],
                               ins["seq_len"], cfg["scale"], cfg["lam"])
     assert max_err(host(out), want) <= TOL[dt]
+
+
+@pytest.mark.parametrize("cfg", long_configs(6 * SCALE, 16), ids=label)
+def test_random_long_sampled(swa, cfg):
+    banner(cfg)
+    dt, N, Hq, dv = cfg["dtype"], cfg["N"], cfg["Hq"], cfg["dv"]
+    W, s, dil, g = cfg["window"], cfg["stride"], cfg["dilation"], cfg["n_global"]
+    rng = np.random.default_rng(cfg["seed"])
+    rows = np.unique(np.concatenate([rng.integers(0, Hq * N, size=48), [0, N - 1, Hq * N - 1]]))
+    if cfg["two"]:
+        ins = synth.diff_inputs(cfg)
+        mask = swa.swa_block_mask_build(N, W, s, dtype=tdtype(dt), d=cfg["d"], dv=dv, op=swa.SWA_OP_DIFF,
+                                        dilation=dil, n_global=g)
+        out = swa.diff_attn_fwd(*(dev(x, dt) for x in ins), W, s, cfg["scale"], cfg["lam"], mask)
+        want = oracle.diff_rows(*ins, W, s, cfg["scale"], cfg["lam"], rows, dilation=dil, n_global=g)
+    else:
+        q, k, v = synth.prefill_inputs(cfg)
+        mask = swa.swa_block_mask_build(N, W, s, dtype=tdtype(dt), d=cfg["d"], dilation=dil, n_global=g)
+        out = swa.swa_attn_fwd(dev(q, dt), dev(k, dt), dev(v, dt), W, s, cfg["scale"], mask)
+        want = oracle.attn_rows(q, k, v, W, s, cfg["scale"], rows, dilation=dil, n_global=g)
+    got = host(out).reshape(-1, dv)
+    assert np.all(np.isfinite(got))
+    assert max_err(got[rows], want) <= TOL[dt]
