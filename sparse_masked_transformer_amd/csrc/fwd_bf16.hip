@@ -104,6 +104,18 @@ struct Params {
 // ceil((N - r) / dil)), so no cell off the lattice is computed.  In MODE 2
 // the workgroup's class is part of its tile index, row and key indices are
 // class-local, and position = r + dil * index.
+// Bits lo..hi (inclusive) of a 32-bit word, the range clipped to 0..31;
+// zero when it is empty.
+__device__ __forceinline__ uint32_t bit_range(int lo, int hi) {
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 31 ? 31 : hi;
+    if (hi < lo)
+        return 0u;
+    return ((2u << hi) - 1u) & (~0u << lo);   // 2u << 31 wraps to 0: all bits
+}
+
+constexpr int kNegInfBits = static_cast<int>(0xff800000u);   // -inf as fp32 bits
+
 template <int D, int DV, int NMAPS, int RG, int MODE>
 __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
     constexpr int WAVES = 4 * NMAPS;   // waves per workgroup: 4 per score map
@@ -380,42 +392,34 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                         sh[rg][kb][r] = kcst < lim ? sh[rg][kb][r] : ninf;
                     }
                 } else {
-                    // dist = i - j = base - kc; window part iff 0 <= dist < W
-                    // (dilation 1), else dist <= span on the dilation lattice
+                    // One bit word per lane for its 16 cells (bit kc: key
+                    // kb*32 + kc + 4*hl), then one bit-field select per cell.
+                    // dist = i - j = base - kc; the window part is 0 <= dist < W
+                    // (dilation 1), else dist <= span on the dilation lattice;
+                    // column keys (smask) count wherever dist >= 0.
                     const int base = my_row[rg] - key0 - kb * 32 - 4 * hl;
-                    const unsigned W = (unsigned)p.window;
-                    if (smask == 0 && dil == 1) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int kcst = (r & 3) + 8 * (r >> 2);
-                            const bool ok = (unsigned)(base - kcst) < W;
-                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
-                        }
-                    } else if (dil == 1) {
-                        const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int kcst = (r & 3) + 8 * (r >> 2);
-                            const int dist = base - kcst;
-                            // bitwise, not short-circuit: no per-cell branch
-                            const bool ok = ((unsigned)dist < W) |
-                                            ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
-                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
-                        }
+                    uint32_t bits;
+                    if (dil == 1) {
+                        const int64_t lo = static_cast<int64_t>(base) - p.window + 1;
+                        bits = bit_range(lo > 0 ? static_cast<int>(lo) : 0, base);
                     } else {
-                        const uint32_t lm = (uint32_t)(smask >> (kb * 32 + 4 * hl));
                         // lattice bit kc set iff base - kc is a multiple of the dilation
                         int res = base % dil;
                         res += res < 0 ? dil : 0;
-                        const uint32_t lat = (uint32_t)(lattice << res);
+                        bits = bit_range(base - span, base) & static_cast<uint32_t>(lattice << res);
+                    }
+                    if (smask != 0)
+                        bits |= static_cast<uint32_t>(smask >> (kb * 32 + 4 * hl)) & bit_range(0, base);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int kcst = (r & 3) + 8 * (r >> 2);
-                            const int dist = base - kcst;
-                            const bool ok = (((unsigned)dist <= (unsigned)span) & (((lat >> kcst) & 1u) != 0)) |
-                                            ((dist >= 0) & (((lm >> kcst) & 1u) != 0));
-                            sh[rg][kb][r] = ok ? sh[rg][kb][r] : ninf;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int kcst = (r & 3) + 8 * (r >> 2);
+                        // all ones iff bit kcst is set (sign-extended bit field)
+                        const int keep = static_cast<int>(bits << (31 - kcst)) >> 31;
+                        // through a scalar: a bit_cast of the vector element itself
+                        // reads element 0 (hipcc of ROCm 7.2)
+                        const float sc = sh[rg][kb][r];
+                        const int sv = __builtin_bit_cast(int, sc);
+                        sh[rg][kb][r] = __builtin_bit_cast(float, (sv & keep) | (kNegInfBits & ~keep));
                     }
                 }
             };
