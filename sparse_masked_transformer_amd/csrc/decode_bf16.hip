@@ -47,11 +47,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
 
 // 16-byte load from a global byte address (a global load; a generic pointer
-// rebuilt from an integer would become a flat load).  The ring is read once
-// per step, so the loads carry the nontemporal hint (`nt`): the window decode
-// workload reads KV at 6.6 TB/s with it against 5.8 TB/s without.
+// rebuilt from an integer would become a flat load).  NT adds the
+// nontemporal hint (`nt`), for rings that one workgroup reads once: the
+// window decode workload then reads KV at 6.6 TB/s against 5.8 TB/s without.
+// Where several blocks of query heads read the same ring the hint costs the
+// L2 hits of the later blocks (64 query heads on one KV head: 66 against
+// 50 us), so those launches load without it.
+template <bool NT>
 __device__ inline u32x4 load16(uintptr_t addr) {
-    return __builtin_nontemporal_load(reinterpret_cast<global_u32x4 *>(addr));
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<global_u32x4 *>(addr));
+    else
+        return *reinterpret_cast<global_u32x4 *>(addr);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -105,7 +112,7 @@ struct Params {
     float lambda;
 };
 
-template <int D, int DV, int NMAPS>
+template <int D, int DV, int NMAPS, bool NT>
 __global__ __launch_bounds__(64 * kDecodeMaxWaves)
 __attribute__((amdgpu_waves_per_eu(occupancy<D, DV, NMAPS>())))
 void decode_kernel(Params p) {
@@ -191,7 +198,7 @@ void decode_kernel(Params p) {
             const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * D) + c * 16;
 #pragma unroll
             for (int m = 0; m < NMAPS; ++m)
-                kst[reg][m][u] = load16((in_sink ? ksink_b[m] : kring_b[m]) + off);
+                kst[reg][m][u] = load16<NT>((in_sink ? ksink_b[m] : kring_b[m]) + off);
         }
 #pragma unroll
         for (int u = 0; u < Y::vChunks; ++u) {
@@ -200,7 +207,7 @@ void decode_kernel(Params p) {
             const int vs = base + r < v1 ? base + r : v1 - 1;
             const bool in_sink = vs < s_eff;
             const uintptr_t off = static_cast<uintptr_t>(in_sink ? vs : vs - s_eff) * (2 * DV) + c * 16;
-            vst[reg][u] = load16((in_sink ? vsink_b : vring_b) + off);
+            vst[reg][u] = load16<NT>((in_sink ? vsink_b : vring_b) + off);
         }
     };
     char *smem = dsm + wave * Y::wave_bytes;
@@ -471,16 +478,19 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
 
     const int group = a.Hq / a.Hkv;
     const size_t lds = lds_bytes<D, DV, NMAPS>(plan.waves, group < 16 ? group : 16);
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * plan.splits);
+    const unsigned blocks = static_cast<unsigned>(decode_head_blocks(a.Hq, a.Hkv));
+    // one block of query heads reads each ring once: nontemporal loads
+    void (*kernel)(Params) = blocks == 1 ? decode_kernel<D, DV, NMAPS, true>
+                                         : decode_kernel<D, DV, NMAPS, false>;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<D, DV, NMAPS>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess)
             return e;
     }
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * plan.splits);
-    const unsigned blocks = static_cast<unsigned>(decode_head_blocks(a.Hq, a.Hkv));
-    hipLaunchKernelGGL((decode_kernel<D, DV, NMAPS>), dim3(grid, blocks), dim3(64 * plan.waves),
+    hipLaunchKernelGGL(kernel, dim3(grid, blocks), dim3(64 * plan.waves),
                        static_cast<unsigned>(lds), stream, p);
     if (plan.splits > 1)
         hipLaunchKernelGGL((decode_combine_kernel<DV, NMAPS>), dim3(static_cast<unsigned>((rows + 3) / 4)),
