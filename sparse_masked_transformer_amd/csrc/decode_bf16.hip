@@ -18,7 +18,8 @@
 // dimension y); each wave takes a contiguous run of whole 32-slot steps.
 // (With more than 16 query heads per key/value head, each block of 16 reads
 // the head's keys and values again; the blocks run side by side, so the
-// repeats mostly hit L2.)
+// repeats mostly hit L2.  With a single block the loads carry the
+// nontemporal hint instead.)
 //   * A wave streams its slots 32 at a time: coalesced 16-byte loads into
 //     registers two steps ahead (two register stages; one for two maps with
 //     2 d + dv > 256), then into its own LDS area, rows padded (K +16 bytes,
