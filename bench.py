@@ -400,7 +400,7 @@ def main():
         dsrc = os.path.join(ROOT, "sparse_masked_transformer_amd", "csrc", "decode_bf16.hip")
         line["decode"] = {"workload": "window_decode_bf16", "value": round(dd["gbs"], 1), "unit": "GB/s",
                           "kv_gbs": round(dd["kv_gbs"], 1), "us_per_step": round(dd["event_ms"] * 1e3, 2),
-                          "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,1,true>",
+                          "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,128,1,true,false>",
                                        "achieved": round(dd["gbs"], 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": round(dd["gbs"] / PEAK_HBM_GBS, 4),
