@@ -39,8 +39,10 @@
  *     query head, query tile) of 256 lanes (512 for diff_attn_fwd in bf16);
  *     the decode calls' launches are sized by their own work split.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
- *   - No global mutable state: calls on different streams may overlap as
- *     long as their output buffers do not.
+ *   - No global mutable state, except the static scratch array of
+ *     swa_attn_decode_noalloc: calls on different streams may overlap as
+ *     long as their output buffers do not (and, for swa_attn_decode_noalloc,
+ *     as long as they run on different GPUs).
  */
 #ifndef SWA_H
 #define SWA_H
@@ -61,7 +63,9 @@ typedef enum {
     SWA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, inconsistent mask */
     SWA_ERR_UNSUPPORTED = -2, /* valid request this library does not implement      */
     SWA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small               */
-    SWA_ERR_HIP = -4          /* a HIP launch reported an error                       */
+    SWA_ERR_HIP = -4,         /* a HIP launch reported an error                       */
+    SWA_ERR_SCRATCH = -5      /* swa_attn_decode_noalloc: the call needs more than    */
+                              /* SWA_DECODE_SCRATCH_BYTES of scratch                  */
 } swa_status_t;
 
 typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
@@ -248,6 +252,31 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
                   const void *v, void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N,
                   int d, int dv, int window, int stride, int dilation, int n_global, float scale,
                   float lambda, const swa_block_mask_t *mask, hipStream_t stream);
+
+/*
+ * swa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It runs the kernels of swa_attn_decode
+ * and gives them a file-scope device array of SWA_DECODE_SCRATCH_BYTES in
+ * place of the caller's workspace; the library calls no allocating routine.
+ *   Arguments: as swa_attn_decode minus workspace and workspace_bytes.
+ *   A call whose swa_attn_decode_workspace_bytes(SWA_OP_ATTN, B, Hq, Hkv, d,
+ *   window, 0) exceeds SWA_DECODE_SCRATCH_BYTES returns SWA_ERR_SCRATCH
+ *   (checked on the host before any HIP call); other checks and errors as
+ *   swa_attn_decode.
+ *   Each GPU holds its own copy of the array from the first call on that GPU
+ *   (its address is looked up once per device, with that device current)
+ *   until the process ends.  Every call on one GPU uses that GPU's array:
+ *   calls that overlap in time on one GPU (other streams, other host threads)
+ *   race on it and must be serialized by the caller, e.g. on one stream.  The
+ *   kernels write every partial result before reading it, so what an earlier
+ *   call left in the array does not matter.
+ */
+#define SWA_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
+int swa_attn_decode_noalloc(const void *q, const void *k_ring, const void *v_ring, void *out,
+                            const int32_t *seq_len, swa_dtype_t dt, int B, int Hq, int Hkv,
+                            int N, int d, int window, int stride, float scale,
+                            hipStream_t stream);
 
 /* Static description of a status code. */
 const char *swa_strerror(int status);

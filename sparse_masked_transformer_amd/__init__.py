@@ -22,6 +22,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP = 0, -1, -2, -3, -4
+SWA_ERR_SCRATCH = -5
+SWA_DECODE_SCRATCH_BYTES = 4 << 20
 SWA_F32, SWA_BF16 = 0, 1
 SWA_OP_ATTN, SWA_OP_DIFF = 0, 1
 SWA_MAX_N = 1 << 22
@@ -56,6 +58,9 @@ _lib.swa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.swa_attn_decode.restype = _i
 _lib.swa_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i, _i, _i,
                                  _i, _i, ctypes.c_float, _p]
+_lib.swa_attn_decode_noalloc.restype = _i
+_lib.swa_attn_decode_noalloc.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                         ctypes.c_float, _p]
 _lib.swa_attn_decode_sinks.restype = _i
 _lib.swa_attn_decode_sinks.argtypes = [_p, _p, _p, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i,
                                        _i, _i, _i, _i, _i, ctypes.c_float, _p]
@@ -268,6 +273,23 @@ def swa_attn_decode(q, k_ring, v_ring, seq_len, scale, workspace=None, out=None,
     return out
 
 
+def swa_attn_decode_noalloc(q, k_ring, v_ring, seq_len, scale, out, N=0, stride=0):
+    """swa_attn_decode with the library's static per-GPU scratch in place of a
+    workspace: the call itself allocates nothing (`out` is required).  Calls
+    that overlap in time on one GPU race on that scratch."""
+    B, Hq, d = _dims(q, "q", 3)
+    _, Hkv, W, _ = _dims(k_ring, "k_ring", 4)
+    dev = q.device
+    for t, n in ((k_ring, "k_ring"), (v_ring, "v_ring")):
+        _expect(t, n, (B, Hkv, W, d), q.dtype, dev)
+    _expect_seq_len(seq_len, B, dev)
+    _expect(out, "out", (B, Hq, d), q.dtype, dev)
+    _check(_lib.swa_attn_decode_noalloc(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(out), _ptr(seq_len),
+                                        _dtype_code(q), B, Hq, Hkv, N, d, W, stride, float(scale),
+                                        _stream(q)), "swa_attn_decode_noalloc")
+    return out
+
+
 def swa_attn_decode_sinks(q, k_sink, v_sink, k_ring, v_ring, seq_len, scale, workspace=None,
                           out=None, N=0):
     """Decode step with sink slots.  k_sink/v_sink [B,Hkv,S,d] hold positions
@@ -340,6 +362,6 @@ def diff_attn_fwd(q1, k1, q2, k2, v, window, stride, scale, lam, mask, out=None)
 
 
 __all__ = ["swa_tile_config", "swa_block_mask_query", "swa_block_mask_build", "swa_mask_dense",
-           "swa_attn_fwd", "swa_attn_decode_workspace_bytes", "swa_attn_decode",
+           "swa_attn_fwd", "swa_attn_decode_workspace_bytes", "swa_attn_decode", "swa_attn_decode_noalloc",
            "swa_attn_decode_sinks", "diff_attn_decode", "diff_attn_fwd",
            "swa_strerror", "SwaError", "BlockMask"]

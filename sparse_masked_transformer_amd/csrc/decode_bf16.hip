@@ -34,9 +34,45 @@
 //     With one split the workgroup writes the output; otherwise it writes a
 //     partial to the workspace and a combine kernel merges the splits:
 //     m* = max m_s, l* = sum l_s 2^(m_s - m*), o = sum o_s 2^(m_s - m*) / l*.
+#include <mutex>
+
 #include "swa_internal.h"
 
 namespace swa {
+
+// Scratch of swa_attn_decode_noalloc: the split partials (max, sum, output)
+// that the combine kernel merges, in a file-scope array instead of a
+// caller's workspace.  Each GPU holds its own copy.  In host code the name
+// `scratch` is only a stand-in for the symbol; the device address comes from
+// decode_static_scratch.
+static __device__ __align__(256) char scratch[SWA_DECODE_SCRATCH_BYTES];
+
+hipError_t decode_static_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // once per device, with that device current (the caller's current
+        // device is the one its stream belongs to)
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -161,8 +161,9 @@ size_t decode_ws_bytes(int nmaps, int B, int Hq, int Hkv, int dv, int window, in
     return static_cast<size_t>(swa::decode_ws_ml_floats(parts) + parts * dv) * sizeof(float);
 }
 
-// Checks shared by the decode entry points; fills nothing on failure.
-int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes) {
+// Checks shared by the decode entry points, all but the workspace's; fills
+// nothing on failure.
+int decode_arg_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride) {
     for (int m = 0; m < a.nmaps; ++m) {
         if (!aligned16(a.q[m]) || !aligned16(a.k_ring[m]))
             return SWA_ERR_INVALID_ARG;
@@ -192,6 +193,13 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
         return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
     if (dt == SWA_BF16 && swa::decode_head_blocks(a.Hq, a.Hkv) > 65535)
         return SWA_ERR_UNSUPPORTED;  // blocks of 16 query heads fill the grid's y dimension
+    return SWA_OK;
+}
+
+int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes) {
+    int st = decode_arg_checks(a, dt, stride);
+    if (st != SWA_OK)
+        return st;
     const size_t need = decode_ws_bytes(a.nmaps, a.B, a.Hq, a.Hkv, a.dv, a.window, a.n_sink);
     if (need > 0 && (a.workspace == nullptr || !aligned16(a.workspace) || workspace_bytes < need))
         return SWA_ERR_WORKSPACE;
@@ -323,6 +331,42 @@ int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void 
     return decode_run(a, dt, stride, workspace_bytes, stream);
 }
 
+int swa_attn_decode_noalloc(const void *q, const void *k_ring, const void *v_ring, void *out,
+                            const int32_t *seq_len, swa_dtype_t dt, int B, int Hq, int Hkv,
+                            int N, int d, int window, int stride, float scale,
+                            hipStream_t stream) {
+    swa::DecodeArgs a{};
+    a.q[0] = q;
+    a.k_ring[0] = k_ring;
+    a.v_ring = v_ring;
+    a.out = out;
+    a.seq_len = seq_len;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.dv = d;
+    a.window = window;
+    a.n_sink = 0;
+    a.nmaps = 1;
+    a.scale = scale;
+    a.lambda = 0.f;
+    // every check, the scratch bound included, before the first HIP call
+    int st = decode_arg_checks(a, dt, stride);
+    if (st != SWA_OK)
+        return st;
+    const size_t need = decode_ws_bytes(a.nmaps, a.B, a.Hq, a.Hkv, a.dv, a.window, a.n_sink);
+    if (need > SWA_DECODE_SCRATCH_BYTES)
+        return SWA_ERR_SCRATCH;
+    if (need > 0) {
+        st = hip_status(swa::decode_static_scratch(&a.workspace));
+        if (st != SWA_OK)
+            return st;
+    }
+    return decode_run(a, dt, stride, need > 0 ? SWA_DECODE_SCRATCH_BYTES : 0, stream);
+}
+
 int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink, int n_sink,
                           const void *k_ring, const void *v_ring, void *out,
                           const int32_t *seq_len, void *workspace, size_t workspace_bytes,
@@ -434,6 +478,9 @@ const char *swa_strerror(int status) {
         return "decode workspace missing or too small";
     case SWA_ERR_HIP:
         return "HIP launch error";
+    case SWA_ERR_SCRATCH:
+        return "decode needs more scratch than the no-allocation entry point holds "
+               "(SWA_DECODE_SCRATCH_BYTES)";
     default:
         return "unknown status";
     }

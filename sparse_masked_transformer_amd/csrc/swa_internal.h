@@ -138,6 +138,10 @@ int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt);
 // partial results, padded so the output section starts 16-byte aligned.
 inline int64_t decode_ws_ml_floats(int64_t parts) { return (parts * 2 + 3) / 4 * 4; }
 
+// Address, on the current device, of the decode kernels' static scratch
+// array (SWA_DECODE_SCRATCH_BYTES): looked up once per device.
+hipError_t decode_static_scratch(void **ptr);
+
 hipError_t launch_block_mask_build(const swa_block_mask_t &m, hipStream_t stream);
 hipError_t launch_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
                              hipStream_t stream);

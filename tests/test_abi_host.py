@@ -42,7 +42,7 @@ def test_header_declares_the_hot_path_calls():
     for n in ("swa_block_mask_build", "swa_attn_fwd", "swa_attn_decode", "swa_attn_decode_sinks",
               "diff_attn_fwd", "diff_attn_decode"):
         assert n in names
-    assert len(names) == 11, names
+    assert len(names) == 12, names
 
 
 def test_library_exports_every_declared_symbol(swa):
@@ -68,7 +68,7 @@ def test_library_does_not_touch_the_oracle(swa):
 
 def test_strerror(swa):
     assert swa.swa_strerror(0) == "success"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert swa.swa_strerror(code) not in ("success", "unknown status")
     assert swa.swa_strerror(-99) == "unknown status"
 
@@ -202,6 +202,30 @@ def test_decode_rejections(swa):
     assert dec(swa, ws=0) == WS
     assert dec(swa, wsb=swa.swa_attn_decode_workspace_bytes(2, 8, 2, 128, 64) - 4) == WS
     assert dec(swa, ws=FAKE + 8) == WS
+
+
+def test_decode_noalloc_rejections(swa):
+    """The no-allocation decode runs every check of swa_attn_decode, plus the
+    bound of its static scratch, before its first HIP call."""
+    E, U, SC = swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED, swa.SWA_ERR_SCRATCH
+
+    def call(q=FAKE, vr=FAKE, sl=None, dt=1, B=2, Hq=8, Hkv=2, N=100, d=128, W=64, s=0, scale=0.1):
+        return swa.lib.swa_attn_decode_noalloc(q, FAKE, vr, FAKE, sl, dt, B, Hq, Hkv, N, d, W, s, scale,
+                                               None)
+    assert call(q=0) == E
+    assert call(vr=FAKE + 4) == E
+    assert call(sl=FAKE + 2) == E
+    assert call(Hq=6, Hkv=4) == E
+    assert call(W=0) == E
+    assert call(scale=float("inf")) == E
+    assert call(d=96) == U
+    assert call(s=3) == U
+    # 1024 query heads on one key/value head: 64 blocks of 16, 8 splits of a
+    # 4096-slot ring -> 8192 partials of 130 floats, beyond the 4 MiB scratch
+    need = swa.swa_attn_decode_workspace_bytes(1, 1024, 1, 128, 4096)
+    assert need > swa.SWA_DECODE_SCRATCH_BYTES
+    assert call(B=1, Hq=1024, Hkv=1, W=4096) == SC
+    assert swa.swa_strerror(SC) not in ("success", "unknown status")
 
 
 def test_decode_rejects_grids_beyond_one_dispatch(swa):
