@@ -146,6 +146,13 @@ hipError_t launch_block_mask_build(const swa_block_mask_t &m, hipStream_t stream
 hipError_t launch_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
                              hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
+// The generated assembly kernel for grouped-query sliding windows (bf16,
+// d = dv = 128, no stride, dilation or global tokens, a multiple of 4 query
+// heads per key/value head): whether it serves `a`, its workgroup count,
+// and its launch.
+bool fwd_gqa_applies(const FwdArgs &a);
+int64_t fwd_gqa_workgroups(const FwdArgs &a);
+hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t stream);

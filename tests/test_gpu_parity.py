@@ -19,6 +19,10 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
+# log-sum-exp: bf16 kernels may sum the bf16-rounded probabilities (each
+# within a relative 2^-8 of its exact value), so their log of the row sum is
+# within ln(1 + 2^-8) < 4e-3 of the exact one; fp32 kernels sum in fp32
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 @pytest.fixture(scope="module")
@@ -138,7 +142,7 @@ def test_prefill_parity_small(swa, dtype, B, Hq, Hkv, N, d, W, s):
     got, lse = run_prefill(swa, cfg, q, k, v, with_lse=True)
     want, want_lse = oracle.attn_full(q, k, v, W, s, cfg["scale"], with_lse=True)
     assert max_err(got, want) <= TOL[dtype]
-    assert max_err(lse, want_lse) <= (1e-3 if dtype == "bf16" else 1e-5)
+    assert max_err(lse, want_lse) <= LSE_TOL[dtype]
 
 
 PREFILL_EXT_CASES = [
@@ -175,7 +179,7 @@ def test_prefill_dilated_global_parity(swa, dtype, B, Hq, Hkv, N, d, W, s, dil, 
     want, want_lse = oracle.attn_full(q, k, v, W, s, cfg["scale"], with_lse=True, dilation=dil,
                                       n_global=g)
     assert max_err(got, want) <= TOL[dtype]
-    assert max_err(lse, want_lse) <= (1e-3 if dtype == "bf16" else 1e-5)
+    assert max_err(lse, want_lse) <= LSE_TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
