@@ -433,7 +433,9 @@ V_LT = [[v(247), v(248)], [v(249), v(250)]]   # this tile's row sums (two partia
 V_KADDR, V_VADDR = v(217), v(218)
 V_IBASE = [v(219), v(220)]           # row - 4 * (lane / 32), for the per-cell mask
 V_T = [v(222 + i) for i in range(16)]  # even start: pairs of them are 64-bit tuples
-V_OOFF = [v(238), v(239)]
+V_OOFF = [v(238), v(239)]           # (spare since the output goes through LDS)
+V_OWL, V_ORDL, V_OST = v(251), v(252), v(253)   # epilogue lane bases: LDS write, LDS read, global store
+V_OW, V_ORD = v(254), v(255)
 V_LOFF = [v(240), v(241)]
 V_COL, V_HL, V_LANE = v(242), v(243), v(244)
 
@@ -630,13 +632,22 @@ def max_ops(sbuf, rg, track_flag):
     a list of emit callbacks (one instruction each)."""
     sv = [v(sbuf + 32 * rg + k) for k in range(32)]
     t, t1, t2, t3 = V_T[8 + 4 * rg], V_T[9 + 4 * rg], V_T[10 + 4 * rg], V_T[11 + 4 * rg]
+    acc = [t, t1, t2, t3]
     ops = []
-    ops.append(lambda P: P.valu("v_max3_f32", t, sv[0], sv[1], sv[2]))
-    k = 3
-    while k + 1 < 32:
-        ops.append(lambda P, k=k: P.valu("v_max3_f32", t, t, sv[k], sv[k + 1]))
-        k += 2
-    ops.append(lambda P: P.valu("v_max_f32", t, t, sv[31]))
+    # four independent chains over 8 scores each (short dependency chains),
+    # interleaved, then combined
+    for step in range(4):
+        for c in range(4):
+            b = 8 * c
+            if step == 0:
+                ops.append(lambda P, c=c, b=b: P.valu("v_max3_f32", acc[c], sv[b], sv[b + 1], sv[b + 2]))
+            elif step < 3:
+                k = b + 1 + 2 * step
+                ops.append(lambda P, c=c, k=k: P.valu("v_max3_f32", acc[c], acc[c], sv[k], sv[k + 1]))
+            else:
+                ops.append(lambda P, c=c, b=b: P.valu("v_max_f32", acc[c], acc[c], sv[b + 7]))
+    ops.append(lambda P: P.valu("v_max3_f32", t, t, t1, t2))
+    ops.append(lambda P: P.valu("v_max_f32", t, t, t3))
     ops.append(lambda P: P.valu("v_mov_b32", t1, t))
     ops.append(lambda P: P.add(I(f"  v_permlane32_swap_b32 {t}, {t1}", "perm", regs_of(t, t1), regs_of(t, t1))))
     ops.append(lambda P: P.valu("v_max_f32", t, t, t1))
@@ -644,8 +655,12 @@ def max_ops(sbuf, rg, track_flag):
     ops.append(lambda P: P.add(I(f"  v_cmp_gt_f32 {S_CMP[rg]}, {t}, {V_MTHR[rg]}", "vcmp",
                                  regs_of(t, V_MTHR[rg]), S_CMP[rg].regs())))
     ops.append(lambda P: P.valu("v_max_f32", t2, V_M[rg], t))                # candidate maximum
-    ops.append(lambda P: P.scmp("s_cmp_lg_u64", S_CMP[rg], "0"))
-    ops.append(lambda P: P.salu("s_cselect_b64", S_MV[rg], "-1", "0", reads_scc=True, writes_scc=False))
+    # (compare and select in one op: merged op lists must not split an SCC
+    # producer from its consumer)
+    def moved(P):
+        P.scmp("s_cmp_lg_u64", S_CMP[rg], "0")
+        P.salu("s_cselect_b64", S_MV[rg], "-1", "0", reads_scc=True, writes_scc=False)
+    ops.append(moved)
     ops.append(lambda P: P.valu("v_mov_b32", V_MOLD[rg], V_M[rg]))
     ops.append(lambda P: P.valu("v_cndmask_b32", V_M[rg], V_M[rg], t2, S_MV[rg]))  # moved (any lane) ? new : old
     ops.append(lambda P: P.salu("s_or_b64", S_FLAG, S_FLAG, S_MV[rg]))
@@ -661,7 +676,9 @@ def exp_ops(sbuf, rg, kb):
     for k in range(16):
         ops.append(lambda P, k=k: P.valu("v_fma_f32", sv[k], sv[k], S_C, NegR(V_M[rg])))
     for k in range(16):
-        ops.append(lambda P, k=k: P.valu("v_exp_f32", sv[k], sv[k], kind="trans"))
+        op = (lambda P, k=k: P.valu("v_exp_f32", sv[k], sv[k], kind="trans"))
+        op.cost = 2.0
+        ops.append(op)
     lt = V_LT[rg]
     if OPT["fp32_sums"]:
         if kb == 0:
@@ -676,11 +693,22 @@ def exp_ops(sbuf, rg, kb):
         ops.append(lambda P, i=i: P.valu("v_cvt_pk_bf16_f32", sv[i], sv[2 * i], sv[2 * i + 1]))
     if not OPT["fp32_sums"]:
         for i in range(8):
+            a = i % 2            # (the key half kb = 0 initializes both partials)
             if kb == 0 and i < 2:
-                ops.append(lambda P, i=i: P.valu("v_dot2_f32_bf16", lt[i % 2], sv[i], S_ONES, "0"))
+                ops.append(lambda P, i=i, a=a: P.valu("v_dot2_f32_bf16", lt[a], sv[i], S_ONES, "0"))
             else:
-                ops.append(lambda P, i=i: P.valu("v_dot2_f32_bf16", lt[i % 2], sv[i], S_ONES, lt[i % 2]))
+                ops.append(lambda P, i=i, a=a: P.valu("v_dot2_f32_bf16", lt[a], sv[i], S_ONES, lt[a]))
     return ops
+
+
+def merge_rr(lists):
+    """Round-robin merge of op lists (the i-th op of each list, in turn)."""
+    out = []
+    for i in range(max(len(x) for x in lists)):
+        for x in lists:
+            if i < len(x):
+                out.append(x[i])
+    return out
 
 
 def mask_block(P, sbuf):
@@ -747,21 +775,23 @@ def interleave(P, pairs, valu_ops, extra_ops=()):
         pairs[k][0](P)
     extra = list(extra_ops)
     every = max(1, (n_mfma - 8) // max(1, len(extra))) if extra else 0
+    # issue cost of each op (transcendentals take two VALU slots)
+    costs = [getattr(op, "cost", 1.0) for op in valu_ops]
+    total = sum(costs)
     vi = 0
     done = 0
+    spent = 0.0
     for p_idx, (rd, mf) in enumerate(pairs):
         for half in range(2):
             mf(P, half)
             done += 1
             if extra and done % every == 0:
                 extra.pop(0)(P)
-            remaining = len(valu_ops) - vi
-            left = n_mfma - done + 1
-            take = -(-remaining // left) if left > 0 else remaining
-            for _ in range(take):
-                if vi < len(valu_ops):
-                    valu_ops[vi](P)
-                    vi += 1
+            target = total * done / n_mfma
+            while vi < len(valu_ops) and spent + 0.5 * costs[vi] <= target:
+                valu_ops[vi](P)
+                spent += costs[vi]
+                vi += 1
             if half == 0 and p_idx + PREFETCH < len(pairs):
                 pairs[p_idx + PREFETCH][0](P)
     while vi < len(valu_ops):
@@ -813,6 +843,8 @@ def iteration(P, phase, has_qk, has_pv, first):
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
     P.waitcnt(vm=0)
     P.barrier()
+    if has_pv:
+        settle_previous(P)
     # DMA of tile j + 2 into stage (j + 2) & 3; past the band (j + 2 >= T)
     # the offset is N rows, out of the descriptor's range: the loads read
     # zeros without touching memory, into a stage nothing reads
@@ -848,18 +880,32 @@ def iteration(P, phase, has_qk, has_pv, first):
     P.label(skip)
     dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 64)])
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
-    valu = max_ops(sb_cur, 0, has_pv) + max_ops(sb_cur, 1, has_pv)
-    for rg in range(2):
-        for kb in range(2):
-            valu += exp_ops(sb_cur, rg, kb)
+    valu = merge_rr([max_ops(sb_cur, 0, has_pv), max_ops(sb_cur, 1, has_pv)])
+    # (blocks in the order (rg, kb) = (0,0), (1,0), (0,1), (1,1): a key half
+    # 1 op accumulates into the partial its key half 0 op initialized two
+    # ops earlier)
+    valu += merge_rr([exp_ops(sb_cur, rg, kb) for kb in range(2) for rg in range(2)])
     pairs = make_pairs(has_qk, has_pv, sb_next, sb_prev)
     interleave(P, pairs, valu, dma_ops() if has_qk else [])
     dump(P, f"soft{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 64), V_M[0], V_M[1], V_L[0][0], V_L[0][1],
                                                         V_L[1][0], V_L[1][1], V_ALPHA[0], V_ALPHA[1]])
+    if not has_pv:
+        # first tile: nothing accumulated yet (O = 0, l = 0), so the moved
+        # maximum only moves the threshold; this tile's sums are merged at
+        # the start of the next step
+        for rg in range(2):
+            P.valu("v_add_f32", V_MTHR[rg], str(SLACK), V_M[rg])
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+
+
+def settle_previous(P):
+    """Between the P V products of the previous tile and of this one: if the
+    previous tile moved the running maximum, rescale l and O (rare), then add
+    the previous tile's row sums to l."""
     skip = P.new_label("norescale")
     P.scmp("s_cmp_eq_u64", S_FLAG, "0")
     P.branch("s_cbranch_scc1", skip)
-    rescale_block(P, with_o=has_pv)
+    rescale_block(P, with_o=True)
     P.label(skip)
     for rg in range(2):
         P.valu("v_add_f32", V_L[rg][0], V_L[rg][0], V_LT[rg][0])
@@ -871,6 +917,7 @@ def epilogue(P, phase):
     pbuf = S_BUF[phase]
     P.waitcnt(vm=0)
     P.barrier()
+    settle_previous(P)
     stage_base(P, S_SBV, S_J, 0)
     P.valu("v_add_u32", V_VADDR, S_SBV, V_VLANE)
     pairs = make_pairs(False, True, None, pbuf)
@@ -893,6 +940,18 @@ def epilogue(P, phase):
         P.valu("v_mul_f32", l2, "0x3f317218", l2)
         P.buf_store("buffer_store_dword", l2, V_LOFF[rg], S_RSL)
         P.label(skip)
+    # O / l -> bf16, staged through LDS so the global stores are whole rows
+    # (16 lanes x 16 bytes per 256-byte row) instead of 8-byte pieces of 32
+    # rows.  Each wave uses its own 64 x 272-byte region in the two stages
+    # that do not hold the last V tile (the only one other waves may still
+    # read): stages 0-1 if that tile is in stage 2 or 3, else stages 2-3.
+    P.salu("s_and_b32", S_X[0], S_J, "3")
+    P.scmp("s_cmp_ge_u32", S_X[0], "2")
+    P.salu("s_cselect_b32", S_X[1], "0", str(2 * STAGE), reads_scc=True, writes_scc=False)
+    P.salu("s_mul_i32", S_X[2], S_WAVE, str(64 * KROW))
+    P.salu("s_add_u32", S_X[1], S_X[1], S_X[2])                    # this wave's region
+    P.valu("v_add_u32", V_OW, S_X[1], V_OWL)
+    P.valu("v_add_u32", V_ORD, S_X[1], V_ORDL)
     for rg in range(2):
         inv = t[2 + rg]
         for db in range(4):
@@ -906,7 +965,22 @@ def epilogue(P, phase):
                 pk0, pk1 = t[8 + 2 * (r4 % 2)], t[9 + 2 * (r4 % 2)]
                 P.valu("v_cvt_pk_bf16_f32", pk0, x[0], x[1])
                 P.valu("v_cvt_pk_bf16_f32", pk1, x[2], x[3])
-                P.buf_store("buffer_store_dwordx2", v(pk0.i, 2), V_OOFF[rg], S_RSO, db * 64 + r4 * 16)
+                # row 32 rg + col, values 32 db + 8 r4 + 4 hl .. +3
+                P.add(I(f"  ds_write_b64 {V_OW}, {v(pk0.i, 2)} offset:{rg * 32 * KROW + db * 64 + r4 * 16}", "lds",
+                        regs_of(V_OW, v(pk0.i, 2)), EMPTY))
+    ob = S_BUF[(phase + 1) % 3]                                     # free score buffer
+
+    def rd(kk):
+        # rows 4 kk + lane / 16, bytes 16 (lane % 16) .. +15 of each
+        P.ds_read("ds_read_b128", v(ob + 4 * kk, 4), V_ORD, kk * 4 * KROW)
+    for kk in range(8):
+        rd(kk)
+    for kk in range(16):
+        P.salu("s_mov_b32", S_X[3 + (kk % 4)], str(kk * 1024), writes_scc=False)
+        P.add(I(f"  buffer_store_dwordx4 {v(ob + 4 * kk, 4)}, {V_OST}, {S_RSO}, {S_X[3 + (kk % 4)]} offen",
+                "vstore", regs_of(v(ob + 4 * kk, 4), V_OST, S_RSO, S_X[3 + (kk % 4)]), EMPTY))
+        if kk + 8 < 16:
+            rd(kk + 8)
     P.add(I("  s_endpgm", "branch"))
 
 
@@ -1010,6 +1084,19 @@ def prologue(P):
         P.valu("v_lshlrev_b32", V_LOFF[rg], "2", t[5])
         P.valu("v_lshlrev_b32", t[7], "2", V_HL)
         P.valu("v_sub_u32", V_IBASE[rg], t[5], t[7])
+    # epilogue: LDS write base (row col, values 4 hl: col * 272 + 8 hl), LDS
+    # read base (row lane / 16, bytes 16 (lane % 16)), global store offset
+    P.valu("v_mul_u32_u24", V_OWL, str(KROW), V_COL)
+    P.valu("v_lshlrev_b32", t[0], "3", V_HL)
+    P.valu("v_add_u32", V_OWL, V_OWL, t[0])
+    P.valu("v_lshrrev_b32", t[0], "4", V_LANE)
+    P.valu("v_and_b32", t[1], "15", V_LANE)
+    P.valu("v_lshlrev_b32", t[1], "4", t[1])
+    P.valu("v_mul_u32_u24", V_ORDL, str(KROW), t[0])
+    P.valu("v_add_u32", V_ORDL, V_ORDL, t[1])
+    P.valu("v_add_u32", t[0], S_R0, t[0])
+    P.valu("v_lshlrev_b32", t[0], "8", t[0])
+    P.valu("v_add_u32", V_OST, t[0], t[1])
     # DMA lane offsets: K chunk wave + 4 jk (jk < 4) or 16, V chunk wave + 4 jv
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
     P.valu("v_mov_b32", t[9], S_WAVE1K)
