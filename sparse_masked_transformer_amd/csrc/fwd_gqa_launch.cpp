@@ -88,7 +88,7 @@ hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
     size_t size = sizeof(k);
     void *config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &k, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
                       HIP_LAUNCH_PARAM_END};
-    e = hipModuleLaunchKernel(fn, static_cast<unsigned>(k.workgroups), 1, 1, 256, 1, 1, 0, stream, nullptr,
+    e = hipModuleLaunchKernel(fn, static_cast<unsigned>(k.workgroups), 1, 1, 512, 1, 1, 0, stream, nullptr,
                               config);
     if (e != hipSuccess)
         return e;

@@ -9,34 +9,39 @@ same page): running maximum, running sum and running weighted sum per query
 row while the key tiles of the window stream through LDS.
 
 Work decomposition
-  Workgroup = 4 waves = the 4 query heads h0 .. h0+3 of one key/value head
-  (grouped-query attention), on the same 64 query rows.  Each wave owns 64
-  rows of its head (two row groups of 32), so the K and V tiles staged in
-  LDS serve all four heads, and every wave needs exactly the same key tiles
-  (the band of its 64 rows): no wave idles on a tile its rows cannot see.
-  One workgroup per CU (LDS holds four 64-key stages), one wave per SIMD.
+  Workgroup = 8 waves on the 4 query heads h0 .. h0+3 of one key/value head
+  (grouped-query attention) and the same 64 query rows: wave w takes head
+  h0 + (w & 3) and rows 32 (w >> 2) .. +31 of the block, so the K and V
+  tiles staged in LDS serve all four heads and every wave needs the same key
+  tiles (the band of the 64 rows).  One workgroup per CU (LDS holds four
+  64-key stages), two waves per SIMD: while one wave waits on a dependency
+  or an LDS read, the other issues.
 
-Registers (512 per lane: 256 VGPRs + 256 AGPRs)
-  AGPR  a[0:127]    O^T accumulators, two row groups x 4 blocks of 32 values
-        a[128:191]  Q^T fragments (B operand of S^T = K Q^T), 2 x 8
-        a[192:223]  K fragment ring (A operand), 8 slots
-        a[224:255]  V^T fragment ring (A operand of O^T += V^T P^T), 8 slots
-  VGPR  v[0:191]    three score buffers of 64 values: the tile whose scores
-                    are being computed, the tile whose softmax is running
-                    (its probabilities packed to bf16 in place), and the tile
-                    whose probabilities feed the P V product
-        v[192:255]  addressing, softmax state, temporaries
+Registers (256 per lane: 128 VGPRs + 128 AGPRs, two waves per SIMD)
+  AGPR  a[0:63]     O^T accumulators, 4 blocks of 32 values
+        a[64:95]    Q^T fragments (B operand of S^T = K Q^T), 8
+        a[96:111]   K fragment ring (A operand), 4 slots
+        a[112:127]  V^T fragment ring (A operand of O^T += V^T P^T), 4 slots
+  VGPR  v[0:63]     two score buffers of 32 values: the tile whose scores
+                    are being computed and the tile whose softmax is running
+        v[64:79]    the probabilities that feed the P V product, bf16 pairs
+        v[80:126]   addressing, softmax state, temporaries
 
 Software pipeline (one iteration per 64-key tile j)
-  matrix cores: S(j+1) = K(j+1) Q^T (32 MFMAs) interleaved with
-                O += V(j-1)^T P(j-1) (32 MFMAs)
-  vector ALU:   row maxima of S(j), then p = exp2(s * c - m), the row sums
-                and the bf16 packing of P(j), spread between the MFMAs
-  LDS:          the fragments of both products, a few pairs ahead
-  DMA:          tile j+2 into the fourth stage (buffer_load ... lds)
+  matrix cores: O += V(j-1)^T P(j-1) (16 MFMAs: four, then two per QK MFMA)
+                and S(j+1) = K(j+1) Q^T (16 MFMAs, the last ten after the
+                P V product)
+  vector ALU:   row maxima of S(j), then p = exp2(s * c - m), the bf16
+                packing of P(j) into the P buffer (once the P V product has
+                read it) and the row sums, spread evenly between the MFMAs
+  LDS:          the fragments of both products, three ahead of their MFMA;
+                the first three V fragments of the next step are read before
+                the next barrier (their tile is already in LDS)
+  DMA:          tile j+2 into the fourth stage (buffer_load ... lds), and
+                the scalar set-up of the next step, spread between the MFMAs
 The running maximum moves only when a tile's maximum exceeds it by more than
-8 (log2 units); O is then rescaled at the end of the iteration, after the
-products of the old maximum have been accumulated.
+8 (log2 units); O is then rescaled at the start of the next iteration, after
+the products of the old maximum have been accumulated.
 
 Hazards: every instruction records the registers it reads and writes; a
 final pass inserts the wait states gfx950 requires between producers and
@@ -273,7 +278,7 @@ def _need(p, x):
                 n = max(n, MFMA_RAW)
             if x.writes & p.srcc or x.dests & p.srcc:
                 n = max(n, MFMA_WAR_C)
-            if x.dests & p.srcab:
+            if x.dests & p.srcab or x.writes & p.srcab:
                 n = max(n, 4)
     elif p.kind in ("valu", "trans", "perm", "vcmp", "rfl"):
         vw = frozenset(r for r in p.writes if r[0] in "va")
@@ -418,31 +423,32 @@ def resolve(ins):
 
 
 # ---------------------------------------------------------------------------
-# register map
-S_BUF = [0, 64, 128]                 # three score buffers of 64 VGPRs
-V_TID, V_KLANE, V_VLANE = v(192), v(193), v(194)
-V_DK = [v(195 + i) for i in range(5)]
-V_DV = [v(200 + i) for i in range(5)]
-V_QOFF = [v(205), v(206)]
-V_M = [v(207), v(208)]               # running maximum (scaled, log2 units)
-V_MTHR = [v(209), v(210)]            # running maximum + slack
-V_L = [[v(211), v(212)], [v(213), v(214)]]   # running sums, two partials per row group
-V_ALPHA = [v(215), v(216)]
-V_MOLD = [v(245), v(246)]            # running maximum before this tile
-V_LT = [[v(247), v(248)], [v(249), v(250)]]   # this tile's row sums (two partials per row group)
-V_KADDR, V_VADDR = v(217), v(218)
-V_IBASE = [v(219), v(220)]           # row - 4 * (lane / 32), for the per-cell mask
-V_T = [v(222 + i) for i in range(16)]  # even start: pairs of them are 64-bit tuples
-V_OOFF = [v(238), v(239)]           # (spare since the output goes through LDS)
-V_OWL, V_ORDL, V_OST = v(251), v(252), v(253)   # epilogue lane bases: LDS write, LDS read, global store
-V_OW, V_ORD = v(254), v(255)
-V_LOFF = [v(240), v(241)]
-V_COL, V_HL, V_LANE = v(242), v(243), v(244)
+# register map: 256 per lane (VGPRs v0..v127, AGPRs a0..a127), two waves per
+# SIMD
+NW = 8                               # waves per workgroup
+S_BUF = [0, 32]                      # two score buffers of 32 VGPRs: tile j, tile j + 1
+P_BUF = 64                           # probabilities of one tile, bf16 pairs: 16 VGPRs
+V_TID, V_KLANE, V_VLANE, V_KADDR, V_VADDR = v(80), v(81), v(82), v(83), v(84)
+V_DK = [v(85 + i) for i in range(3)]  # LDS-DMA source offsets per lane (K chunks)
+V_DV = [v(88 + i) for i in range(3)]  # (V chunks)
+V_M = v(91)                          # running maximum (scaled, log2 units)
+V_MTHR = v(92)                       # running maximum + slack
+V_ALPHA = v(93)
+V_MOLD = v(94)                       # running maximum before this tile
+V_L = [v(95), v(96)]                 # running sum, two partials
+V_LT = [v(97), v(98)]                # this tile's row sums, two partials
+V_IBASE = v(99)                      # row - 4 * (lane / 32), for the per-cell mask
+V_LOFF, V_QOFF = v(100), v(101)
+V_COL, V_HL = v(102), v(103)
+V_T = [v(104 + i) for i in range(16)]  # even start: pairs of them are 64-bit tuples
+V_OWL, V_ORDL, V_OST, V_OW, V_ORD = v(120), v(121), v(122), v(123), v(124)
+V_LANE = v(125)
 
-A_O = [a(0, 64), a(64, 64)]          # O^T per row group: block db at 16 db
-A_Q = [a(128, 32), a(160, 32)]       # Q^T fragments per row group: ks at 4 ks
-A_KR = a(192, 32)                    # K fragment ring: slot at 4 slot
-A_VR = a(224, 32)                    # V fragment ring
+A_O = a(0, 64)                       # O^T: block db at 16 db
+A_Q = a(64, 32)                      # Q^T fragments: ks at 4 ks
+A_KR = a(96, 16)                     # K fragment ring: 4 slots
+A_VR = a(112, 16)                    # V^T fragment ring: 4 slots
+RING = 4
 
 # SGPRs
 S_KARG = s(0, 2)
@@ -450,16 +456,21 @@ S_WG = s(2)
 S_Q, S_K, S_V, S_OUT, S_LSE = s(4, 2), s(6, 2), s(8, 2), s(10, 2), s(12, 2)
 S_N, S_W, S_G, S_NHB, S_NRB, S_C = s(14), s(15), s(16), s(17), s(18), s(19)
 S_TOTAL, S_HKV, S_HQ = s(20), s(21), s(22)
+S_WH, S_WR, S_R0W = s(23), s(34), s(35)   # wave & 3 (head), wave >> 2 (row half), its first row
 S_WAVE, S_LID, S_HB, S_RB, S_BG, S_R0, S_TLO, S_T, S_J = (s(24), s(25), s(26), s(27), s(28), s(29),
                                                           s(30), s(31), s(32))
 S_RSK, S_RSV, S_RSQ, S_RSO, S_RSL = s(36, 4), s(40, 4), s(44, 4), s(48, 4), s(52, 4)
-S_WAVE1K, S_SOFF, S_SB, S_SBK, S_SBV, S_K0 = s(56), s(57), s(58), s(59), s(60), s(61)
+S_WAVE1K, S_SOFF, S_SB = s(56), s(57), s(58)
+S_R0W32 = s(59)                      # this wave's first row + 32
+S_K0P = [s(61), s(76)]               # key0 of the tile, by iteration phase
+S_FULL = [s(77), s(60)]              # 1 if every cell of the tile attends this wave's rows, by phase
 S_WM1, S_NINF, S_ONES = s(63), s(64), s(65)
 S_SBW = s(62)                        # DMA stage base + 1024 * wave
+S_WAVE1K3, S_SBW3 = s(72), s(73)     # 1024 * (wave & 3), stage base + that
 S_NB = s(33)                         # N * 256: bytes per head, first offset past the rows
 S_FLAG = s(68, 2)
-S_CMP = [s(70, 2), s(72, 2)]
-S_MV = [s(74, 2), s(76, 2)]
+S_CMP = s(70, 2)
+S_MV = s(74, 2)
 S_X = [s(78 + i) for i in range(14)]  # scalar temporaries s78..s91
 
 
@@ -476,6 +487,8 @@ OPT = {"fp32_sums": False}
 # optional register dumps (a development aid: off in the library build)
 DEBUG = {"on": False, "dumps": True, "n": 0, "tags": []}
 S_DBG = s(92, 4)
+S_DBGW, S_DBGG = s(66), s(67)   # total waves, this wave's global index (debug only)
+V_DBGL = v(126)                 # lane * 4 (debug only)
 
 
 def dump(P, tag, regs):
@@ -494,8 +507,6 @@ def dump(P, tag, regs):
             if src.f == "a":
                 P.add(I(f"  v_accvgpr_read_b32 {V_T[15]}, {src}", "valu", src.regs(), V_T[15].regs()))
                 src = V_T[15]
-            # offset = ((k*256 + r) * waves + gwave) * 256 + lane * 4; waves
-            # and gwave in S_X[0] / S_X[1] (set at kernel entry)
             P.salu("s_mul_i32", S_X[2], S_DBGW, str(k * 256 + r))
             P.salu("s_add_u32", S_X[2], S_X[2], S_DBGG)
             P.salu("s_lshl_b32", S_X[2], S_X[2], "8")
@@ -520,15 +531,11 @@ def dump_lds(P, tag, nbytes):
                 regs_of(V_T[14], V_DBGL, S_DBG, S_X[2]), EMPTY))
 
 
-S_DBGW, S_DBGG = s(66), s(67)   # total waves, this wave's global index (debug only)
-V_DBGL = v(221)                 # lane * 4 (debug only)
-
-
 # ---------------------------------------------------------------------------
 # building blocks
 def udiv(P, x, d, q, r, t0, t1):
     """q = x / d, r = x % d for wave-uniform 0 <= x < 2^24, 1 <= d < 2^24
-    (SGPRs); float estimate, then one correction each way."""
+    (SGPRs); float estimate, then corrections each way."""
     P.valu("v_cvt_f32_u32", t0, x)
     P.valu("v_cvt_f32_u32", t1, d)
     P.valu("v_rcp_f32", t1, t1, kind="trans")
@@ -565,73 +572,80 @@ def rsrc(P, dst, base, idx, bytes_per_idx_sgpr, num_sgpr):
 def dma_ops():
     """This wave's LDS-DMA loads of the tile whose key offset (bytes) is
     S_SOFF into the stage at LDS byte S_SB, as a list of emitters (each sets
-    M0 and issues one load; S_SBW = S_SB + 1024 * wave).  K chunks wave + 4 jk
-    (jk < 4) and chunk 16 (every wave writes the same bytes), V chunks
-    wave + 4 jv."""
+    M0 and issues one 1 KiB load).  K chunks wave, wave + 8 and 16 (every
+    wave writes the same bytes of chunk 16); V chunks wave, wave + 8 and
+    16 + (wave & 3)."""
     ops = []
-    for jk in range(5):
+    for jk in range(3):
         def op(P, jk=jk):
-            if jk < 4:
-                P.salu("s_add_u32", "m0", S_SBW, str(jk * 4096))
+            if jk < 2:
+                P.salu("s_add_u32", "m0", S_SBW, str(jk * 8192))
             else:
                 P.salu("s_add_u32", "m0", S_SB, str(16 * 1024))
             P.dma(V_DK[jk], S_RSK, S_SOFF)
         ops.append(op)
-    for jv in range(5):
+    for jv in range(3):
         def op(P, jv=jv):
-            P.salu("s_add_u32", "m0", S_SBW, str(KTILE + jv * 4096))
+            if jv < 2:
+                P.salu("s_add_u32", "m0", S_SBW, str(KTILE + jv * 8192))
+            else:
+                P.salu("s_add_u32", "m0", S_SBW3, str(KTILE + 16 * 1024))
             P.dma(V_DV[jv], S_RSV, S_SOFF)
         ops.append(op)
     return ops
 
 
-def dma_tile(P):
+def dma_bases(P):
     P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
+    P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
+
+
+def dma_tile(P):
+    dma_bases(P)
     for op in dma_ops():
         op(P)
 
 
-def qk_pair(P, qi, sbuf):
-    """MFMAs of K fragment qi (key half kb, channels 16 ks .. 16 ks + 15)
-    for both row groups: S^T[rg][kb] (+)= K Q^T."""
-    kb, ks = divmod(qi, 8)
-    slot = A_KR.sub(4 * (qi % 8), 4)
-    for rg in range(2):
-        dst = v(sbuf + 32 * rg + 16 * kb, 16)
-        P.mfma(dst, slot, A_Q[rg].sub(4 * ks, 4), None if ks == 0 else dst)
+# K fragments in issue order n = 0..15: key half kb = n % 2, channels
+# 16 ks .. 16 ks + 15 with ks = n / 2 (the two key halves' accumulation
+# chains alternate); V^T fragments n = 0..15: key step n / 4 (key half
+# kb, keys 16 hf .. 16 hf + 15 of it), values 32 db .. 32 db + 31 with
+# db = n % 4 (four O^T blocks in turn).  Ring slot n % 4.
+def qk_read(P, n):
+    kb, ks = n % 2, n // 2
+    P.ds_read("ds_read_b128", A_KR.sub(4 * (n % RING), 4), V_KADDR, kb * 32 * KROW + ks * 32)
 
 
-def qk_read(P, qi):
-    kb, ks = divmod(qi, 8)
-    P.ds_read("ds_read_b128", A_KR.sub(4 * (qi % 8), 4), V_KADDR, kb * 32 * KROW + ks * 32)
+def qk_mfma(P, n, sbuf):
+    """S^T[kb] (+)= K Q^T for K fragment n."""
+    kb, ks = n % 2, n // 2
+    dst = v(sbuf + 16 * kb, 16)
+    P.mfma(dst, A_KR.sub(4 * (n % RING), 4), A_Q.sub(4 * ks, 4), None if ks == 0 else dst)
 
 
-def pv_pair(P, pi, pbuf):
-    """MFMAs of V^T fragment pi (key half kb, keys 16 hf .. 16 hf + 15 of it,
-    values 32 db .. 32 db + 31) for both row groups: O^T += V^T P^T."""
-    kb, rest = divmod(pi, 8)
-    hf, db = divmod(rest, 4)
-    slot = A_VR.sub(4 * (pi % 8), 4)
-    for rg in range(2):
-        o = A_O[rg].sub(16 * db, 16)
-        P.mfma(o, slot, v(pbuf + 32 * rg + 16 * kb + 4 * hf, 4), o)
-
-
-def pv_read(P, pi):
-    kb, rest = divmod(pi, 8)
-    hf, db = divmod(rest, 4)
-    slot = A_VR.sub(4 * (pi % 8), 4)
+def pv_read(P, n):
+    kstep, db = divmod(n, 4)
+    kb, hf = divmod(kstep, 2)
+    slot = A_VR.sub(4 * (n % RING), 4)
     off = (kb * 32 + hf * 16) * VROW + db * 64
     P.ds_read("ds_read_b64_tr_b16", slot.sub(0, 2), V_VADDR, off)
     P.ds_read("ds_read_b64_tr_b16", slot.sub(2, 2), V_VADDR, off + 8 * VROW)
 
 
-def max_ops(sbuf, rg, track_flag):
+def pv_mfma(P, n):
+    """O^T[db] += V^T P^T for V^T fragment n."""
+    kstep, db = divmod(n, 4)
+    kb, hf = divmod(kstep, 2)
+    o = A_O.sub(16 * db, 16)
+    P.mfma(o, A_VR.sub(4 * (n % RING), 4), v(P_BUF + 8 * kb + 4 * hf, 4), o)
+
+
+def max_ops(sbuf):
     """Row maximum of the tile's 32 scores per lane (both key halves), the
-    lazy update of the running maximum, alpha and the rescaled sums.  Returns
-    a list of emit callbacks (one instruction each)."""
-    sv = [v(sbuf + 32 * rg + k) for k in range(32)]
-    t, t1, t2, t3 = V_T[8 + 4 * rg], V_T[9 + 4 * rg], V_T[10 + 4 * rg], V_T[11 + 4 * rg]
+    lazy update of the running maximum and the flag of a moved maximum.
+    Returns a list of emit callbacks (one instruction each)."""
+    sv = [v(sbuf + k) for k in range(32)]
+    t, t1, t2, t3 = V_T[8], V_T[9], V_T[10], V_T[11]
     acc = [t, t1, t2, t3]
     ops = []
     # four independent chains over 8 scores each (short dependency chains),
@@ -652,35 +666,34 @@ def max_ops(sbuf, rg, track_flag):
     ops.append(lambda P: P.add(I(f"  v_permlane32_swap_b32 {t}, {t1}", "perm", regs_of(t, t1), regs_of(t, t1))))
     ops.append(lambda P: P.valu("v_max_f32", t, t, t1))
     ops.append(lambda P: P.valu("v_mul_f32", t, S_C, t))                     # tile max, scaled
-    ops.append(lambda P: P.add(I(f"  v_cmp_gt_f32 {S_CMP[rg]}, {t}, {V_MTHR[rg]}", "vcmp",
-                                 regs_of(t, V_MTHR[rg]), S_CMP[rg].regs())))
-    ops.append(lambda P: P.valu("v_max_f32", t2, V_M[rg], t))                # candidate maximum
+    ops.append(lambda P: P.add(I(f"  v_cmp_gt_f32 {S_CMP}, {t}, {V_MTHR}", "vcmp",
+                                 regs_of(t, V_MTHR), S_CMP.regs())))
+    ops.append(lambda P: P.valu("v_max_f32", t2, V_M, t))                    # candidate maximum
+
     # (compare and select in one op: merged op lists must not split an SCC
     # producer from its consumer)
     def moved(P):
-        P.scmp("s_cmp_lg_u64", S_CMP[rg], "0")
-        P.salu("s_cselect_b64", S_MV[rg], "-1", "0", reads_scc=True, writes_scc=False)
+        P.scmp("s_cmp_lg_u64", S_CMP, "0")
+        P.salu("s_cselect_b64", S_MV, "-1", "0", reads_scc=True, writes_scc=False)
     ops.append(moved)
-    ops.append(lambda P: P.valu("v_mov_b32", V_MOLD[rg], V_M[rg]))
-    ops.append(lambda P: P.valu("v_cndmask_b32", V_M[rg], V_M[rg], t2, S_MV[rg]))  # moved (any lane) ? new : old
-    ops.append(lambda P: P.salu("s_or_b64", S_FLAG, S_FLAG, S_MV[rg]))
+    ops.append(lambda P: P.valu("v_mov_b32", V_MOLD, V_M))
+    ops.append(lambda P: P.valu("v_cndmask_b32", V_M, V_M, t2, S_MV))       # moved (any lane) ? new : old
+    ops.append(lambda P: P.salu("s_or_b64", S_FLAG, S_FLAG, S_MV))
     return ops
 
 
-def exp_ops(sbuf, rg, kb):
-    """p = exp2(s * c - m) for 16 scores, packed in place to bf16 pairs (the
-    B operand of the P V product), row sums of the packed values."""
-    base = sbuf + 32 * rg + 16 * kb
-    sv = [v(base + k) for k in range(16)]
+def exp_ops(sbuf, kb):
+    """p = exp2(s * c - m) for the 16 scores of key half kb, in place."""
+    sv = [v(sbuf + 16 * kb + k) for k in range(16)]
     ops = []
     for k in range(16):
-        ops.append(lambda P, k=k: P.valu("v_fma_f32", sv[k], sv[k], S_C, NegR(V_M[rg])))
+        ops.append(lambda P, k=k: P.valu("v_fma_f32", sv[k], sv[k], S_C, NegR(V_M)))
     for k in range(16):
         op = (lambda P, k=k: P.valu("v_exp_f32", sv[k], sv[k], kind="trans"))
         op.cost = 2.0
         ops.append(op)
-    lt = V_LT[rg]
     if OPT["fp32_sums"]:
+        lt = V_LT
         if kb == 0:
             ops.append(lambda P: P.valu("v_add_f32", lt[0], sv[0], sv[2]))
             ops.append(lambda P: P.valu("v_add_f32", lt[1], sv[1], sv[3]))
@@ -689,15 +702,29 @@ def exp_ops(sbuf, rg, kb):
             first = 0
         for k in range(first, 16):
             ops.append(lambda P, k=k: P.valu("v_add_f32", lt[k % 2], lt[k % 2], sv[k]))
+    return ops
+
+
+def pack_ops(sbuf, kb):
+    """The probabilities of key half kb packed to bf16 pairs into the P
+    buffer (the B operand of the P V product), and the row sums of the
+    packed values."""
+    sv = [v(sbuf + 16 * kb + k) for k in range(16)]
+    pv = [v(P_BUF + 8 * kb + i) for i in range(8)]
+    lt = V_LT
+    ops = []
+    # (the P buffer's key half kb is read by the V fragments 8 kb .. 8 kb + 7
+    # of the current P V product)
     for i in range(8):
-        ops.append(lambda P, i=i: P.valu("v_cvt_pk_bf16_f32", sv[i], sv[2 * i], sv[2 * i + 1]))
+        ops.append(after(lambda P, i=i: P.valu("v_cvt_pk_bf16_f32", pv[i], sv[2 * i], sv[2 * i + 1]),
+                         "v", 8 * kb + 7))
     if not OPT["fp32_sums"]:
         for i in range(8):
-            a = i % 2            # (the key half kb = 0 initializes both partials)
+            a_ = i % 2            # (key half 0 initializes both partials)
             if kb == 0 and i < 2:
-                ops.append(lambda P, i=i, a=a: P.valu("v_dot2_f32_bf16", lt[a], sv[i], S_ONES, "0"))
+                ops.append(lambda P, i=i, a_=a_: P.valu("v_dot2_f32_bf16", lt[a_], pv[i], S_ONES, "0"))
             else:
-                ops.append(lambda P, i=i, a=a: P.valu("v_dot2_f32_bf16", lt[a], sv[i], S_ONES, lt[a]))
+                ops.append(lambda P, i=i, a_=a_: P.valu("v_dot2_f32_bf16", lt[a_], pv[i], S_ONES, lt[a_]))
     return ops
 
 
@@ -711,30 +738,29 @@ def merge_rr(lists):
     return out
 
 
-def mask_block(P, sbuf):
-    """Per-cell window mask of tile j (key offset S_K0) on score buffer sbuf:
+def mask_block(P, sbuf, k0):
+    """Per-cell window mask of tile j (key offset in k0) on score buffer sbuf:
     key j attends row i iff 0 <= i - j <= W - 1.  One 32-bit word per lane
     and key half (bit kc set iff the lane's key kc attends), then one
     bit-field select per score."""
     tb, tlo, thi, tm1, tm2, tk = V_T[0], V_T[1], V_T[2], V_T[3], V_T[4], V_T[5]
-    for rg in range(2):
-        for kb in range(2):
-            P.salu("s_add_u32", S_X[3], S_K0, str(32 * kb))
-            P.valu("v_subrev_u32", tb, S_X[3], V_IBASE[rg])                  # base = i - 4 hl - key0
-            P.valu("v_subrev_u32", tlo, S_WM1, tb)                            # base - (W - 1)
-            P.valu("v_max_i32", tlo, "0", tlo)
-            P.valu("v_min_i32", thi, "31", tb)
-            P.valu("v_lshlrev_b32_e64", tm1, thi, "2")
-            P.valu("v_add_u32", tm1, "-1", tm1)                                # (2 << hi) - 1
-            P.valu("v_lshlrev_b32_e64", tm2, tlo, "-1")                        # ~0 << lo
-            P.valu("v_and_b32", tm1, tm1, tm2)
-            P.add(I(f"  v_cmp_le_i32 vcc, {tlo}, {thi}", "vcmp", regs_of(tlo, thi), VCC))
-            P.valu("v_cndmask_b32", tm1, "0", tm1, "vcc")
-            for r in range(16):
-                kc = (r % 4) + 8 * (r // 4)
-                sr = v(sbuf + 32 * rg + 16 * kb + r)
-                P.valu("v_bfe_i32", tk, tm1, str(kc), "1")
-                P.valu("v_bitop3_b32", sr, sr, S_NINF, tk, extra="bitop3:0xe4")
+    for kb in range(2):
+        P.salu("s_add_u32", S_X[3], k0, str(32 * kb))
+        P.valu("v_subrev_u32", tb, S_X[3], V_IBASE)                      # base = i - 4 hl - key0
+        P.valu("v_subrev_u32", tlo, S_WM1, tb)                            # base - (W - 1)
+        P.valu("v_max_i32", tlo, "0", tlo)
+        P.valu("v_min_i32", thi, "31", tb)
+        P.valu("v_lshlrev_b32_e64", tm1, thi, "2")
+        P.valu("v_add_u32", tm1, "-1", tm1)                                # (2 << hi) - 1
+        P.valu("v_lshlrev_b32_e64", tm2, tlo, "-1")                        # ~0 << lo
+        P.valu("v_and_b32", tm1, tm1, tm2)
+        P.add(I(f"  v_cmp_le_i32 vcc, {tlo}, {thi}", "vcmp", regs_of(tlo, thi), VCC))
+        P.valu("v_cndmask_b32", tm1, "0", tm1, "vcc")
+        for r in range(16):
+            kc = (r % 4) + 8 * (r // 4)
+            sr = v(sbuf + 16 * kb + r)
+            P.valu("v_bfe_i32", tk, tm1, str(kc), "1")
+            P.valu("v_bitop3_b32", sr, sr, S_NINF, tk, extra="bitop3:0xe4")
 
 
 def rescale_block(P, with_o=True):
@@ -743,91 +769,104 @@ def rescale_block(P, with_o=True):
     has been accumulated) O are rescaled, after every product of the old
     maximum."""
     tmp = V_T
-    for rg in range(2):
-        P.valu("v_sub_f32", tmp[0], V_MOLD[rg], V_M[rg])
-        P.valu("v_exp_f32", V_ALPHA[rg], tmp[0], kind="trans")
-        P.valu("v_add_f32", V_MTHR[rg], str(SLACK), V_M[rg])
-        P.valu("v_mul_f32", V_L[rg][0], V_L[rg][0], V_ALPHA[rg])
+    P.valu("v_sub_f32", tmp[0], V_MOLD, V_M)
+    P.valu("v_exp_f32", V_ALPHA, tmp[0], kind="trans")
+    P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
+    P.valu("v_mul_f32", V_L[0], V_L[0], V_ALPHA)
+    P.valu("v_mul_f32", V_L[1], V_L[1], V_ALPHA)
     if not with_o:
         return
-    for rg in range(2):
-        for k0 in range(0, 64, 8):
-            for k in range(8):
-                P.add(I(f"  v_accvgpr_read_b32 {tmp[k]}, {A_O[rg].sub(k0 + k)}", "valu",
-                        A_O[rg].sub(k0 + k).regs(), tmp[k].regs()))
-            for k in range(8):
-                P.valu("v_mul_f32", tmp[k], tmp[k], V_ALPHA[rg])
-            for k in range(8):
-                P.add(I(f"  v_accvgpr_write_b32 {A_O[rg].sub(k0 + k)}, {tmp[k]}", "valu",
-                        tmp[k].regs(), A_O[rg].sub(k0 + k).regs()))
+    for k0 in range(0, 64, 8):
+        for k in range(8):
+            P.add(I(f"  v_accvgpr_read_b32 {tmp[k]}, {A_O.sub(k0 + k)}", "valu",
+                    A_O.sub(k0 + k).regs(), tmp[k].regs()))
+        for k in range(8):
+            P.valu("v_mul_f32", tmp[k], tmp[k], V_ALPHA)
+        for k in range(8):
+            P.add(I(f"  v_accvgpr_write_b32 {A_O.sub(k0 + k)}, {tmp[k]}", "valu",
+                    tmp[k].regs(), A_O.sub(k0 + k).regs()))
 
 
 # ---------------------------------------------------------------------------
-PREFETCH = 6   # MFMA pairs whose fragments are read ahead
+AHEAD = RING - 1   # fragments of each kind read ahead of their MFMA
 
 
-def interleave(P, pairs, valu_ops, extra_ops=()):
-    """pairs: list of (read_fn, mfma_fn) in order; valu_ops, extra_ops: lists
-    of emitters.  Reads run PREFETCH pairs ahead; VALU work is spread evenly
-    between the MFMAs, the extra ops (LDS-DMA loads) one every few MFMAs."""
-    n_mfma = 2 * len(pairs)
-    for k in range(min(PREFETCH, len(pairs))):
-        pairs[k][0](P)
-    extra = list(extra_ops)
-    every = max(1, (n_mfma - 8) // max(1, len(extra))) if extra else 0
-    # issue cost of each op (transcendentals take two VALU slots)
+def after(op, kind, n):
+    """Mark op to run only after the MFMA of fragment (kind, n) is issued."""
+    op.after = (kind, n)
+    return op
+
+
+def interleave(P, order, sbuf_next, valu_ops, extra_ops=(), v_ready=0):
+    """order: the MFMAs as ("k", n) (QK fragment n into sbuf_next) or ("v",
+    n) (PV fragment n).  Fragment reads of each kind run AHEAD fragments
+    ahead of their MFMA (the first v_ready V fragments are already read).
+    valu_ops keep their order and are spread evenly (by issue cost) over
+    all the MFMAs; an op marked with after() waits for that MFMA (when it
+    is part of this order).  extra_ops (the LDS-DMA loads and the scalar
+    set-up of the next step) go one every few MFMAs."""
+    nk = sum(1 for x in order if x[0] == "k")
+    nv = len(order) - nk
+    rd = {"k": lambda n: qk_read(P, n), "v": lambda n: pv_read(P, n)}
+    cnt = {"k": nk, "v": nv}
+    issued = {"k": 0, "v": v_ready if nv else 0}
+
+    def read_upto(kind, last):
+        while issued[kind] <= min(last, cnt[kind] - 1):
+            rd[kind](issued[kind])
+            issued[kind] += 1
+    for kind in ("v", "k"):
+        read_upto(kind, AHEAD - 1)
+    index = {x: i for i, x in enumerate(order)}
     costs = [getattr(op, "cost", 1.0) for op in valu_ops]
     total = sum(costs)
-    vi = 0
-    done = 0
-    spent = 0.0
-    for p_idx, (rd, mf) in enumerate(pairs):
-        for half in range(2):
-            mf(P, half)
-            done += 1
-            if extra and done % every == 0:
-                extra.pop(0)(P)
-            target = total * done / n_mfma
-            while vi < len(valu_ops) and spent + 0.5 * costs[vi] <= target:
-                valu_ops[vi](P)
-                spent += costs[vi]
-                vi += 1
-            if half == 0 and p_idx + PREFETCH < len(pairs):
-                pairs[p_idx + PREFETCH][0](P)
-    while vi < len(valu_ops):
-        valu_ops[vi](P)
-        vi += 1
+    placed = {}
+    vi, spent = 0, 0.0
+    for m in range(len(order)):
+        target = total * (m + 1) / len(order)
+        while vi < len(valu_ops) and spent + 0.5 * costs[vi] <= target:
+            need = index.get(getattr(valu_ops[vi], "after", None), -1)
+            if need > m:
+                break
+            placed.setdefault(m, []).append(valu_ops[vi])
+            spent += costs[vi]
+            vi += 1
+    tail = valu_ops[vi:]
+    extra = list(extra_ops)
+    every = max(1, (len(order) - 4) // max(1, len(extra))) if extra else 0
+    for m, (kind, n) in enumerate(order):
+        read_upto(kind, n)
+        if kind == "k":
+            qk_mfma(P, n, sbuf_next)
+        else:
+            pv_mfma(P, n)
+        read_upto(kind, n + AHEAD)
+        if extra and (m + 1) % every == 0:
+            extra.pop(0)(P)
+        for op in placed.get(m, []):
+            op(P)
+    for op in tail:
+        op(P)
     while extra:
         extra.pop(0)(P)
 
 
-def make_pairs(has_qk, has_pv, sbuf_next, pbuf):
-    qk = [((lambda P, qi=qi: qk_read(P, qi)),
-           (lambda P, half, qi=qi: qk_pair_half(P, qi, sbuf_next, half))) for qi in range(16)]
-    pv = [((lambda P, pi=pi: pv_read(P, pi)),
-           (lambda P, half, pi=pi: pv_pair_half(P, pi, pbuf, half))) for pi in range(16)]
+def mfma_order(has_qk, has_pv):
     if has_qk and has_pv:
-        out = []
-        for k in range(16):
-            out.append(pv[k])
-            out.append(qk[k])
-        return out
-    return qk if has_qk else (pv if has_pv else [])
-
-
-def qk_pair_half(P, qi, sbuf, rg):
-    kb, ks = divmod(qi, 8)
-    slot = A_KR.sub(4 * (qi % 8), 4)
-    dst = v(sbuf + 32 * rg + 16 * kb, 16)
-    P.mfma(dst, slot, A_Q[rg].sub(4 * ks, 4), None if ks == 0 else dst)
-
-
-def pv_pair_half(P, pi, pbuf, rg):
-    kb, rest = divmod(pi, 8)
-    hf, db = divmod(rest, 4)
-    slot = A_VR.sub(4 * (pi % 8), 4)
-    o = A_O[rg].sub(16 * db, 16)
-    P.mfma(o, slot, v(pbuf + 32 * rg + 16 * kb + 4 * hf, 4), o)
+        # four P V products first (their first fragments were read before
+        # the barrier; the K fragments of the new tile are read after it),
+        # then two P V products per QK product until the P V products are
+        # done: the VALU work that must follow them (the packing of P) then
+        # has the last ten QK products to hide behind
+        out = [("v", 0), ("v", 1), ("v", 2), ("v", 3)]
+        for k in range(6):
+            out += [("k", k), ("v", 4 + 2 * k), ("v", 5 + 2 * k)]
+        return out + [("k", k) for k in range(6, 16)]
+    if has_qk:
+        return [("k", k) for k in range(16)]
+    if has_pv:
+        return [("v", k) for k in range(16)]
+    return []
 
 
 def stage_base(P, dst, jsgpr, add):
@@ -837,64 +876,97 @@ def stage_base(P, dst, jsgpr, add):
     P.salu("s_mul_i32", dst, dst, str(STAGE))
 
 
+def setup_ops(pn):
+    """Scalar set-up of iteration i = j + 1 (S_J = j), as emitters: the DMA
+    of tile i + 2 (offset, stage, M0 bases), key0 of tile i and whether
+    every cell of tile i attends this wave's rows.  Runs after this
+    iteration's DMA loads (it overwrites their offset and bases)."""
+    def o1(P):
+        P.salu("s_add_u32", S_X[9], S_J, "1")                  # i
+        P.salu("s_add_u32", S_X[4], S_X[9], "2")               # tile i + 2
+        P.salu("s_add_u32", S_X[5], S_TLO, S_X[4])
+        P.salu("s_lshl_b32", S_X[5], S_X[5], "14")
+
+    # past the band (i + 2 >= T) the offset is N rows, out of the
+    # descriptor's range: the loads read zeros without touching memory,
+    # into a stage nothing reads
+    def o2(P):
+        P.scmp("s_cmp_lt_u32", S_X[4], S_T)
+        P.salu("s_cselect_b32", S_SOFF, S_X[5], S_NB, reads_scc=True, writes_scc=False)
+
+    def o3(P):
+        P.salu("s_and_b32", S_SB, S_X[4], "3")
+        P.salu("s_mul_i32", S_SB, S_SB, str(STAGE))
+        P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
+        P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
+
+    def o4(P):
+        P.salu("s_add_u32", S_X[6], S_TLO, S_X[9])
+        P.salu("s_lshl_b32", S_K0P[pn], S_X[6], "6")           # key0 of tile i
+        P.salu("s_add_u32", S_X[7], S_K0P[pn], "63")
+        P.salu("s_add_u32", S_X[8], S_K0P[pn], S_W)
+
+    def o5(P):
+        P.scmp("s_cmp_le_u32", S_X[7], S_R0W)                  # last key <= first row
+        P.salu("s_cselect_b32", S_X[10], "1", "0", reads_scc=True, writes_scc=False)
+
+    def o6(P):
+        P.scmp("s_cmp_ge_u32", S_X[8], S_R0W32)                # key0 + W >= last row + 1
+        P.salu("s_cselect_b32", S_X[11], "1", "0", reads_scc=True, writes_scc=False)
+        P.salu("s_and_b32", S_FULL[pn], S_X[10], S_X[11])
+    return [o1, o2, o3, o4, o5, o6]
+
+
+def v_prefetch_ops():
+    """The first AHEAD V^T fragments of the next P V product (tile j, in
+    stage j & 3, visible since an earlier barrier), read before the next
+    barrier."""
+    def addr(P):
+        P.salu("s_and_b32", S_X[12], S_J, "3")
+        P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
+        P.valu("v_add_u32", V_VADDR, S_X[12], V_VLANE)
+    # (after the last V read of this step, which uses the same address
+    # register, and after the MFMAs that read the ring slots it refills)
+    return [after(op, "v", 15) for op in [addr] + [(lambda P, n=n: pv_read(P, n)) for n in range(AHEAD)]]
+
+
+def k_addr_next(P):
+    """LDS address of the K fragments of the next QK product (tile j + 2)."""
+    P.salu("s_add_u32", S_X[12], S_J, "2")
+    P.salu("s_and_b32", S_X[12], S_X[12], "3")
+    P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+
+
 def iteration(P, phase, has_qk, has_pv, first):
-    """One tile j (S_J) of the pipeline; buffers by phase = j % 3."""
-    sb_cur, sb_next, sb_prev = S_BUF[phase], S_BUF[(phase + 1) % 3], S_BUF[(phase + 2) % 3]
+    """One tile j (S_J) of the pipeline; score buffers by phase = j % 2."""
+    sb_cur, sb_next = S_BUF[phase], S_BUF[1 - phase]
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
     P.waitcnt(vm=0)
     P.barrier()
     if has_pv:
         settle_previous(P)
-    # DMA of tile j + 2 into stage (j + 2) & 3; past the band (j + 2 >= T)
-    # the offset is N rows, out of the descriptor's range: the loads read
-    # zeros without touching memory, into a stage nothing reads
-    if has_qk:
-        P.salu("s_add_u32", S_X[4], S_J, "2")
-        P.salu("s_add_u32", S_X[5], S_TLO, S_X[4])
-        P.salu("s_lshl_b32", S_X[5], S_X[5], "14")
-        P.scmp("s_cmp_lt_u32", S_X[4], S_T)
-        P.salu("s_cselect_b32", S_SOFF, S_X[5], S_NB, reads_scc=True, writes_scc=False)
-        stage_base(P, S_SB, S_J, 2)
-        P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
-    if has_qk:
-        stage_base(P, S_SBK, S_J, 1)
-        P.valu("v_add_u32", V_KADDR, S_SBK, V_KLANE)
-    if has_pv:
-        stage_base(P, S_SBV, S_J, -1 + 4)
-        P.valu("v_add_u32", V_VADDR, S_SBV, V_VLANE)
-    # per-cell mask of tile j unless every cell attends
-    P.salu("s_add_u32", S_X[6], S_TLO, S_J)
-    P.salu("s_lshl_b32", S_K0, S_X[6], "6")                 # key0 of tile j
-    P.salu("s_add_u32", S_X[7], S_K0, "63")
-    P.salu("s_add_u32", S_X[8], S_K0, S_W)                  # key0 + W >= r0 + 64 ?
-    P.salu("s_add_u32", S_X[9], S_R0, "64")
-    P.scmp("s_cmp_le_u32", S_X[7], S_R0)
-    P.salu("s_cselect_b32", S_X[10], "1", "0", reads_scc=True, writes_scc=False)
-    P.scmp("s_cmp_ge_u32", S_X[8], S_X[9])
-    P.salu("s_cselect_b32", S_X[11], "1", "0", reads_scc=True, writes_scc=False)
-    P.salu("s_and_b32", S_X[10], S_X[10], S_X[11])
-    P.scmp("s_cmp_eq_u32", S_X[10], "1")
+    # per-cell mask of tile j unless every cell of this wave's 32 rows attends
+    P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
     skip = P.new_label("full")
     P.branch("s_cbranch_scc1", skip)
-    mask_block(P, sb_cur)
+    mask_block(P, sb_cur, S_K0P[phase])
     P.label(skip)
-    dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 64)])
+    dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32)])
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
-    valu = merge_rr([max_ops(sb_cur, 0, has_pv), max_ops(sb_cur, 1, has_pv)])
-    # (blocks in the order (rg, kb) = (0,0), (1,0), (0,1), (1,1): a key half
-    # 1 op accumulates into the partial its key half 0 op initialized two
-    # ops earlier)
-    valu += merge_rr([exp_ops(sb_cur, rg, kb) for kb in range(2) for rg in range(2)])
-    pairs = make_pairs(has_qk, has_pv, sb_next, sb_prev)
-    interleave(P, pairs, valu, dma_ops() if has_qk else [])
-    dump(P, f"soft{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 64), V_M[0], V_M[1], V_L[0][0], V_L[0][1],
-                                                        V_L[1][0], V_L[1][1], V_ALPHA[0], V_ALPHA[1]])
+    valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
+            + v_prefetch_ops() + pack_ops(sb_cur, 1))
+    extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
+    interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
+    if has_qk:
+        k_addr_next(P)
+    dump(P, f"soft{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32), v(P_BUF, 16), V_M, V_L[0], V_L[1],
+                                                        V_LT[0], V_LT[1]])
     if not has_pv:
         # first tile: nothing accumulated yet (O = 0, l = 0), so the moved
         # maximum only moves the threshold; this tile's sums are merged at
         # the start of the next step
-        for rg in range(2):
-            P.valu("v_add_f32", V_MTHR[rg], str(SLACK), V_M[rg])
+        P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
 
 
@@ -907,80 +979,70 @@ def settle_previous(P):
     P.branch("s_cbranch_scc1", skip)
     rescale_block(P, with_o=True)
     P.label(skip)
-    for rg in range(2):
-        P.valu("v_add_f32", V_L[rg][0], V_L[rg][0], V_LT[rg][0])
-        P.valu("v_add_f32", V_L[rg][0], V_L[rg][0], V_LT[rg][1])
+    P.valu("v_add_f32", V_L[0], V_L[0], V_LT[0])
+    P.valu("v_add_f32", V_L[1], V_L[1], V_LT[1])
 
 
 def epilogue(P, phase):
     """O += V(T-1)^T P(T-1), then O / l -> bf16 rows, and the log-sum-exp."""
-    pbuf = S_BUF[phase]
     P.waitcnt(vm=0)
     P.barrier()
     settle_previous(P)
-    stage_base(P, S_SBV, S_J, 0)
-    P.valu("v_add_u32", V_VADDR, S_SBV, V_VLANE)
-    pairs = make_pairs(False, True, None, pbuf)
-    interleave(P, pairs, [])
-    dump(P, f"O{phase}", [A_O[0], A_O[1]])
+    interleave(P, mfma_order(False, True), None, [], v_ready=AHEAD)
+    dump(P, f"O{phase}", [A_O])
     t = V_T
-    for rg in range(2):
-        l, l2, inv = t[0], t[1], t[2 + rg]
-        P.valu("v_add_f32", l, V_L[rg][0], V_L[rg][1])
-        P.valu("v_mov_b32", l2, l)
-        P.add(I(f"  v_permlane32_swap_b32 {l}, {l2}", "perm", regs_of(l, l2), regs_of(l, l2)))
-        P.valu("v_add_f32", l, l, l2)                       # the row's sum over both lane halves
-        P.valu("v_rcp_f32", inv, l, kind="trans")
-        # log-sum-exp, natural log: (m + log2 l) * ln 2
-        skip = P.new_label("nolse")
-        P.scmp("s_cmp_eq_u64", S_LSE, "0")
-        P.branch("s_cbranch_scc1", skip)
-        P.valu("v_log_f32", l2, l, kind="trans")
-        P.valu("v_add_f32", l2, V_M[rg], l2)
-        P.valu("v_mul_f32", l2, "0x3f317218", l2)
-        P.buf_store("buffer_store_dword", l2, V_LOFF[rg], S_RSL)
-        P.label(skip)
+    l, l2, inv = t[0], t[1], t[2]
+    P.valu("v_add_f32", l, V_L[0], V_L[1])
+    P.valu("v_mov_b32", l2, l)
+    P.add(I(f"  v_permlane32_swap_b32 {l}, {l2}", "perm", regs_of(l, l2), regs_of(l, l2)))
+    P.valu("v_add_f32", l, l, l2)                       # the row's sum over both lane halves
+    P.valu("v_rcp_f32", inv, l, kind="trans")
+    # log-sum-exp, natural log: (m + log2 l) * ln 2
+    skip = P.new_label("nolse")
+    P.scmp("s_cmp_eq_u64", S_LSE, "0")
+    P.branch("s_cbranch_scc1", skip)
+    P.valu("v_log_f32", l2, l, kind="trans")
+    P.valu("v_add_f32", l2, V_M, l2)
+    P.valu("v_mul_f32", l2, "0x3f317218", l2)
+    P.buf_store("buffer_store_dword", l2, V_LOFF, S_RSL)
+    P.label(skip)
     # O / l -> bf16, staged through LDS so the global stores are whole rows
     # (16 lanes x 16 bytes per 256-byte row) instead of 8-byte pieces of 32
-    # rows.  Each wave uses its own 64 x 272-byte region in the two stages
+    # rows.  Each wave uses its own 32 x 272-byte region in the two stages
     # that do not hold the last V tile (the only one other waves may still
     # read): stages 0-1 if that tile is in stage 2 or 3, else stages 2-3.
     P.salu("s_and_b32", S_X[0], S_J, "3")
     P.scmp("s_cmp_ge_u32", S_X[0], "2")
     P.salu("s_cselect_b32", S_X[1], "0", str(2 * STAGE), reads_scc=True, writes_scc=False)
-    P.salu("s_mul_i32", S_X[2], S_WAVE, str(64 * KROW))
+    P.salu("s_mul_i32", S_X[2], S_WAVE, str(32 * KROW))
     P.salu("s_add_u32", S_X[1], S_X[1], S_X[2])                    # this wave's region
     P.valu("v_add_u32", V_OW, S_X[1], V_OWL)
     P.valu("v_add_u32", V_ORD, S_X[1], V_ORDL)
-    for rg in range(2):
-        inv = t[2 + rg]
-        for db in range(4):
-            for r4 in range(4):
-                x = [t[4 + k] for k in range(4)]
-                for k in range(4):
-                    P.add(I(f"  v_accvgpr_read_b32 {x[k]}, {A_O[rg].sub(16 * db + 4 * r4 + k)}", "valu",
-                            A_O[rg].sub(16 * db + 4 * r4 + k).regs(), x[k].regs()))
-                for k in range(4):
-                    P.valu("v_mul_f32", x[k], x[k], inv)
-                pk0, pk1 = t[8 + 2 * (r4 % 2)], t[9 + 2 * (r4 % 2)]
-                P.valu("v_cvt_pk_bf16_f32", pk0, x[0], x[1])
-                P.valu("v_cvt_pk_bf16_f32", pk1, x[2], x[3])
-                # row 32 rg + col, values 32 db + 8 r4 + 4 hl .. +3
-                P.add(I(f"  ds_write_b64 {V_OW}, {v(pk0.i, 2)} offset:{rg * 32 * KROW + db * 64 + r4 * 16}", "lds",
-                        regs_of(V_OW, v(pk0.i, 2)), EMPTY))
-    ob = S_BUF[(phase + 1) % 3]                                     # free score buffer
+    for db in range(4):
+        for r4 in range(4):
+            x = [t[4 + k] for k in range(4)]
+            for k in range(4):
+                P.add(I(f"  v_accvgpr_read_b32 {x[k]}, {A_O.sub(16 * db + 4 * r4 + k)}", "valu",
+                        A_O.sub(16 * db + 4 * r4 + k).regs(), x[k].regs()))
+            for k in range(4):
+                P.valu("v_mul_f32", x[k], x[k], inv)
+            pk0, pk1 = t[8 + 2 * (r4 % 2)], t[9 + 2 * (r4 % 2)]
+            P.valu("v_cvt_pk_bf16_f32", pk0, x[0], x[1])
+            P.valu("v_cvt_pk_bf16_f32", pk1, x[2], x[3])
+            # row col, values 32 db + 8 r4 + 4 hl .. +3
+            P.add(I(f"  ds_write_b64 {V_OW}, {v(pk0.i, 2)} offset:{db * 64 + r4 * 16}", "lds",
+                    regs_of(V_OW, v(pk0.i, 2)), EMPTY))
+    ob = S_BUF[0]                                                   # free score buffer
 
     def rd(kk):
         # rows 4 kk + lane / 16, bytes 16 (lane % 16) .. +15 of each
         P.ds_read("ds_read_b128", v(ob + 4 * kk, 4), V_ORD, kk * 4 * KROW)
     for kk in range(8):
         rd(kk)
-    for kk in range(16):
+    for kk in range(8):
         P.salu("s_mov_b32", S_X[3 + (kk % 4)], str(kk * 1024), writes_scc=False)
         P.add(I(f"  buffer_store_dwordx4 {v(ob + 4 * kk, 4)}, {V_OST}, {S_RSO}, {S_X[3 + (kk % 4)]} offen",
                 "vstore", regs_of(v(ob + 4 * kk, 4), V_OST, S_RSO, S_X[3 + (kk % 4)]), EMPTY))
-        if kk + 8 < 16:
-            rd(kk + 8)
     P.add(I("  s_endpgm", "branch"))
 
 
@@ -997,11 +1059,13 @@ def prologue(P):
         P.smem("s_load_dwordx2", s(92, 2), S_KARG, "0x50")
         P.smem("s_load_dword", s(94), S_KARG, "0x58")
     P.waitcnt(lgkm=0)
+    P.salu("s_and_b32", S_WH, S_WAVE, "3")
+    P.salu("s_lshr_b32", S_WR, S_WAVE, "2")
     if DEBUG["on"]:
         P.salu("s_and_b32", S_DBG.sub(1), S_DBG.sub(1), "0xffff")
         P.salu("s_mov_b32", S_DBG.sub(3), "0x00020000", writes_scc=False)
-        P.salu("s_lshl_b32", S_DBGW, S_TOTAL, "2")
-        P.salu("s_lshl_b32", S_DBGG, S_WG, "2")
+        P.salu("s_lshl_b32", S_DBGW, S_TOTAL, "3")
+        P.salu("s_lshl_b32", S_DBGG, S_WG, "3")
         P.salu("s_add_u32", S_DBGG, S_DBGG, S_WAVE)
         P.valu("v_lshlrev_b32", V_DBGL, "2", V_LANE)
     # workgroup -> logical id: consecutive ids go to the 8 XCDs in turn; each
@@ -1017,14 +1081,16 @@ def prologue(P):
     # lid -> (head block, row block, batch * kv head).  Row blocks in
     # ascending order: the first blocks of a head have short bands, so the
     # first workgroups on the CUs end at different times and the later ones'
-    # loads and stores do not all hit memory at once (measured 5% faster
-    # than longest first)
+    # loads and stores do not all hit memory at once
     udiv(P, S_LID, S_NHB, S_X[4], S_HB, V_T[1], V_T[2])        # S_X[4] = rest
     udiv(P, S_X[4], S_NRB, S_BG, S_RB, V_T[1], V_T[2])         # row block
     P.salu("s_lshl_b32", S_R0, S_RB, "6")
     done = ".Ldone"
     P.scmp("s_cmp_ge_u32", S_R0, S_N)
     P.branch("s_cbranch_scc1", done)
+    P.salu("s_lshl_b32", S_R0W, S_WR, "5")
+    P.salu("s_add_u32", S_R0W, S_R0W, S_R0)                    # this wave's first row
+    P.salu("s_add_u32", S_R0W32, S_R0W, "32")
     # band of rows r0 .. r0+63: key tiles t_lo .. t_hi
     P.salu("s_sub_i32", S_X[0], S_R0, S_W)
     P.salu("s_add_i32", S_X[0], S_X[0], "1")
@@ -1040,15 +1106,16 @@ def prologue(P):
     P.salu("s_lshl_b32", S_X[6], S_N, "8")                     # bytes per head (N rows of 256 B)
     rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[6])
     rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
-    P.salu("s_mul_i32", S_X[7], S_BG, S_G)                     # query head = bg * G + 4 hb + wave
+    P.salu("s_mul_i32", S_X[7], S_BG, S_G)                     # query head = bg * G + 4 hb + (wave & 3)
     P.salu("s_lshl_b32", S_X[8], S_HB, "2")
     P.salu("s_add_u32", S_X[7], S_X[7], S_X[8])
-    P.salu("s_add_u32", S_X[7], S_X[7], S_WAVE)
+    P.salu("s_add_u32", S_X[7], S_X[7], S_WH)
     rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
     rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[6])
     P.salu("s_lshl_b32", S_X[9], S_N, "2")
     rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[9])
     P.salu("s_lshl_b32", S_WAVE1K, S_WAVE, "10")
+    P.salu("s_lshl_b32", S_WAVE1K3, S_WH, "10")
     P.salu("s_lshl_b32", S_NB, S_N, "8")
     P.salu("s_sub_u32", S_WM1, S_W, "1")
     P.salu("s_mov_b32", S_NINF, "0xff800000", writes_scc=False)
@@ -1072,18 +1139,13 @@ def prologue(P):
     P.valu("v_add_u32", t[2], t[2], t[3])
     P.valu("v_add_u32", t[2], t[2], t[4])
     P.valu("v_add_u32", V_VLANE, str(KTILE), t[2])
-    for rg in range(2):
-        P.valu("v_add_u32", t[5], S_R0, V_COL)
-        if rg:
-            P.valu("v_add_u32", t[5], "32", t[5])              # row
-        P.valu("v_lshlrev_b32", t[6], "8", t[5])               # row * 256
-        P.valu("v_lshlrev_b32", t[7], "4", V_HL)
-        P.valu("v_add_u32", V_QOFF[rg], t[6], t[7])
-        P.valu("v_lshlrev_b32", t[7], "3", V_HL)
-        P.valu("v_add_u32", V_OOFF[rg], t[6], t[7])
-        P.valu("v_lshlrev_b32", V_LOFF[rg], "2", t[5])
-        P.valu("v_lshlrev_b32", t[7], "2", V_HL)
-        P.valu("v_sub_u32", V_IBASE[rg], t[5], t[7])
+    P.valu("v_add_u32", t[5], S_R0W, V_COL)                    # row
+    P.valu("v_lshlrev_b32", t[6], "8", t[5])                   # row * 256
+    P.valu("v_lshlrev_b32", t[7], "4", V_HL)
+    P.valu("v_add_u32", V_QOFF, t[6], t[7])
+    P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
+    P.valu("v_lshlrev_b32", t[7], "2", V_HL)
+    P.valu("v_sub_u32", V_IBASE, t[5], t[7])
     # epilogue: LDS write base (row col, values 4 hl: col * 272 + 8 hl), LDS
     # read base (row lane / 16, bytes 16 (lane % 16)), global store offset
     P.valu("v_mul_u32_u24", V_OWL, str(KROW), V_COL)
@@ -1094,35 +1156,39 @@ def prologue(P):
     P.valu("v_lshlrev_b32", t[1], "4", t[1])
     P.valu("v_mul_u32_u24", V_ORDL, str(KROW), t[0])
     P.valu("v_add_u32", V_ORDL, V_ORDL, t[1])
-    P.valu("v_add_u32", t[0], S_R0, t[0])
+    P.valu("v_add_u32", t[0], S_R0W, t[0])
     P.valu("v_lshlrev_b32", t[0], "8", t[0])
     P.valu("v_add_u32", V_OST, t[0], t[1])
-    # DMA lane offsets: K chunk wave + 4 jk (jk < 4) or 16, V chunk wave + 4 jv
+    # DMA lane offsets: K chunks wave + 8 jk (jk < 2) and 16, V chunks
+    # wave + 8 jv (jv < 2) and 16 + (wave & 3)
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
     P.valu("v_mov_b32", t[9], S_WAVE1K)
-    for jk in range(5):
-        if jk < 4:
+    P.valu("v_mov_b32", t[13], S_WAVE1K3)
+    for jk in range(3):
+        if jk < 2:
             P.valu("v_add_u32", t[10], t[9], t[8])
-            P.valu("v_add_u32", t[10], str(jk * 4096), t[10])
+            P.valu("v_add_u32", t[10], str(jk * 8192), t[10])
         else:
             P.valu("v_add_u32", t[10], str(16 * 1024), t[8])
         _chunk_src(P, V_DK[jk], t[10], M272, KROW, t)
-    for jv in range(5):
-        P.valu("v_add_u32", t[10], t[9], t[8])
-        P.valu("v_add_u32", t[10], str(jv * 4096), t[10])
+    for jv in range(3):
+        if jv < 2:
+            P.valu("v_add_u32", t[10], t[9], t[8])
+            P.valu("v_add_u32", t[10], str(jv * 8192), t[10])
+        else:
+            P.valu("v_add_u32", t[10], t[13], t[8])
+            P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
         _chunk_src(P, V_DV[jv], t[10], M320, VROW, t)
     # softmax state
-    for rg in range(2):
-        P.valu("v_mov_b32", V_M[rg], "0xf149f2ca")             # -1e30
-        P.valu("v_mov_b32", V_MTHR[rg], "0xf149f2ca")
-        for k in range(2):
-            P.valu("v_mov_b32", V_L[rg][k], "0")
-        for k in range(64):
-            P.add(I(f"  v_accvgpr_write_b32 {A_O[rg].sub(k)}, 0", "valu", EMPTY, A_O[rg].sub(k).regs()))
+    P.valu("v_mov_b32", V_M, "0xf149f2ca")             # -1e30
+    P.valu("v_mov_b32", V_MTHR, "0xf149f2ca")
+    for k in range(2):
+        P.valu("v_mov_b32", V_L[k], "0")
+    for k in range(64):
+        P.add(I(f"  v_accvgpr_write_b32 {A_O.sub(k)}, 0", "valu", EMPTY, A_O.sub(k).regs()))
     # Q fragments
-    for rg in range(2):
-        for ks in range(8):
-            P.buf_load(A_Q[rg].sub(4 * ks, 4), V_QOFF[rg], S_RSQ, "0", 32 * ks)
+    for ks in range(8):
+        P.buf_load(A_Q.sub(4 * ks, 4), V_QOFF, S_RSQ, "0", 32 * ks)
     # stage tiles 0 and 1 (tile 1 also when the band has one tile: its rows
     # are read, or are past N and read as zeros, and never used)
     P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
@@ -1131,16 +1197,20 @@ def prologue(P):
     P.salu("s_add_u32", S_SOFF, S_SOFF, str(1 << 14))
     P.salu("s_mov_b32", S_SB, str(STAGE), writes_scc=False)
     dma_tile(P)
-    P.waitcnt(vm=10)
+    # set-up of iteration 0 (as if from an iteration j = -1)
+    P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
+    for op in setup_ops(0):
+        op(P)
+    P.waitcnt(vm=len(dma_ops()))
     P.barrier()
     # S(0) = K(0) Q^T
     P.salu("s_mov_b32", S_J, "0", writes_scc=False)
     P.valu("v_add_u32", V_KADDR, "0", V_KLANE)
     dump_lds(P, "lds0", STAGE)
-    dump(P, "q", [A_Q[0], A_Q[1]])
-    pairs = make_pairs(True, False, S_BUF[0], None)
-    interleave(P, pairs, [])
-    dump(P, "s0", [v(S_BUF[0], 64)])
+    dump(P, "q", [A_Q])
+    interleave(P, mfma_order(True, False), S_BUF[0], [])
+    P.valu("v_add_u32", V_KADDR, str(STAGE), V_KLANE)          # QK(1) reads stage 1
+    dump(P, "s0", [v(S_BUF[0], 32)])
 
 
 def _chunk_src(P, dst, pos, magic, rowb, t):
@@ -1169,14 +1239,14 @@ def kernel_text():
     P.scmp("s_cmp_ge_u32", S_X[0], S_T)
     P.branch("s_cbranch_scc1", ".Llast1")
     P.label(".Lmid1")
-    for ph in (1, 2, 0):
+    for ph in (1, 0):
         iteration(P, ph, True, True, False)
         P.salu("s_add_u32", S_J, S_J, "1")
         P.salu("s_add_u32", S_X[0], S_J, "1")
         P.scmp("s_cmp_ge_u32", S_X[0], S_T)                   # j == T - 1 (>=: a bound)
-        P.branch("s_cbranch_scc1", f".Llast{(ph + 1) % 3}")
+        P.branch("s_cbranch_scc1", f".Llast{1 - ph}")
     P.branch("s_branch", ".Lmid1")
-    for ph in range(3):
+    for ph in range(2):
         P.label(f".Llast{ph}")
         iteration(P, ph, False, True, False)
         epilogue(P, ph)
@@ -1218,9 +1288,9 @@ def render():
   .amdhsa_user_sgpr_kernarg_segment_ptr 1
   .amdhsa_system_sgpr_workgroup_id_x 1
   .amdhsa_system_vgpr_workitem_id 0
-  .amdhsa_next_free_vgpr 512
+  .amdhsa_next_free_vgpr 256
   .amdhsa_next_free_sgpr 96
-  .amdhsa_accum_offset 256
+  .amdhsa_accum_offset 128
   .amdhsa_reserve_vcc 1
   .amdhsa_float_denorm_mode_32 3
   .amdhsa_float_denorm_mode_16_64 3
@@ -1240,9 +1310,9 @@ amdhsa.kernels:
     .kernarg_segment_align: 8
     .wavefront_size: 64
     .sgpr_count: 96
-    .vgpr_count: 512
-    .agpr_count: 256
-    .max_flat_workgroup_size: 256
+    .vgpr_count: 256
+    .agpr_count: 128
+    .max_flat_workgroup_size: {64 * NW}
     .args:
       - {{ .offset: 0, .size: {karg}, .value_kind: by_value }}
 ...
