@@ -70,6 +70,10 @@ _lib.diff_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_
 _lib.diff_attn_fwd.restype = _i
 _lib.diff_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                ctypes.c_float, ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
+_lib.swa_probe_mfma_bf16.restype = _i
+_lib.swa_probe_mfma_bf16.argtypes = [_p, _p, _i, _i, _p]
+_lib.swa_probe_stream_read.restype = _i
+_lib.swa_probe_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
 _lib.swa_strerror.restype = ctypes.c_char_p
 _lib.swa_strerror.argtypes = [_i]
 
@@ -365,3 +369,24 @@ __all__ = ["swa_tile_config", "swa_block_mask_query", "swa_block_mask_build", "s
            "swa_attn_fwd", "swa_attn_decode_workspace_bytes", "swa_attn_decode", "swa_attn_decode_noalloc",
            "swa_attn_decode_sinks", "diff_attn_decode", "diff_attn_fwd",
            "swa_strerror", "SwaError", "BlockMask"]
+
+
+# ---- measurement probes (include/swa_probe.h) ---------------------------------
+def swa_probe_mfma_bf16(operands, out, workgroups, iters):
+    """Dense bf16 MFMA loop: `operands` 512 x 8 bf16 (device), `out`
+    workgroups * 512 float32.  FLOP per call: workgroups * 8 * iters * 32 * 32768."""
+    _expect(operands, "operands", (512, 8), torch.bfloat16, operands.device)
+    _expect(out, "out", (workgroups * 512,), torch.float32, operands.device)
+    _check(_lib.swa_probe_mfma_bf16(_ptr(operands), _ptr(out), workgroups, iters, _stream(out)),
+           "swa_probe_mfma_bf16")
+    return out
+
+
+def swa_probe_stream_read(buf, out, workgroups):
+    """Streaming read of the contiguous device tensor `buf` with 16-byte loads;
+    `out` workgroups * 256 int32."""
+    _need(buf, "buf")
+    _expect(out, "out", (workgroups * 256,), torch.int32, buf.device)
+    _check(_lib.swa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), workgroups,
+                                      _stream(out)), "swa_probe_stream_read")
+    return out

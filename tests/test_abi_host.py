@@ -1,6 +1,6 @@
 """CPU tests of the C-ABI boundary (no GPU, no kernel launch).
 
-The library must load and export every entry point include/swa.h declares;
+The library must load and export every entry point include/*.h declares;
 argument checks run on the host before any HIP call, so every rejection is
 exercised here with fake (never dereferenced) pointers; the host-side block
 mask sizing must agree exactly with the oracle's brute-force tile list.
@@ -16,7 +16,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("swa.h", "swa_probe.h")]
 PKG = os.path.join(ROOT, "sparse_masked_transformer_amd")
 
 FAKE = 0x7F0000000000  # 16-byte aligned; never dereferenced by a rejected call
@@ -31,7 +31,7 @@ def swa():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*\b([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "while")))
@@ -42,7 +42,28 @@ def test_header_declares_the_hot_path_calls():
     for n in ("swa_block_mask_build", "swa_attn_fwd", "swa_attn_decode", "swa_attn_decode_sinks",
               "diff_attn_fwd", "diff_attn_decode"):
         assert n in names
-    assert len(names) == 12, names
+    assert "swa_probe_mfma_bf16" in names and "swa_probe_stream_read" in names
+    assert len(names) == 14, names
+
+
+def test_every_header_is_listed():
+    assert sorted(os.path.basename(h) for h in HEADERS) == sorted(
+        f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+
+
+def test_probe_rejections(swa):
+    lib = swa.lib
+    P = ctypes.c_void_p
+    assert lib.swa_probe_mfma_bf16(None, P(FAKE), 1, 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_mfma_bf16(P(FAKE + 8), P(FAKE), 1, 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_mfma_bf16(P(FAKE), P(FAKE), 0, 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_mfma_bf16(P(FAKE), P(FAKE), 1, 0, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_mfma_bf16(P(FAKE), P(FAKE), 1, (1 << 24) + 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_stream_read(None, 16, P(FAKE), 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_stream_read(P(FAKE), 0, P(FAKE), 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_stream_read(P(FAKE), 24, P(FAKE), 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_stream_read(P(FAKE + 4), 16, P(FAKE), 1, None) == swa.SWA_ERR_INVALID_ARG
+    assert lib.swa_probe_stream_read(P(FAKE), 16, P(FAKE), 65536, None) == swa.SWA_ERR_INVALID_ARG
 
 
 def test_library_exports_every_declared_symbol(swa):
