@@ -203,6 +203,17 @@ def test_tiny_fp32_workload_full(swa):
     assert max_err(got, want) <= TOL["f32"]
 
 
+def threaded(fn, idx):
+    """fn over index chunks on the host's threads (the oracle releases the
+    GIL), concatenated in order."""
+    import concurrent.futures
+    import os
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [c for c in np.array_split(np.asarray(idx), threads * 4) if len(c)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        return np.concatenate(list(ex.map(fn, chunks)))
+
+
 def boundary_rows(B, H, N, step, extra):
     must = []
     for b in range(B):
@@ -214,16 +225,18 @@ def boundary_rows(B, H, N, step, extra):
 
 @pytest.mark.parametrize("name", ["swa_prefill_bf16", "local_strided_bf16", "global_prefill_bf16",
                                   "dilated_prefill_bf16"])
-def test_prefill_workload_sampled(swa, name):
+def test_prefill_workload_all_rows(swa, name):
+    """Every row of the workload at full size (every workgroup of the launch
+    the benchmark times), against the oracle run on the host's threads."""
     cfg = synth.workload(name)
-    banner(f"workload {name} (sampled rows)")
+    banner(f"workload {name} (all rows)")
     q, k, v = synth.prefill_inputs(cfg)
     got = run_prefill(swa, cfg, q, k, v).reshape(-1, cfg["dv"])
-    rows = boundary_rows(cfg["B"], cfg["Hq"], cfg["N"], 3, 768)
-    want = oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], rows,
-                            dilation=cfg.get("dilation", 1), n_global=cfg.get("n_global", 0))
-    assert max_err(got[rows], want) <= TOL["bf16"]
-    assert np.all(np.isfinite(got))
+    rows = np.arange(got.shape[0], dtype=np.int64)
+    want = threaded(lambda r: oracle.attn_rows(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], r,
+                                               dilation=cfg.get("dilation", 1),
+                                               n_global=cfg.get("n_global", 0)), rows)
+    assert max_err(got, want) <= TOL["bf16"]
 
 
 def test_prefill_longest_sequence(swa):
@@ -303,14 +316,25 @@ def test_diff_dilated_global_parity(swa, dtype, N, d, dv, W, s, dil, g):
     assert max_err(got, want) <= TOL[dtype]
 
 
-def test_diff_workload_sampled(swa):
+def test_diff_workload_all_rows(swa):
     cfg = synth.workload("diff_bf16")
-    banner("workload diff_bf16 (sampled rows)")
+    banner("workload diff_bf16 (all rows)")
     ins = synth.diff_inputs(cfg)
     got = run_diff(swa, cfg, *ins).reshape(-1, cfg["dv"])
-    rows = boundary_rows(cfg["B"], cfg["Hq"], cfg["N"], 4, 768)
-    want = oracle.diff_rows(*ins, cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], rows)
-    assert max_err(got[rows], want) <= TOL["bf16"]
+    rows = np.arange(got.shape[0], dtype=np.int64)
+    want = threaded(lambda r: oracle.diff_rows(*ins, cfg["window"], cfg["stride"], cfg["scale"], cfg["lam"], r),
+                    rows)
+    assert max_err(got, want) <= TOL["bf16"]
+
+
+def test_diff_deterministic(swa):
+    cfg = dict(dtype="bf16", B=1, Hq=4, Hkv=4, N=1000, d=64, dv=128, window=300, stride=0, scale=0.125,
+               lam=0.5, seed=55)
+    banner("diff determinism")
+    ins = synth.diff_inputs(cfg)
+    a = run_diff(swa, cfg, *ins)
+    b = run_diff(swa, cfg, *ins)
+    np.testing.assert_array_equal(a, b)
 
 
 # --------------------------------------------------------------------------
@@ -356,12 +380,13 @@ def test_decode_parity(swa, dtype, B, Hq, Hkv, W, d, lens):
 
 
 def test_decode_longest_ring(swa):
-    # a ring of 2^22 slots (the largest window the boundary accepts): split
-    # across workgroups, byte offsets up to 1 GiB per ring; one sequence
-    # past the ring's first wrap, one still filling it
+    # a ring of 2^22 slots (the largest window the boundary accepts) at
+    # d = 128: split across workgroups, byte offsets up to 1 GiB per ring
+    # (the bound the ring's 32-bit lane offsets rely on); one sequence past
+    # the ring's first wrap, one still filling it
     W = swa.SWA_MAX_N
-    cfg = dict(dtype="bf16", B=2, Hq=4, Hkv=1, window=W, d=64, dv=64, position=0, n_sink=0,
-               scale=0.125, seed=23)
+    cfg = dict(dtype="bf16", B=2, Hq=2, Hkv=1, window=W, d=128, dv=128, position=0, n_sink=0,
+               scale=1.0 / math.sqrt(128), seed=23)
     banner(f"decode with a ring of {W} slots")
     ins = synth.decode_inputs(cfg, seq_len=[W + 1000, W // 2 + 3])
     got = run_decode(swa, cfg, ins)
@@ -464,35 +489,54 @@ def test_diff_decode_f32_wide_heads(swa):
 
 def test_sink_decode_workload(swa):
     cfg = synth.workload("sink_decode_bf16")
-    banner("workload sink_decode_bf16 (sequences 0, 29, 63)")
+    banner("workload sink_decode_bf16 (all 64 sequences)")
     ins = synth.decode_inputs(cfg)
     got = run_decode_sinks(swa, cfg, ins)
-    pick = [0, 29, 63]
-    want = oracle.decode(ins["q"][pick], ins["k_ring"][pick], ins["v_ring"][pick], ins["seq_len"][pick],
-                         cfg["scale"], k_sink=ins["k_sink"][pick], v_sink=ins["v_sink"][pick])
-    assert max_err(got[pick], want) <= TOL["bf16"]
-    assert np.all(np.isfinite(got))
+    want = threaded(lambda b: oracle.decode(ins["q"][b], ins["k_ring"][b], ins["v_ring"][b], ins["seq_len"][b],
+                                            cfg["scale"], k_sink=ins["k_sink"][b], v_sink=ins["v_sink"][b]),
+                    np.arange(cfg["B"]))
+    assert max_err(got, want) <= TOL["bf16"]
 
 
 def test_diff_decode_workload(swa):
     cfg = synth.workload("diff_decode_bf16")
-    banner("workload diff_decode_bf16 (sequences 0, 13, 31)")
+    banner("workload diff_decode_bf16 (all 32 sequences)")
     ins = synth.diff_decode_inputs(cfg)
     got = run_diff_decode(swa, cfg, ins)
-    pick = [0, 13, 31]
-    want = oracle.diff_decode(*(ins[x][pick] for x in ("q1", "k1_ring", "q2", "k2_ring", "v_ring",
-                                                        "seq_len")), cfg["scale"], cfg["lam"])
-    assert max_err(got[pick], want) <= TOL["bf16"]
-    assert np.all(np.isfinite(got))
+    want = threaded(lambda b: oracle.diff_decode(*(ins[x][b] for x in ("q1", "k1_ring", "q2", "k2_ring",
+                                                                       "v_ring", "seq_len")),
+                                                 cfg["scale"], cfg["lam"]), np.arange(cfg["B"]))
+    assert max_err(got, want) <= TOL["bf16"]
 
 
 def test_decode_workload(swa):
     cfg = synth.workload("window_decode_bf16")
-    banner("workload window_decode_bf16 (sequences 0, 17, 63)")
+    banner("workload window_decode_bf16 (all 64 sequences)")
     ins = synth.decode_inputs(cfg)
     got = run_decode(swa, cfg, ins)
-    pick = [0, 17, 63]
-    want = oracle.decode(ins["q"][pick], ins["k_ring"][pick], ins["v_ring"][pick],
-                         ins["seq_len"][pick], cfg["scale"])
-    assert max_err(got[pick], want) <= TOL["bf16"]
-    assert np.all(np.isfinite(got))
+    want = threaded(lambda b: oracle.decode(ins["q"][b], ins["k_ring"][b], ins["v_ring"][b],
+                                            ins["seq_len"][b], cfg["scale"]), np.arange(cfg["B"]))
+    assert max_err(got, want) <= TOL["bf16"]
+
+
+# Run-to-run determinism (a race canary): the split of a window over
+# workgroups and its combine, sink slots and the two-map decode must give
+# bitwise the same output every time.
+@pytest.mark.parametrize("kind", ["window_split", "sinks", "diff"])
+def test_decode_deterministic(swa, kind):
+    banner(f"decode determinism {kind}")
+    if kind == "diff":
+        cfg = dict(dtype="bf16", B=1, Hq=4, Hkv=2, window=3000, d=64, dv=128, position=0, scale=0.125,
+                   lam=0.5, seed=81)
+        ins = synth.diff_decode_inputs(cfg, seq_len=[2900])
+        run = lambda: run_diff_decode(swa, cfg, ins)
+    else:
+        # one sequence, one key/value head: the window is split over many
+        # workgroups and the partial results combined
+        cfg = dict(dtype="bf16", B=1, Hq=4, Hkv=1, window=4096, d=128, dv=128, position=0,
+                   n_sink=4 if kind == "sinks" else 0, scale=1.0 / math.sqrt(128), seed=82)
+        ins = synth.decode_inputs(cfg, seq_len=[100000])
+        run = (lambda: run_decode_sinks(swa, cfg, ins)) if kind == "sinks" else (lambda: run_decode(swa, cfg, ins))
+    a = run()
+    b = run()
+    np.testing.assert_array_equal(a, b)
