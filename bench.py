@@ -175,6 +175,21 @@ def traffic_record(kernel_src, key):
     return rec["bytes_per_launch"] if rec.get("kernel_sha256") == kernel_build_sha(kernel_src) else None
 
 
+def decode_alg_bytes(cfg, n_sink=0):
+    """Bytes one decode step must move: the K and V of the window (and of the
+    sink slots) of every (sequence, key/value head) read once, q read and
+    the output written once (2-byte elements)."""
+    B, Hq, Hkv, W, d, dv = (cfg[x] for x in ("B", "Hq", "Hkv", "window", "d", "dv"))
+    return B * Hkv * (W + n_sink) * (d + dv) * 2 + B * Hq * (d + dv) * 2
+
+
+def diff_decode_alg_bytes(cfg):
+    """Bytes one differential decode step must move: the two key windows and
+    the one value window read once, q1, q2 read and the output written once."""
+    B, Hq, Hkv, W, d, dv = (cfg[x] for x in ("B", "Hq", "Hkv", "window", "d", "dv"))
+    return B * Hkv * W * (2 * d + dv) * 2 + B * Hq * (2 * d + dv) * 2
+
+
 def row_keys(i, w, s):
     """Attended keys of query row i: the window's min(i + 1, w) plus the
     stride keys j <= i - w with j mod s == 0 (the mask's closed form)."""
@@ -354,11 +369,11 @@ def main():
         ws = torch.empty(max(1, swa.swa_attn_decode_workspace_bytes(B, Hq, Hkv, d, Wr)),
                          dtype=torch.uint8, device="cuda")
         dout = torch.empty((B, Hq, d), dtype=bf16, device="cuda")
-        kv_bytes = 2 * B * Hkv * Wr * d * 2
+        kv_bytes = decode_alg_bytes(dcfg) - B * Hq * 2 * d * 2
         res["decode"] = time_decode(
             "decode", mk, lambda t: swa.swa_attn_decode(t["q"], t["k"], t["v"], t["sl"], dcfg["scale"],
                                                         workspace=ws, out=dout),
-            kv_bytes + 2 * B * Hq * d * 2, keep_name="window_decode_bf16")
+            decode_alg_bytes(dcfg), keep_name="window_decode_bf16")
         res["decode"]["kv_gbs"] = kv_bytes / (res["decode"]["event_ms"] * 1e-3) / 1e9
 
     if args.only in (None, "sink_decode"):
@@ -376,7 +391,7 @@ def main():
             "sink decode", mk,
             lambda t: swa.swa_attn_decode_sinks(t["q"], t["k_sink"], t["v_sink"], t["k_ring"], t["v_ring"],
                                                 t["sl"], scfg_["scale"], workspace=ws, out=dout),
-            2 * B * Hkv * (Wr + S) * d * 2 + 2 * B * Hq * d * 2)
+            decode_alg_bytes(scfg_, S))
 
     if args.only in (None, "diff_decode"):
         gcfg = synth.workload("diff_decode_bf16")
@@ -393,7 +408,7 @@ def main():
             "diff decode", mk,
             lambda t: swa.diff_attn_decode(t["q1"], t["k1_ring"], t["q2"], t["k2_ring"], t["v_ring"], t["sl"],
                                            gcfg["scale"], gcfg["lam"], workspace=ws, out=dout),
-            B * Hkv * Wr * (2 * d + dv) * 2 + B * Hq * (2 * d + dv) * 2)
+            diff_decode_alg_bytes(gcfg))
 
     # ---- local + strided prefill ----------------------------------------------
     if args.only in (None, "strided"):
@@ -605,7 +620,7 @@ def cpu_baselines(keep, budget_s):
         want = np.concatenate(outs)
         _, Hq, d = ins["q"].shape
         Hkv, Wr = ins["k_ring"].shape[1], ins["k_ring"].shape[2]
-        nbytes = 2 * B * Hkv * Wr * d * 2 + 2 * B * Hq * d * 2
+        nbytes = decode_alg_bytes(synth.workload("window_decode_bf16"))
         per["window_decode_bf16"] = dict(rows=int(B * Hq), of=int(B * Hq), sequences=int(B), seconds=round(dt, 3),
                                          value=round(nbytes / dt / 1e9, 3), unit="GB/s",
                                          max_abs_err_vs_gpu=float(np.max(np.abs(gout - want))))

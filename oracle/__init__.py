@@ -47,6 +47,8 @@ def _configure(lib):
     lib.orc_decode.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _ptr, _ptr]
     lib.orc_count_nsa.restype = _i64
     lib.orc_count_nsa.argtypes = [_i64] * 4
+    lib.orc_kv_cache_bytes.restype = _i64
+    lib.orc_kv_cache_bytes.argtypes = [_i64] * 5
     return lib
 
 
@@ -245,3 +247,10 @@ def diff_decode(q1, k1_ring, q2, k2_ring, v_ring, seq_len, scale, lam):
 def count_nsa(n, l, k, w):
     """count_nsa(N, l, k, W): keys read per query by native sparse attention."""
     return int(_load().orc_count_nsa(n, l, k, w))
+
+
+def kv_cache_bytes(N, n_layers, n_heads_kv, d_head, dtype=2):
+    """kv_cache_bytes(N, n_layers, n_heads_kv, d_head, dtype=2): bytes of the
+    keys and values kept for N positions ("Attention Variants Compared",
+    task table)."""
+    return int(_load().orc_kv_cache_bytes(N, n_layers, n_heads_kv, d_head, dtype))

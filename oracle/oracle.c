@@ -430,3 +430,19 @@ int64_t orc_count_nsa(int64_t n, int64_t l, int64_t k, int64_t w)
 {
     return n / l + k * l + w;
 }
+
+/* [VAR] task table, "KV cache bytes": kv_cache_bytes(N, n_layers, n_heads_kv,
+ * d_head, dtype=2) -- the bytes that keep one key and one value vector of
+ * d_head elements for each of N positions, key/value heads and layers, at
+ * dtype bytes per element.  [EXP] "Quantifying Memory Impact with KV-Cache
+ * Calculations" computes the same quantity from layers, KV heads, head
+ * dimension and sequence length (in another argument order; the task
+ * table's is kept here).  [SSW] §6 "FLOPs & memory" states the position
+ * counts it is taken at: all s positions for dense decode, the last w for a
+ * rolling window, k sinks plus w for StreamingLLM. */
+int64_t orc_kv_cache_bytes(int64_t n, int64_t n_layers, int64_t n_heads_kv, int64_t d_head,
+                           int64_t dtype_bytes)
+{
+    const int64_t per_tensor = n * n_layers * n_heads_kv * d_head * dtype_bytes;
+    return 2 * per_tensor;   /* K and V */
+}

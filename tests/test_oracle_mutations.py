@@ -43,6 +43,9 @@ MUTATIONS = {
     "tile_kind_full_never": ("else if (c == (i1 - i0) * (j1 - j0))", "else if (c == (i1 - i0) * (j1 - j0) + 1)"),
     "nsa_branch_dropped": ("return n / l + k * l + w;", "return n / l + k * l;"),
     "lse_without_max": ("return l > 0.0 ? m + log(l) : -INFINITY;", "return l > 0.0 ? log(l) : -INFINITY;"),
+    "kv_cache_keys_only": ("return 2 * per_tensor;   /* K and V */", "return per_tensor;"),
+    "kv_cache_layers_dropped": ("const int64_t per_tensor = n * n_layers * n_heads_kv * d_head * dtype_bytes;",
+                                "const int64_t per_tensor = n * n_heads_kv * d_head * dtype_bytes;"),
 }
 
 
@@ -74,6 +77,8 @@ def all_pins():
         ("decode_partial_ring", lambda: pins.test_decode_is_last_row_of_window_attention(5, 8)),
         ("sinks", lambda: pins.test_decode_with_sinks(40, 8, 4)),
         ("nsa", pins.test_nsa_key_count_printed_value),
+        ("kv_worked", pins.test_kv_cache_bytes_worked_example),
+        ("kv_rolling", pins.test_kv_cache_bytes_rolling_window_and_sinks),
     ]
     return out
 

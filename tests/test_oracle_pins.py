@@ -559,6 +559,44 @@ def test_nsa_key_count_printed_value():
     assert 1024 / oracle.count_nsa(1024, 32, 4, 128) >= 3.5
 
 
+def test_kv_cache_bytes_worked_example():
+    """The 128K-token example of "Exploring Attention Variants" (80 layers, 8
+    KV heads, head dimension 128, 131,072 positions, 2-byte elements): K and
+    V at 80 x 8 x 128 = 81,920 elements per position each, 2 bytes per
+    element, 131,072 = 2^17 positions -- 81,920 x 4 x 2^17 bytes = 40 GiB
+    exactly; a 4,096-token window keeps 4096/131072 = 1/32 of it, 1.25 GiB.
+    (The page's own printed figures, about 17 GB and 2.8 GB and "up to 6x",
+    cannot both hold under the linear window scaling the same page states:
+    2.8/17 is not 4096/131072.  They are left unpinned.)"""
+    full = oracle.kv_cache_bytes(131072, 80, 8, 128)
+    assert full == 40 * 2 ** 30
+    assert oracle.kv_cache_bytes(4096, 80, 8, 128) == 5 * 2 ** 28
+    assert abs(2.8 / 17 - 4096 / 131072) > 0.1
+
+
+def test_kv_cache_bytes_rolling_window_and_sinks():
+    """Learn: Sparse & Sliding-Window Attention, §6 "FLOPs & memory": dense
+    decode keeps every past position (the cache grows with s), a rolling
+    window keeps the last w whatever s is, StreamingLLM keeps k sinks plus
+    the last w.  Bytes are additive over positions and proportional to the
+    element size; a single element of K and one of V is 2 x dtype bytes."""
+    L, H, d = 2, 3, 5
+    assert oracle.kv_cache_bytes(1, 1, 1, 1, dtype=1) == 2
+    assert oracle.kv_cache_bytes(1, 1, 1, 1, dtype=4) == 8
+    one = oracle.kv_cache_bytes(1, L, H, d)
+    for s_, w, k in ((10, 4, 2), (100, 16, 4), (3, 8, 1)):
+        # dense: every one of the s positions; grows by one position per token
+        assert oracle.kv_cache_bytes(s_, L, H, d) == s_ * one
+        assert oracle.kv_cache_bytes(s_ + 1, L, H, d) - oracle.kv_cache_bytes(s_, L, H, d) == one
+        # rolling window: min(s, w) positions, the same for every s >= w
+        held = [oracle.kv_cache_bytes(min(t, w), L, H, d) for t in range(w, w + 50)]
+        assert len(set(held)) == 1 and held[0] == w * one
+        # sinks plus window: k + w positions
+        assert oracle.kv_cache_bytes(k + w, L, H, d) == (k + w) * one
+    # the elements of one position: a key and a value vector per layer and head
+    assert oracle.kv_cache_bytes(1, L, H, d, dtype=1) == 2 * L * H * d
+
+
 def test_bf16_rounding_matches_torch():
     x = np.random.default_rng(50).standard_normal(100000).astype(np.float32) * 3
     x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 0.0]  # ties to even
