@@ -68,9 +68,14 @@ typedef enum {
                               /* SWA_DECODE_SCRATCH_BYTES of scratch                  */
 } swa_status_t;
 
+/* Element type of Q, K, V and the output.  Entry points take it as an int
+ * `dt` holding one of these values; any other value is SWA_ERR_INVALID_ARG
+ * (an int, not the enum type, so that an out-of-range value is a defined
+ * input the library rejects). */
 typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
 
-/* The attention call a block mask is built for (their tile shapes differ). */
+/* The attention call a block mask is built for (their tile shapes differ);
+ * taken as an int `op` holding one of these values, like `dt`. */
 typedef enum { SWA_OP_ATTN = 0, SWA_OP_DIFF = 1 } swa_op_t;
 
 /* Largest sequence length any entry point accepts (keeps every index and
@@ -123,7 +128,7 @@ typedef struct {
  * dtype and head sizes (swa_attn_fwd: SWA_OP_ATTN, diff_attn_fwd:
  * SWA_OP_DIFF); a block mask built with other sizes is rejected by that
  * call.  Host only, no HIP call.  d, dv in {32, 64, 128}. */
-int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn);
+int swa_tile_config(int op, int dt, int d, int dv, int32_t *bm, int32_t *bn);
 
 /* Number of query tiles and list entries of the block mask of
  * (N, window, stride, dilation, n_global, bm, bn).  Host only, no HIP call.
@@ -157,7 +162,7 @@ int swa_mask_dense(int N, int window, int stride, int dilation, int n_global, ui
  * (SWA_BF16) or kept fp32 (SWA_F32).
  */
 int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
-                 swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                 int dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                  int dilation, int n_global, float scale, const swa_block_mask_t *mask,
                  hipStream_t stream);
 
@@ -166,7 +171,7 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
  * diff_attn_decode; n_sink = 0 except for swa_attn_decode_sinks.  0 means
  * the call needs none (workspace may then be NULL); also 0 for invalid
  * sizes, which the call itself rejects. */
-size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int dv, int window,
+size_t swa_attn_decode_workspace_bytes(int op, int B, int Hq, int Hkv, int dv, int window,
                                        int n_sink);
 
 /*
@@ -192,7 +197,7 @@ size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int 
  */
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,
-                    swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                    int dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                     float scale, hipStream_t stream);
 
 /*
@@ -210,7 +215,7 @@ int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void 
 int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink, int n_sink,
                           const void *k_ring, const void *v_ring, void *out,
                           const int32_t *seq_len, void *workspace, size_t workspace_bytes,
-                          swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window,
+                          int dt, int B, int Hq, int Hkv, int N, int d, int window,
                           float scale, hipStream_t stream);
 
 /*
@@ -231,7 +236,7 @@ int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink,
  */
 int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const void *k2_ring,
                      const void *v_ring, void *out, const int32_t *seq_len, void *workspace,
-                     size_t workspace_bytes, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d,
+                     size_t workspace_bytes, int dt, int B, int Hq, int Hkv, int N, int d,
                      int dv, int window, float scale, float lambda, hipStream_t stream);
 
 /*
@@ -249,7 +254,7 @@ int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const 
  *   and the tiles of swa_tile_config(SWA_OP_DIFF, dt, d, dv).
  */
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2,
-                  const void *v, void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N,
+                  const void *v, void *out, int dt, int B, int Hq, int Hkv, int N,
                   int d, int dv, int window, int stride, int dilation, int n_global, float scale,
                   float lambda, const swa_block_mask_t *mask, hipStream_t stream);
 
@@ -274,7 +279,7 @@ int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2
  */
 #define SWA_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
 int swa_attn_decode_noalloc(const void *q, const void *k_ring, const void *v_ring, void *out,
-                            const int32_t *seq_len, swa_dtype_t dt, int B, int Hq, int Hkv,
+                            const int32_t *seq_len, int dt, int B, int Hq, int Hkv,
                             int N, int d, int window, int stride, float scale,
                             hipStream_t stream);
 

@@ -19,76 +19,17 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
                       "`python sparse_masked_transformer_amd/build.py` (hipcc, gfx950)")
 
-_lib = ctypes.CDLL(LIB_PATH)
+from ._abi import (SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE,  # noqa: E402
+                   SWA_ERR_HIP, SWA_ERR_SCRATCH, SWA_DECODE_SCRATCH_BYTES, SWA_F32, SWA_BF16,
+                   SWA_OP_ATTN, SWA_OP_DIFF, SWA_MAX_N, SwaError, swa_block_mask_t)
+from . import _abi  # noqa: E402
 
-SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP = 0, -1, -2, -3, -4
-SWA_ERR_SCRATCH = -5
-SWA_DECODE_SCRATCH_BYTES = 4 << 20
-SWA_F32, SWA_BF16 = 0, 1
-SWA_OP_ATTN, SWA_OP_DIFF = 0, 1
-SWA_MAX_N = 1 << 22
-
-_p = ctypes.c_void_p
-_i = ctypes.c_int
-_i32p = ctypes.POINTER(ctypes.c_int32)
-
-
-class swa_block_mask_t(ctypes.Structure):
-    _fields_ = [("N", ctypes.c_int32), ("window", ctypes.c_int32), ("stride", ctypes.c_int32),
-                ("dilation", ctypes.c_int32), ("n_global", ctypes.c_int32),
-                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
-                ("num_q_tiles", ctypes.c_int32), ("nnz", ctypes.c_int32),
-                ("row_ptr", _p), ("kv_tile", _p), ("kind", _p), ("cells", _p),
-                ("prefix_keys", _p), ("band_begin", _p)]
-
-
-_lib.swa_tile_config.restype = _i
-_lib.swa_tile_config.argtypes = [_i, _i, _i, _i, _i32p, _i32p]
-_lib.swa_block_mask_query.restype = _i
-_lib.swa_block_mask_query.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i32p, _i32p]
-_lib.swa_block_mask_build.restype = _i
-_lib.swa_block_mask_build.argtypes = [ctypes.POINTER(swa_block_mask_t), _p]
-_lib.swa_mask_dense.restype = _i
-_lib.swa_mask_dense.argtypes = [_i, _i, _i, _i, _i, _p, _p]
-_lib.swa_attn_fwd.restype = _i
-_lib.swa_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
-                              ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
-_lib.swa_attn_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.swa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
-_lib.swa_attn_decode.restype = _i
-_lib.swa_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i, _i, _i,
-                                 _i, _i, ctypes.c_float, _p]
-_lib.swa_attn_decode_noalloc.restype = _i
-_lib.swa_attn_decode_noalloc.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
-                                         ctypes.c_float, _p]
-_lib.swa_attn_decode_sinks.restype = _i
-_lib.swa_attn_decode_sinks.argtypes = [_p, _p, _p, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i,
-                                       _i, _i, _i, _i, _i, ctypes.c_float, _p]
-_lib.diff_attn_decode.restype = _i
-_lib.diff_attn_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _i, _i, _i, _i,
-                                  _i, _i, _i, _i, ctypes.c_float, ctypes.c_float, _p]
-_lib.diff_attn_fwd.restype = _i
-_lib.diff_attn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
-                               ctypes.c_float, ctypes.c_float, ctypes.POINTER(swa_block_mask_t), _p]
-_lib.swa_probe_mfma_bf16.restype = _i
-_lib.swa_probe_mfma_bf16.argtypes = [_p, _p, _i, _i, _p]
-_lib.swa_probe_stream_read.restype = _i
-_lib.swa_probe_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
-_lib.swa_strerror.restype = ctypes.c_char_p
-_lib.swa_strerror.argtypes = [_i]
-
+_lib = _abi.configure(ctypes.CDLL(LIB_PATH))
 lib = _lib  # raw ctypes handle (the tests call the C functions directly)
 
 
-class SwaError(RuntimeError):
-    def __init__(self, status, where):
-        self.status = status
-        super().__init__(f"{where}: {swa_strerror(status)} ({status})")
-
-
 def _check(status, where):
-    if status != SWA_OK:
-        raise SwaError(status, where)
+    _abi.check(_lib, status, where)
 
 
 def _dtype_code(t):
@@ -150,7 +91,7 @@ def _expect_workspace(workspace, device):
 
 
 def swa_strerror(status):
-    return _lib.swa_strerror(status).decode()
+    return _abi.strerror(_lib, status)
 
 
 def swa_tile_config(dtype, d, dv=None, op=SWA_OP_ATTN):
@@ -165,10 +106,7 @@ def swa_tile_config(dtype, d, dv=None, op=SWA_OP_ATTN):
 def swa_block_mask_query(N, window, stride, bm, bn, dilation=1, n_global=0):
     """(num_q_tiles, nnz) of the block mask of (N, window, stride, dilation,
     n_global, bm, bn)."""
-    nq, nnz = ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.swa_block_mask_query(N, window, stride, dilation, n_global, bm, bn, ctypes.byref(nq),
-                                     ctypes.byref(nnz)), "swa_block_mask_query")
-    return nq.value, nnz.value
+    return _abi.block_mask_query(_lib, N, window, stride, bm, bn, dilation, n_global)
 
 
 class BlockMask:

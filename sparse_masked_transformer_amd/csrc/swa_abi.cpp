@@ -100,7 +100,7 @@ int check_sizes(int B, int Hq, int Hkv, int N, int window, int stride, int dilat
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 
-int fwd_run(const swa::FwdArgs &a, swa_dtype_t dt, hipStream_t stream) {
+int fwd_run(const swa::FwdArgs &a, int dt, hipStream_t stream) {
     if (swa::fwd_workgroups(a, dt) * swa::fwd_threads(a, dt) > swa::kMaxGridItems)
         return SWA_ERR_UNSUPPORTED;  // more work-items than one dispatch holds
     return hip_status(dt == SWA_BF16 ? swa::launch_fwd_bf16(a, stream) : swa::launch_fwd_f32(a, stream));
@@ -130,7 +130,7 @@ DecodePlan decode_plan(int B, int Hkv, int slots) {
     return DecodePlan{static_cast<int>(waves), static_cast<int>(splits), static_cast<int>(spw)};
 }
 
-int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt) {
+int64_t decode_launch_items(const DecodeArgs &a, int dt) {
     const int64_t rows = static_cast<int64_t>(a.B) * a.Hq;   // (sequence, query head) pairs
     if (dt == SWA_F32) {
         // 64-lane workgroups of 64 / kF32TPR rows
@@ -163,7 +163,7 @@ size_t decode_ws_bytes(int nmaps, int B, int Hq, int Hkv, int dv, int window, in
 
 // Checks shared by the decode entry points, all but the workspace's; fills
 // nothing on failure.
-int decode_arg_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride) {
+int decode_arg_checks(const swa::DecodeArgs &a, int dt, int stride) {
     for (int m = 0; m < a.nmaps; ++m) {
         if (!aligned16(a.q[m]) || !aligned16(a.k_ring[m]))
             return SWA_ERR_INVALID_ARG;
@@ -196,7 +196,7 @@ int decode_arg_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride) {
     return SWA_OK;
 }
 
-int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes) {
+int decode_checks(const swa::DecodeArgs &a, int dt, int stride, size_t workspace_bytes) {
     int st = decode_arg_checks(a, dt, stride);
     if (st != SWA_OK)
         return st;
@@ -206,7 +206,7 @@ int decode_checks(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t w
     return SWA_OK;
 }
 
-int decode_run(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t workspace_bytes,
+int decode_run(const swa::DecodeArgs &a, int dt, int stride, size_t workspace_bytes,
                hipStream_t stream) {
     int st = decode_checks(a, dt, stride, workspace_bytes);
     if (st != SWA_OK)
@@ -219,7 +219,7 @@ int decode_run(const swa::DecodeArgs &a, swa_dtype_t dt, int stride, size_t work
 
 extern "C" {
 
-int swa_tile_config(swa_op_t op, swa_dtype_t dt, int d, int dv, int32_t *bm, int32_t *bn) {
+int swa_tile_config(int op, int dt, int d, int dv, int32_t *bm, int32_t *bn) {
     if ((op != SWA_OP_ATTN && op != SWA_OP_DIFF) || (dt != SWA_F32 && dt != SWA_BF16) ||
         !head_dim_ok(d) || !head_dim_ok(dv) || !bm || !bn)
         return SWA_ERR_INVALID_ARG;
@@ -257,7 +257,7 @@ int swa_mask_dense(int N, int window, int stride, int dilation, int n_global, ui
 }
 
 int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
-                 swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                 int dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                  int dilation, int n_global, float scale, const swa_block_mask_t *mask,
                  hipStream_t stream) {
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -299,7 +299,7 @@ int swa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     return fwd_run(a, dt, stream);
 }
 
-size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int dv, int window,
+size_t swa_attn_decode_workspace_bytes(int op, int B, int Hq, int Hkv, int dv, int window,
                                        int n_sink) {
     if (op != SWA_OP_ATTN && op != SWA_OP_DIFF)
         return 0;
@@ -308,7 +308,7 @@ size_t swa_attn_decode_workspace_bytes(swa_op_t op, int B, int Hq, int Hkv, int 
 
 int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void *out,
                     const int32_t *seq_len, void *workspace, size_t workspace_bytes,
-                    swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
+                    int dt, int B, int Hq, int Hkv, int N, int d, int window, int stride,
                     float scale, hipStream_t stream) {
     swa::DecodeArgs a{};
     a.q[0] = q;
@@ -332,7 +332,7 @@ int swa_attn_decode(const void *q, const void *k_ring, const void *v_ring, void 
 }
 
 int swa_attn_decode_noalloc(const void *q, const void *k_ring, const void *v_ring, void *out,
-                            const int32_t *seq_len, swa_dtype_t dt, int B, int Hq, int Hkv,
+                            const int32_t *seq_len, int dt, int B, int Hq, int Hkv,
                             int N, int d, int window, int stride, float scale,
                             hipStream_t stream) {
     swa::DecodeArgs a{};
@@ -370,7 +370,7 @@ int swa_attn_decode_noalloc(const void *q, const void *k_ring, const void *v_rin
 int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink, int n_sink,
                           const void *k_ring, const void *v_ring, void *out,
                           const int32_t *seq_len, void *workspace, size_t workspace_bytes,
-                          swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int window,
+                          int dt, int B, int Hq, int Hkv, int N, int d, int window,
                           float scale, hipStream_t stream) {
     swa::DecodeArgs a{};
     a.q[0] = q;
@@ -397,7 +397,7 @@ int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink,
 
 int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const void *k2_ring,
                      const void *v_ring, void *out, const int32_t *seq_len, void *workspace,
-                     size_t workspace_bytes, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d,
+                     size_t workspace_bytes, int dt, int B, int Hq, int Hkv, int N, int d,
                      int dv, int window, float scale, float lambda, hipStream_t stream) {
     swa::DecodeArgs a{};
     a.q[0] = q1;
@@ -423,7 +423,7 @@ int diff_attn_decode(const void *q1, const void *k1_ring, const void *q2, const 
 }
 
 int diff_attn_fwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
-                  void *out, swa_dtype_t dt, int B, int Hq, int Hkv, int N, int d, int dv,
+                  void *out, int dt, int B, int Hq, int Hkv, int N, int d, int dv,
                   int window, int stride, int dilation, int n_global, float scale, float lambda,
                   const swa_block_mask_t *mask, hipStream_t stream) {
     if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) ||

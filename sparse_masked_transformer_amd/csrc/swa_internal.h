@@ -30,7 +30,7 @@ static_assert(kF32BM * kF32TPR == kFwdThreads, "fp32 forward tile = one 256-lane
 constexpr int64_t kMaxGridItems = 0xffffffffLL;
 
 // Query tile rows of the kernel serving (op, dtype).
-inline int tile_rows(swa_op_t op, swa_dtype_t dt) {
+inline int tile_rows(int op, int dt) {
     if (dt == SWA_F32)
         return kF32BM;
     return 128 * (op == SWA_OP_DIFF ? kDiffRowGroups : kFwdRowGroups);
@@ -64,17 +64,17 @@ struct FwdArgs {
 // global tokens) walks each residue class of the rows mod dilation as a dense
 // band: one workgroup per (batch, head, residue class, class-local tile).
 // Every other forward has one workgroup per (batch, head, query tile).
-inline bool fwd_by_residue_class(const FwdArgs &a, swa_dtype_t dt) {
+inline bool fwd_by_residue_class(const FwdArgs &a, int dt) {
     return dt == SWA_BF16 && a.nmaps == 1 && a.dilation > 1 && a.stride == 0 && a.n_global == 0;
 }
 
 // Lanes per workgroup of the forward launch for (a, dt).
-inline int fwd_threads(const FwdArgs &a, swa_dtype_t dt) {
+inline int fwd_threads(const FwdArgs &a, int dt) {
     return dt == SWA_BF16 && a.nmaps == 2 ? kDiffFwdThreads : kFwdThreads;
 }
 
 // Workgroups of the forward launch for (a, dt).
-inline int64_t fwd_workgroups(const FwdArgs &a, swa_dtype_t dt) {
+inline int64_t fwd_workgroups(const FwdArgs &a, int dt) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hq;
     if (fwd_by_residue_class(a, dt)) {
         const int64_t bm = 128 * kFwdRowGroups;
@@ -133,7 +133,7 @@ inline DecodePlan decode_plan_for(const DecodeArgs &a) {
     return decode_plan(a.B, a.Hkv * decode_head_blocks(a.Hq, a.Hkv), a.window + a.n_sink);
 }
 // Work-items of the largest dispatch one decode call makes.
-int64_t decode_launch_items(const DecodeArgs &a, swa_dtype_t dt);
+int64_t decode_launch_items(const DecodeArgs &a, int dt);
 // fp32 count of the (max, sum) section of the decode workspace for `parts`
 // partial results, padded so the output section starts 16-byte aligned.
 inline int64_t decode_ws_ml_floats(int64_t parts) { return (parts * 2 + 3) / 4 * 4; }

@@ -24,6 +24,15 @@ FAKE = 0x7F0000000000  # 16-byte aligned; never dereferenced by a rejected call
 
 @pytest.fixture(scope="module")
 def swa():
+    other = os.environ.get("SWA_ABI_LIBRARY")
+    if other:
+        # another build of the library (the sanitizer run): its host surface
+        # through the ctypes layer alone, without PyTorch
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("swa_abi_layer", os.path.join(PKG, "_abi.py"))
+        m = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(m)
+        return m.namespace(m.configure(ctypes.CDLL(other)), other)
     if not os.path.exists(os.path.join(PKG, "libswa.so")):
         subprocess.run([sys.executable, os.path.join(PKG, "build.py")], check=True)
     import sparse_masked_transformer_amd as m
