@@ -131,7 +131,12 @@ typedef struct {
 int swa_tile_config(int op, int dt, int d, int dv, int32_t *bm, int32_t *bn);
 
 /* Number of query tiles and list entries of the block mask of
- * (N, window, stride, dilation, n_global, bm, bn).  Host only, no HIP call.
+ * (N, window, stride, dilation, n_global, bm, bn): the sizes of the arrays
+ * swa_block_mask_build fills (the per-query-tile key-tile lists of the
+ * band, stride, dilation and global-token patterns; sparsity as which
+ * (query, key) pairs are scored, Learn: Sparse & Sliding-Window Attention,
+ * §3, tiled as in the "Flash style softmax" task of "Attention Variants
+ * Compared").  Host only, no HIP call.
  * N in [1, SWA_MAX_N], window >= 1, stride >= 0 (0 = no stride pattern),
  * dilation in [1, bn] (so every tile of a band holds an attended cell),
  * n_global in [0, SWA_MAX_N], bm, bn in {16, 32, 64, 128, 256}. */
@@ -143,8 +148,12 @@ int swa_block_mask_query(int N, int window, int stride, int dilation, int n_glob
  * result is bit-exact. */
 int swa_block_mask_build(const swa_block_mask_t *mask, hipStream_t stream);
 
-/* Debug export of the dense mask: out[i*N + j] = 1 if query i attends key j,
- * else 0, for N <= 16384 (device array of N*N bytes). */
+/* Debug export of the dense mask M of Learn: Sparse & Sliding-Window
+ * Attention, §3 (the swa_mask / strided_mask matrices of "Attention Variants
+ * Compared", OR'd with the dilation and global-token patterns):
+ * out[i*N + j] = 1 if query i attends key j, else 0, for N <= 16384 (device
+ * array of N*N bytes).  Not on the hot path; the tests compare it with the
+ * oracle bit for bit. */
 int swa_mask_dense(int N, int window, int stride, int dilation, int n_global, uint8_t *out,
                    hipStream_t stream);
 
@@ -221,9 +230,10 @@ int swa_attn_decode_sinks(const void *q, const void *k_sink, const void *v_sink,
 /*
  * Differential-attention decode step over a rolling window ("Attention
  * Variants — Sliding Window, Sparse, Differential": two maps from separate
- * query/key projections, the second subtracted with weight lambda; the same
- * page notes that reading the value cache twice slows decoding, so V is read
- * once for both maps):
+ * query/key projections, the second subtracted with weight lambda).  The
+ * symptom/cause/fix table of "Attention Variants Compared" lists a
+ * differential decode that loads the value cache twice as slower than the
+ * baseline, so V is read once for both maps:
  *
  *   out = softmax(q1 K1^T * scale) V - lambda * softmax(q2 K2^T * scale) V
  *

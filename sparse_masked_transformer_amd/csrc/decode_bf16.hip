@@ -7,7 +7,9 @@
 // and is bound by HBM bandwidth; StreamingLLM (same page, §4) also keeps the
 // first few tokens in sink slots.  Attention Variants — Sliding Window,
 // Sparse, Differential, "Differential attention": two maps share one value
-// cache, which must not be read twice (each K and V byte is read once here).
+// cache; the symptom/cause/fix table of "Attention Variants Compared" lists
+// a differential decode that loads the value cache twice as slower than the
+// baseline (each K and V byte is read once here).
 //
 // A sequence's cache is walked as one list of "virtual slots": first the
 // sink slots that the ring no longer covers, then the valid ring slots
