@@ -9,13 +9,20 @@ same page): running maximum, running sum and running weighted sum per query
 row while the key tiles of the window stream through LDS.
 
 Work decomposition
-  Workgroup = 8 waves on the 4 query heads h0 .. h0+3 of one key/value head
-  (grouped-query attention) and the same 64 query rows: wave w takes head
+  Item = the 4 query heads h0 .. h0+3 of one key/value head (grouped-query
+  attention) on the same 64 query rows; its 8 waves: wave w takes head
   h0 + (w & 3) and rows 32 (w >> 2) .. +31 of the block, so the K and V
   tiles staged in LDS serve all four heads and every wave needs the same key
   tiles (the band of the 64 rows).  One workgroup per CU (LDS holds four
   64-key stages), two waves per SIMD: while one wave waits on a dependency
   or an LDS read, the other issues.
+  Persistent grid: workgroup g takes items g, g + grid, g + 2 grid, ...
+  (grid a multiple of 8, so all of them run on one XCD, whose items are a
+  contiguous run of row blocks of one head: neighbouring bands share K and
+  V tiles in that XCD's L2).  In the last step of an item the workgroup
+  already loads the next item's Q fragments and first two tiles, into the
+  two stages the current item no longer reads; the output of the current
+  item is staged through the stage of its last-but-one tile.
 
 Registers (256 per lane: 128 VGPRs + 128 AGPRs, two waves per SIMD)
   AGPR  a[0:63]     O^T accumulators, 4 blocks of 32 values
@@ -64,6 +71,9 @@ NSTAGE = 4
 LDS_BYTES = NSTAGE * STAGE    # 151552
 KCH, VCH = KTILE // 1024, VTILE // 1024   # 17, 20 chunks of 1 KiB
 SLACK = 8.0
+OROW = 144                    # LDS row of the output staging (half a row of values + 16)
+EPI_STORES = 8                # output stores of an item's epilogue (the log-sum-exp store aside)
+assert 8 * 32 * OROW <= STAGE
 KARG_BYTES = 80
 NAME = "swa_fwd_gqa_d128"
 
@@ -213,11 +223,14 @@ class Prog:
         self.add(I(f"  {op} {dst}, {addr} offset:{off}", "lds", addr.regs(), dst.regs(), lds_read=True,
                    dests=dst.regs()))
 
-    def buf_load(self, dst, voff, rsrc, soff, off=0):
+    def buf_load(self, dst, voff, rsrc, soff, off=0, track=True):
+        """track=False: no automatic wait before the destination's readers
+        (the caller places an explicit s_waitcnt; the load may then stay in
+        flight across labels and branches)."""
         o = f" offset:{off}" if off else ""
         self.add(I(f"  buffer_load_dwordx4 {dst}, {voff}, {rsrc}, {soff} offen{o}", "vmem",
                    regs_of(voff, rsrc, soff if isinstance(soff, R) else None), dst.regs(), vm_load=True,
-                   dests=dst.regs()))
+                   dests=dst.regs() if track else EMPTY))
 
     def dma(self, voff, rsrc, soff):
         self.add(I(f"  buffer_load_dwordx4 {voff}, {rsrc}, {soff} offen lds", "dma",
@@ -443,6 +456,7 @@ V_COL, V_HL = v(102), v(103)
 V_T = [v(104 + i) for i in range(16)]  # even start: pairs of them are 64-bit tuples
 V_OWL, V_ORDL, V_OST, V_OW, V_ORD = v(120), v(121), v(122), v(123), v(124)
 V_LANE = v(125)
+V_QLANE = v(127)                     # (lane % 32) * 256 + 16 (lane / 32): Q load offset within the rows
 
 A_O = a(0, 64)                       # O^T: block db at 16 db
 A_Q = a(64, 32)                      # Q^T fragments: ks at 4 ks
@@ -455,7 +469,8 @@ S_KARG = s(0, 2)
 S_WG = s(2)
 S_Q, S_K, S_V, S_OUT, S_LSE = s(4, 2), s(6, 2), s(8, 2), s(10, 2), s(12, 2)
 S_N, S_W, S_G, S_NHB, S_NRB, S_C = s(14), s(15), s(16), s(17), s(18), s(19)
-S_TOTAL, S_HKV, S_HQ = s(20), s(21), s(22)
+S_TOTAL, S_STRIDE, S_VID = s(20), s(21), s(22)   # row-block items, items per pass (grid size), item
+S_BASE = s(3)                        # stage of the next item's first tile
 S_WH, S_WR, S_R0W = s(23), s(34), s(35)   # wave & 3 (head), wave >> 2 (row half), its first row
 S_WAVE, S_LID, S_HB, S_RB, S_BG, S_R0, S_TLO, S_T, S_J = (s(24), s(25), s(26), s(27), s(28), s(29),
                                                           s(30), s(31), s(32))
@@ -939,10 +954,14 @@ def k_addr_next(P):
 
 
 def iteration(P, phase, has_qk, has_pv, first):
-    """One tile j (S_J) of the pipeline; score buffers by phase = j % 2."""
+    """One tile j (S_J) of the pipeline; score buffers by phase = j % 2.  The
+    last step of an item (no QK product) also starts the loads of the
+    workgroup's next item."""
     sb_cur, sb_next = S_BUF[phase], S_BUF[1 - phase]
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
-    P.waitcnt(vm=0)
+    # the first step waits for tile 1 of its item, not for the previous
+    # item's output stores (the last EPI_STORES vector memory operations)
+    P.waitcnt(vm=EPI_STORES if first else 0)
     P.barrier()
     if has_pv:
         settle_previous(P)
@@ -954,6 +973,8 @@ def iteration(P, phase, has_qk, has_pv, first):
     P.label(skip)
     dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32)])
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+    if not has_qk:
+        item_loads(P, first=False)
     valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
             + v_prefetch_ops() + pack_ops(sb_cur, 1))
     extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
@@ -984,8 +1005,11 @@ def settle_previous(P):
 
 
 def epilogue(P, phase):
-    """O += V(T-1)^T P(T-1), then O / l -> bf16 rows, and the log-sum-exp."""
-    P.waitcnt(vm=0)
+    """O += V(T-1)^T P(T-1), then O / l -> bf16 rows, and the log-sum-exp.
+    Ends the workgroup, or goes on with its next item (whose loads are in
+    flight)."""
+    # (the next item's loads are not waited for: the barrier only orders
+    # this item's last reads of the stage the output is staged in)
     P.barrier()
     settle_previous(P)
     interleave(P, mfma_order(False, True), None, [], v_ready=AHEAD)
@@ -1006,44 +1030,179 @@ def epilogue(P, phase):
     P.valu("v_mul_f32", l2, "0x3f317218", l2)
     P.buf_store("buffer_store_dword", l2, V_LOFF, S_RSL)
     P.label(skip)
-    # O / l -> bf16, staged through LDS so the global stores are whole rows
-    # (16 lanes x 16 bytes per 256-byte row) instead of 8-byte pieces of 32
-    # rows.  Each wave uses its own 32 x 272-byte region in the two stages
-    # that do not hold the last V tile (the only one other waves may still
-    # read): stages 0-1 if that tile is in stage 2 or 3, else stages 2-3.
-    P.salu("s_and_b32", S_X[0], S_J, "3")
-    P.scmp("s_cmp_ge_u32", S_X[0], "2")
-    P.salu("s_cselect_b32", S_X[1], "0", str(2 * STAGE), reads_scc=True, writes_scc=False)
-    P.salu("s_mul_i32", S_X[2], S_WAVE, str(32 * KROW))
-    P.salu("s_add_u32", S_X[1], S_X[1], S_X[2])                    # this wave's region
+    # O / l -> bf16, staged through LDS so the global stores are 128-byte
+    # runs of rows instead of 8-byte pieces of 32 rows.  The staging area is
+    # the stage of tile T-2 (no wave reads it after the barrier above; the
+    # stage of tile T-1 is still being read and the next two hold the next
+    # item's first tiles): 8 waves x 32 rows x 144 bytes, half a row at a
+    # time (values 0..63, then 64..127).
+    P.salu("s_add_u32", S_X[0], S_J, "-1")
+    P.salu("s_and_b32", S_X[0], S_X[0], "3")
+    P.salu("s_mul_i32", S_X[0], S_X[0], str(STAGE))
+    P.salu("s_mul_i32", S_X[2], S_WAVE, str(32 * OROW))
+    P.salu("s_add_u32", S_X[1], S_X[0], S_X[2])                    # this wave's region
     P.valu("v_add_u32", V_OW, S_X[1], V_OWL)
     P.valu("v_add_u32", V_ORD, S_X[1], V_ORDL)
-    for db in range(4):
-        for r4 in range(4):
-            x = [t[4 + k] for k in range(4)]
-            for k in range(4):
-                P.add(I(f"  v_accvgpr_read_b32 {x[k]}, {A_O.sub(16 * db + 4 * r4 + k)}", "valu",
-                        A_O.sub(16 * db + 4 * r4 + k).regs(), x[k].regs()))
-            for k in range(4):
-                P.valu("v_mul_f32", x[k], x[k], inv)
-            pk0, pk1 = t[8 + 2 * (r4 % 2)], t[9 + 2 * (r4 % 2)]
-            P.valu("v_cvt_pk_bf16_f32", pk0, x[0], x[1])
-            P.valu("v_cvt_pk_bf16_f32", pk1, x[2], x[3])
-            # row col, values 32 db + 8 r4 + 4 hl .. +3
-            P.add(I(f"  ds_write_b64 {V_OW}, {v(pk0.i, 2)} offset:{db * 64 + r4 * 16}", "lds",
-                    regs_of(V_OW, v(pk0.i, 2)), EMPTY))
-    ob = S_BUF[0]                                                   # free score buffer
-
-    def rd(kk):
-        # rows 4 kk + lane / 16, bytes 16 (lane % 16) .. +15 of each
-        P.ds_read("ds_read_b128", v(ob + 4 * kk, 4), V_ORD, kk * 4 * KROW)
-    for kk in range(8):
-        rd(kk)
-    for kk in range(8):
-        P.salu("s_mov_b32", S_X[3 + (kk % 4)], str(kk * 1024), writes_scc=False)
-        P.add(I(f"  buffer_store_dwordx4 {v(ob + 4 * kk, 4)}, {V_OST}, {S_RSO}, {S_X[3 + (kk % 4)]} offen",
-                "vstore", regs_of(v(ob + 4 * kk, 4), V_OST, S_RSO, S_X[3 + (kk % 4)]), EMPTY))
+    for half in range(2):
+        for db in (2 * half, 2 * half + 1):
+            for r4 in range(4):
+                x = [t[4 + k] for k in range(4)]
+                for k in range(4):
+                    P.add(I(f"  v_accvgpr_read_b32 {x[k]}, {A_O.sub(16 * db + 4 * r4 + k)}", "valu",
+                            A_O.sub(16 * db + 4 * r4 + k).regs(), x[k].regs()))
+                for k in range(4):
+                    P.valu("v_mul_f32", x[k], x[k], inv)
+                pk0, pk1 = t[8 + 2 * (r4 % 2)], t[9 + 2 * (r4 % 2)]
+                P.valu("v_cvt_pk_bf16_f32", pk0, x[0], x[1])
+                P.valu("v_cvt_pk_bf16_f32", pk1, x[2], x[3])
+                # row col, values 32 db + 8 r4 + 4 hl .. +3
+                P.add(I(f"  ds_write_b64 {V_OW}, {v(pk0.i, 2)} offset:{(db - 2 * half) * 64 + r4 * 16}",
+                        "lds", regs_of(V_OW, v(pk0.i, 2)), EMPTY))
+        # rows 8 kk + lane / 8, bytes 16 (lane % 8) .. +15 of the half row
+        # (the next half's writes follow these reads: LDS operations of a
+        # wave execute in order)
+        ob = S_BUF[0] + 16 * half                                   # free score buffer
+        for kk in range(4):
+            P.ds_read("ds_read_b128", v(ob + 4 * kk, 4), V_ORD, kk * 8 * OROW)
+        for kk in range(4):
+            P.salu("s_mov_b32", S_X[3 + kk], str(kk * 8 * 256 + half * 128), writes_scc=False)
+            P.add(I(f"  buffer_store_dwordx4 {v(ob + 4 * kk, 4)}, {V_OST}, {S_RSO}, {S_X[3 + kk]} offen",
+                    "vstore", regs_of(v(ob + 4 * kk, 4), V_OST, S_RSO, S_X[3 + kk]), EMPTY))
+    P.scmp("s_cmp_lt_u32", S_VID, S_TOTAL)
+    P.branch("s_cbranch_scc1", ".Litem")
     P.add(I("  s_endpgm", "branch"))
+
+
+def query_head(P, dst):
+    """dst = bg * G + 4 hb + (wave & 3): this wave's query head."""
+    P.salu("s_mul_i32", dst, S_BG, S_G)
+    P.salu("s_lshl_b32", S_X[8], S_HB, "2")
+    P.salu("s_add_u32", dst, dst, S_X[8])
+    P.salu("s_add_u32", dst, dst, S_WH)
+
+
+def item_loads(P, first):
+    """Start the workgroup's next item (S_VID + S_STRIDE; S_VID itself for
+    the first): its row block, band and K, V, Q descriptors, then the loads
+    of its Q fragments and of its tiles 0 and 1 into stages S_J + 1 and
+    S_J + 2 (mod 4), which no wave reads any more once the last step of the
+    current item has begun.  Nothing here waits for these loads.  The
+    item's step counter then starts at S_BASE = (S_J + 1) & 3, so tile t
+    of every item is in stage (S_BASE + t) & 3."""
+    skip = None
+    if not first:
+        P.salu("s_add_u32", S_VID, S_VID, S_STRIDE)
+        P.scmp("s_cmp_ge_u32", S_VID, S_TOTAL)
+        skip = P.new_label("nonext")
+        P.branch("s_cbranch_scc1", skip)
+    P.salu("s_add_u32", S_BASE, S_J, "1")
+    P.salu("s_and_b32", S_BASE, S_BASE, "3")
+    # item -> logical id: items i, i + 8, ... (the workgroup's own id and its
+    # steps by the grid size, a multiple of 8) run on XCD i % 8, which takes a
+    # contiguous run of logical ids
+    P.salu("s_and_b32", S_X[0], S_TOTAL, "7")
+    P.salu("s_and_b32", S_X[1], S_VID, "7")
+    P.salu("s_lshr_b32", S_X[2], S_TOTAL, "3")
+    P.salu("s_mul_i32", S_X[1], S_X[1], S_X[2])
+    P.salu("s_lshr_b32", S_X[3], S_VID, "3")
+    P.salu("s_add_u32", S_X[1], S_X[1], S_X[3])
+    P.scmp("s_cmp_eq_u32", S_X[0], "0")
+    P.salu("s_cselect_b32", S_LID, S_X[1], S_VID, reads_scc=True, writes_scc=False)
+    # lid -> (head block, row block, batch * kv head), row blocks ascending
+    udiv(P, S_LID, S_NHB, S_X[4], S_HB, V_T[1], V_T[2])        # S_X[4] = rest
+    udiv(P, S_X[4], S_NRB, S_BG, S_RB, V_T[1], V_T[2])         # row block
+    P.salu("s_lshl_b32", S_R0, S_RB, "6")
+    P.salu("s_lshl_b32", S_R0W, S_WR, "5")
+    P.salu("s_add_u32", S_R0W, S_R0W, S_R0)                    # this wave's first row
+    # band of rows r0 .. r0+63: key tiles t_lo .. t_hi
+    P.salu("s_sub_i32", S_X[0], S_R0, S_W)
+    P.salu("s_add_i32", S_X[0], S_X[0], "1")
+    P.salu("s_max_i32", S_X[0], S_X[0], "0")
+    P.salu("s_lshr_b32", S_TLO, S_X[0], "6")
+    P.salu("s_add_u32", S_X[1], S_R0, "63")
+    P.salu("s_sub_u32", S_X[2], S_N, "1")
+    P.salu("s_min_u32", S_X[1], S_X[1], S_X[2])
+    P.salu("s_lshr_b32", S_X[1], S_X[1], "6")
+    P.salu("s_sub_u32", S_T, S_X[1], S_TLO)
+    P.salu("s_add_u32", S_T, S_T, "1")
+    # descriptors
+    P.salu("s_lshl_b32", S_X[6], S_N, "8")                     # bytes per head (N rows of 256 B)
+    rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[6])
+    rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
+    query_head(P, S_X[7])
+    rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
+    # Q fragments
+    P.salu("s_lshl_b32", S_X[9], S_R0W, "8")
+    P.valu("v_add_u32", V_QOFF, S_X[9], V_QLANE)
+    for ks in range(8):
+        P.buf_load(A_Q.sub(4 * ks, 4), V_QOFF, S_RSQ, "0", 32 * ks, track=False)
+    # tiles 0 and 1 (tile 1 also when the band has one tile: its rows are
+    # read, or are past N and read as zeros, and never used)
+    P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
+    P.salu("s_mul_i32", S_SB, S_BASE, str(STAGE))
+    dma_tile(P)
+    P.salu("s_add_u32", S_SOFF, S_SOFF, str(1 << 14))
+    P.salu("s_add_u32", S_X[0], S_BASE, "1")
+    P.salu("s_and_b32", S_X[0], S_X[0], "3")
+    P.salu("s_mul_i32", S_SB, S_X[0], str(STAGE))
+    dma_tile(P)
+    # step counter from S_BASE: first tile and band end shifted to match
+    P.salu("s_sub_u32", S_TLO, S_TLO, S_BASE)
+    P.salu("s_add_u32", S_T, S_T, S_BASE)
+    if skip:
+        P.label(skip)
+
+
+def item_start(P):
+    """Set-up of an item once the previous one's epilogue is issued: output
+    descriptors, the row-dependent lane offsets, the softmax state and the
+    scalar set-up of step 0; then, with Q and tile 0 in, S(0) = K(0) Q^T."""
+    P.label(".Litem")
+    P.salu("s_lshl_b32", S_X[6], S_N, "8")
+    query_head(P, S_X[7])
+    rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[6])
+    P.salu("s_lshl_b32", S_X[9], S_N, "2")
+    rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[9])
+    P.salu("s_add_u32", S_R0W32, S_R0W, "32")
+    t = V_T
+    P.valu("v_add_u32", t[5], S_R0W, V_COL)                    # row
+    P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
+    P.valu("v_lshlrev_b32", t[7], "2", V_HL)
+    P.valu("v_sub_u32", V_IBASE, t[5], t[7])
+    # output store offset: row r0w + lane / 8, bytes 16 (lane % 8) of a half row
+    P.valu("v_lshrrev_b32", t[0], "3", V_LANE)
+    P.valu("v_add_u32", t[0], S_R0W, t[0])
+    P.valu("v_lshlrev_b32", t[0], "8", t[0])
+    P.valu("v_and_b32", t[1], "7", V_LANE)
+    P.valu("v_lshlrev_b32", t[1], "4", t[1])
+    P.valu("v_add_u32", V_OST, t[0], t[1])
+    # softmax state
+    P.valu("v_mov_b32", V_M, "0xf149f2ca")             # -1e30
+    P.valu("v_mov_b32", V_MTHR, "0xf149f2ca")
+    for k in range(2):
+        P.valu("v_mov_b32", V_L[k], "0")
+    for k in range(64):
+        P.add(I(f"  v_accvgpr_write_b32 {A_O.sub(k)}, 0", "valu", EMPTY, A_O.sub(k).regs()))
+    # set-up of step 0 (as if from a step j = -1)
+    P.salu("s_sub_u32", S_J, S_BASE, "1")
+    for op in setup_ops(0):
+        op(P)
+    # Q and tile 0 in: all but tile 1's loads and the previous item's output
+    # stores, issued after them
+    P.waitcnt(vm=len(dma_ops()) + EPI_STORES)
+    P.barrier()
+    # S(0) = K(0) Q^T
+    P.salu("s_mov_b32", S_J, S_BASE, writes_scc=False)
+    P.salu("s_mul_i32", S_X[12], S_BASE, str(STAGE))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    dump_lds(P, "lds0", STAGE)
+    dump(P, "q", [A_Q])
+    interleave(P, mfma_order(True, False), S_BUF[0], [])
+    P.salu("s_add_u32", S_X[12], S_BASE, "1")                  # QK(1) reads the next stage
+    P.salu("s_and_b32", S_X[12], S_X[12], "3")
+    P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    dump(P, "s0", [v(S_BUF[0], 32)])
 
 
 def prologue(P):
@@ -1068,59 +1227,14 @@ def prologue(P):
         P.salu("s_lshl_b32", S_DBGG, S_WG, "3")
         P.salu("s_add_u32", S_DBGG, S_DBGG, S_WAVE)
         P.valu("v_lshlrev_b32", V_DBGL, "2", V_LANE)
-    # workgroup -> logical id: consecutive ids go to the 8 XCDs in turn; each
-    # XCD gets a contiguous run of logical ids
-    P.salu("s_and_b32", S_X[0], S_TOTAL, "7")
-    P.salu("s_and_b32", S_X[1], S_WG, "7")
-    P.salu("s_lshr_b32", S_X[2], S_TOTAL, "3")
-    P.salu("s_mul_i32", S_X[1], S_X[1], S_X[2])
-    P.salu("s_lshr_b32", S_X[3], S_WG, "3")
-    P.salu("s_add_u32", S_X[1], S_X[1], S_X[3])
-    P.scmp("s_cmp_eq_u32", S_X[0], "0")
-    P.salu("s_cselect_b32", S_LID, S_X[1], S_WG, reads_scc=True, writes_scc=False)
-    # lid -> (head block, row block, batch * kv head).  Row blocks in
-    # ascending order: the first blocks of a head have short bands, so the
-    # first workgroups on the CUs end at different times and the later ones'
-    # loads and stores do not all hit memory at once
-    udiv(P, S_LID, S_NHB, S_X[4], S_HB, V_T[1], V_T[2])        # S_X[4] = rest
-    udiv(P, S_X[4], S_NRB, S_BG, S_RB, V_T[1], V_T[2])         # row block
-    P.salu("s_lshl_b32", S_R0, S_RB, "6")
-    done = ".Ldone"
-    P.scmp("s_cmp_ge_u32", S_R0, S_N)
-    P.branch("s_cbranch_scc1", done)
-    P.salu("s_lshl_b32", S_R0W, S_WR, "5")
-    P.salu("s_add_u32", S_R0W, S_R0W, S_R0)                    # this wave's first row
-    P.salu("s_add_u32", S_R0W32, S_R0W, "32")
-    # band of rows r0 .. r0+63: key tiles t_lo .. t_hi
-    P.salu("s_sub_i32", S_X[0], S_R0, S_W)
-    P.salu("s_add_i32", S_X[0], S_X[0], "1")
-    P.salu("s_max_i32", S_X[0], S_X[0], "0")
-    P.salu("s_lshr_b32", S_TLO, S_X[0], "6")
-    P.salu("s_add_u32", S_X[1], S_R0, "63")
-    P.salu("s_sub_u32", S_X[2], S_N, "1")
-    P.salu("s_min_u32", S_X[1], S_X[1], S_X[2])
-    P.salu("s_lshr_b32", S_X[1], S_X[1], "6")
-    P.salu("s_sub_u32", S_T, S_X[1], S_TLO)
-    P.salu("s_add_u32", S_T, S_T, "1")
-    # descriptors
-    P.salu("s_lshl_b32", S_X[6], S_N, "8")                     # bytes per head (N rows of 256 B)
-    rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[6])
-    rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
-    P.salu("s_mul_i32", S_X[7], S_BG, S_G)                     # query head = bg * G + 4 hb + (wave & 3)
-    P.salu("s_lshl_b32", S_X[8], S_HB, "2")
-    P.salu("s_add_u32", S_X[7], S_X[7], S_X[8])
-    P.salu("s_add_u32", S_X[7], S_X[7], S_WH)
-    rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
-    rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[6])
-    P.salu("s_lshl_b32", S_X[9], S_N, "2")
-    rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[9])
+    P.salu("s_mov_b32", S_VID, S_WG, writes_scc=False)
     P.salu("s_lshl_b32", S_WAVE1K, S_WAVE, "10")
     P.salu("s_lshl_b32", S_WAVE1K3, S_WH, "10")
     P.salu("s_lshl_b32", S_NB, S_N, "8")
     P.salu("s_sub_u32", S_WM1, S_W, "1")
     P.salu("s_mov_b32", S_NINF, "0xff800000", writes_scc=False)
     P.salu("s_mov_b32", S_ONES, "0x3f803f80", writes_scc=False)
-    # per-lane addressing
+    # per-lane addressing (the same for every item)
     t = V_T
     P.valu("v_mul_u32_u24", V_KLANE, str(KROW), V_COL)
     P.valu("v_lshlrev_b32", t[0], "4", V_HL)
@@ -1139,26 +1253,20 @@ def prologue(P):
     P.valu("v_add_u32", t[2], t[2], t[3])
     P.valu("v_add_u32", t[2], t[2], t[4])
     P.valu("v_add_u32", V_VLANE, str(KTILE), t[2])
-    P.valu("v_add_u32", t[5], S_R0W, V_COL)                    # row
-    P.valu("v_lshlrev_b32", t[6], "8", t[5])                   # row * 256
-    P.valu("v_lshlrev_b32", t[7], "4", V_HL)
-    P.valu("v_add_u32", V_QOFF, t[6], t[7])
-    P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
-    P.valu("v_lshlrev_b32", t[7], "2", V_HL)
-    P.valu("v_sub_u32", V_IBASE, t[5], t[7])
-    # epilogue: LDS write base (row col, values 4 hl: col * 272 + 8 hl), LDS
-    # read base (row lane / 16, bytes 16 (lane % 16)), global store offset
-    P.valu("v_mul_u32_u24", V_OWL, str(KROW), V_COL)
+    # Q rows: row col of the wave's 32, bytes 16 hl of each 32-byte group
+    P.valu("v_lshlrev_b32", t[0], "8", V_COL)
+    P.valu("v_lshlrev_b32", t[1], "4", V_HL)
+    P.valu("v_add_u32", V_QLANE, t[0], t[1])
+    # output staging: LDS write base (row col, values 4 hl: col * 144 +
+    # 8 hl), LDS read base (row lane / 8, bytes 16 (lane % 8))
+    P.valu("v_mul_u32_u24", V_OWL, str(OROW), V_COL)
     P.valu("v_lshlrev_b32", t[0], "3", V_HL)
     P.valu("v_add_u32", V_OWL, V_OWL, t[0])
-    P.valu("v_lshrrev_b32", t[0], "4", V_LANE)
-    P.valu("v_and_b32", t[1], "15", V_LANE)
+    P.valu("v_lshrrev_b32", t[0], "3", V_LANE)
+    P.valu("v_and_b32", t[1], "7", V_LANE)
     P.valu("v_lshlrev_b32", t[1], "4", t[1])
-    P.valu("v_mul_u32_u24", V_ORDL, str(KROW), t[0])
+    P.valu("v_mul_u32_u24", V_ORDL, str(OROW), t[0])
     P.valu("v_add_u32", V_ORDL, V_ORDL, t[1])
-    P.valu("v_add_u32", t[0], S_R0W, t[0])
-    P.valu("v_lshlrev_b32", t[0], "8", t[0])
-    P.valu("v_add_u32", V_OST, t[0], t[1])
     # DMA lane offsets: K chunks wave + 8 jk (jk < 2) and 16, V chunks
     # wave + 8 jv (jv < 2) and 16 + (wave & 3)
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
@@ -1179,38 +1287,10 @@ def prologue(P):
             P.valu("v_add_u32", t[10], t[13], t[8])
             P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
         _chunk_src(P, V_DV[jv], t[10], M320, VROW, t)
-    # softmax state
-    P.valu("v_mov_b32", V_M, "0xf149f2ca")             # -1e30
-    P.valu("v_mov_b32", V_MTHR, "0xf149f2ca")
-    for k in range(2):
-        P.valu("v_mov_b32", V_L[k], "0")
-    for k in range(64):
-        P.add(I(f"  v_accvgpr_write_b32 {A_O.sub(k)}, 0", "valu", EMPTY, A_O.sub(k).regs()))
-    # Q fragments
-    for ks in range(8):
-        P.buf_load(A_Q.sub(4 * ks, 4), V_QOFF, S_RSQ, "0", 32 * ks)
-    # stage tiles 0 and 1 (tile 1 also when the band has one tile: its rows
-    # are read, or are past N and read as zeros, and never used)
-    P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
-    P.salu("s_mov_b32", S_SB, "0", writes_scc=False)
-    dma_tile(P)
-    P.salu("s_add_u32", S_SOFF, S_SOFF, str(1 << 14))
-    P.salu("s_mov_b32", S_SB, str(STAGE), writes_scc=False)
-    dma_tile(P)
-    # set-up of iteration 0 (as if from an iteration j = -1)
+    # the first item's loads (stage base 0), all of them in before its set-up
     P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
-    for op in setup_ops(0):
-        op(P)
-    P.waitcnt(vm=len(dma_ops()))
-    P.barrier()
-    # S(0) = K(0) Q^T
-    P.salu("s_mov_b32", S_J, "0", writes_scc=False)
-    P.valu("v_add_u32", V_KADDR, "0", V_KLANE)
-    dump_lds(P, "lds0", STAGE)
-    dump(P, "q", [A_Q])
-    interleave(P, mfma_order(True, False), S_BUF[0], [])
-    P.valu("v_add_u32", V_KADDR, str(STAGE), V_KLANE)          # QK(1) reads stage 1
-    dump(P, "s0", [v(S_BUF[0], 32)])
+    item_loads(P, first=True)
+    P.waitcnt(vm=0)
 
 
 def _chunk_src(P, dst, pos, magic, rowb, t):
@@ -1230,11 +1310,13 @@ def _chunk_src(P, dst, pos, magic, rowb, t):
 def kernel_text():
     P = Prog()
     prologue(P)
+    item_start(P)
     # T == 1: softmax of S(0) only
-    P.scmp("s_cmp_le_u32", S_T, "1")
+    P.salu("s_add_u32", S_X[0], S_J, "1")
+    P.scmp("s_cmp_ge_u32", S_X[0], S_T)
     P.branch("s_cbranch_scc1", ".Lsingle")
     iteration(P, 0, True, False, True)                         # j = 0
-    P.salu("s_mov_b32", S_J, "1", writes_scc=False)
+    P.salu("s_add_u32", S_J, S_J, "1")
     P.salu("s_add_u32", S_X[0], S_J, "1")
     P.scmp("s_cmp_ge_u32", S_X[0], S_T)
     P.branch("s_cbranch_scc1", ".Llast1")
@@ -1253,15 +1335,9 @@ def kernel_text():
     P.label(".Lsingle")
     iteration(P, 0, False, False, True)
     epilogue(P, 0)
-    P.label(done_label())
-    P.add(I("  s_endpgm", "branch"))
     body = resolve(P.ins)
     lines = [x.text for x in body]
     return "\n".join(lines)
-
-
-def done_label():
-    return ".Ldone"
 
 
 def render():

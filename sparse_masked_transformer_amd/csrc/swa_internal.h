@@ -151,7 +151,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 // heads per key/value head): whether it serves `a`, its workgroup count,
 // and its launch.
 bool fwd_gqa_applies(const FwdArgs &a);
-int64_t fwd_gqa_workgroups(const FwdArgs &a);
+int64_t fwd_gqa_items(const FwdArgs &a);
 hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);

@@ -2,8 +2,9 @@
 assembly kernel that serves bf16, d = 128, window-only problems with a
 multiple of 4 query heads per key/value head) against the fp64 oracle.
 
-The kernel walks 64-row halves of the 128-row query tiles, one workgroup per
-4 query heads of a key/value head; the cases cover one-tile bands, ragged
+The kernel works on items of 64 query rows of 4 query heads of a key/value
+head, a workgroup per compute unit taking items in turn; the cases cover
+one-tile bands, chains of several items per workgroup, ragged
 sequence ends (rows and keys past N), windows at and around the 64-key tile
 size, windows beyond N, several head blocks per key/value head, batches,
 peaky scores that move the running maximum late, the log-sum-exp output, and
@@ -70,6 +71,14 @@ CASES = [
     (1, 4, 1, 4097, 1024),
     (2, 16, 2, 2100, 700),
     (1, 4, 1, 3000, 2),
+    # more items (row blocks x head blocks) than compute units: a workgroup
+    # takes several in turn, each item's first loads overlapping the
+    # previous item's last step and output
+    (8, 64, 16, 200, 64),       # 512 items, bands of 1 and 2 tiles
+    (16, 32, 8, 130, 100),      # 384 items, bands of 1 to 3 tiles
+    (4, 64, 16, 700, 300),      # 704 items, bands of 1 to 6 tiles
+    (2, 32, 8, 2500, 200),      # 640 items
+    (3, 36, 9, 650, 100),       # 297 items: not a multiple of 8
 ]
 
 
