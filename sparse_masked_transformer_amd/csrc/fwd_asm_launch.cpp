@@ -1,0 +1,181 @@
+// Launch of the generated gfx950 assembly kernels: swa_fwd_gqa_d128
+// (grouped-query sliding-window forward, bf16, d = 128; gen_fwd_gqa.py) and
+// diff_fwd_d64_dv128 (differential sliding-window forward, bf16, d = 64,
+// dv = 128; gen_fwd_diff.py).  Their code objects are embedded in this
+// library (fwd_gqa_blob.cpp, fwd_diff_blob.cpp, made by the build from the
+// generated .s files) and loaded once per device.  Both run a persistent
+// grid of one 512-lane workgroup per compute unit.
+#include <mutex>
+
+#include "swa_internal.h"
+
+namespace swa {
+
+extern const unsigned char kFwdGqaCodeObject[];
+extern const size_t kFwdGqaCodeObjectSize;
+extern const unsigned char kFwdDiffCodeObject[];
+extern const size_t kFwdDiffCodeObjectSize;
+
+namespace {
+
+// Kernel arguments, in the layouts the kernels' prologues load (80 bytes).
+struct GqaArgs {
+    const void *q, *k, *v;
+    void *out;
+    float *lse;
+    int32_t N, window, G, head_blocks, row_blocks;
+    float c;
+    int32_t items, stride, Hkv, Hq;
+};
+static_assert(sizeof(GqaArgs) == 80, "kernel argument block is 80 bytes");
+
+struct DiffArgs {
+    const void *q1, *k1, *q2, *k2, *v;
+    void *out;
+    int32_t N, window, G;
+    float c;
+    float lambda;
+    int32_t items, stride, row_blocks;
+};
+static_assert(sizeof(DiffArgs) == 80, "kernel argument block is 80 bytes");
+
+constexpr int kMaxDevices = 64;
+
+enum AsmKernel { kGqa = 0, kDiff = 1, kNumAsm = 2 };
+
+// The kernel function `which` on the current device and that device's
+// compute unit count.
+hipError_t asm_function(AsmKernel which, hipFunction_t *fn, int *cus) {
+    static std::mutex mu;
+    static hipFunction_t fns[kMaxDevices][kNumAsm] = {};
+    static int cu_count[kMaxDevices] = {};
+    static const unsigned char *const images[kNumAsm] = {kFwdGqaCodeObject, kFwdDiffCodeObject};
+    static const char *const names[kNumAsm] = {"swa_fwd_gqa_d128", "diff_fwd_d64_dv128"};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cu_count[dev] == 0) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        cu_count[dev] = n;
+    }
+    if (fns[dev][which] == nullptr) {
+        hipModule_t mod = nullptr;
+        e = hipModuleLoadData(&mod, images[which]);
+        if (e != hipSuccess)
+            return e;
+        hipFunction_t f = nullptr;
+        e = hipModuleGetFunction(&f, mod, names[which]);
+        if (e != hipSuccess)
+            return e;
+        fns[dev][which] = f;
+    }
+    *fn = fns[dev][which];
+    *cus = cu_count[dev];
+    return hipSuccess;
+}
+
+// Persistent grid: one workgroup per compute unit (the kernels' LDS allows
+// one), each taking items g, g + grid, ...  A grid that is a multiple of 8
+// keeps every item of a workgroup on its XCD's contiguous run of items.
+int32_t persistent_grid(int64_t items, int cus) {
+    const int64_t per_pass = cus >= 8 ? cus - cus % 8 : items;
+    return static_cast<int32_t>(items < per_pass ? items : per_pass);
+}
+
+hipError_t launch(hipFunction_t fn, void *args, size_t size, int32_t grid, hipStream_t stream) {
+    void *config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, args, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
+                      HIP_LAUNCH_PARAM_END};
+    hipError_t e = hipModuleLaunchKernel(fn, static_cast<unsigned>(grid), 1, 1, 512, 1, 1, 0, stream,
+                                         nullptr, config);
+    if (e != hipSuccess)
+        return e;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_gqa_applies(const FwdArgs &a) {
+    return a.nmaps == 1 && a.d == 128 && a.dv == 128 && a.stride == 0 && a.dilation == 1 &&
+           a.n_global == 0 && (a.Hq / a.Hkv) % 4 == 0;
+}
+
+int64_t fwd_gqa_items(const FwdArgs &a) {
+    // one item per (batch, key/value head, block of 4 query heads, block of
+    // 64 query rows)
+    return static_cast<int64_t>(a.B) * a.Hkv * ((a.Hq / a.Hkv) / 4) * ((a.N + 63) / 64);
+}
+
+hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
+    hipFunction_t fn = nullptr;
+    int cus = 0;
+    hipError_t e = asm_function(kGqa, &fn, &cus);
+    if (e != hipSuccess)
+        return e;
+    GqaArgs k{};
+    k.q = a.q[0];
+    k.k = a.k[0];
+    k.v = a.v;
+    k.out = a.out;
+    k.lse = a.lse;
+    k.N = a.N;
+    // distances are < N, so a window of N or more is the full causal mask
+    k.window = a.window < a.N ? a.window : a.N;
+    k.G = a.Hq / a.Hkv;
+    k.head_blocks = k.G / 4;
+    k.row_blocks = (a.N + 63) / 64;
+    k.c = a.scale * 1.4426950408889634f;
+    const int64_t items = fwd_gqa_items(a);
+    if (items <= 0 || items > INT32_MAX)
+        return hipErrorInvalidValue;
+    k.items = static_cast<int32_t>(items);
+    k.stride = persistent_grid(items, cus);
+    k.Hkv = a.Hkv;
+    k.Hq = a.Hq;
+    return launch(fn, &k, sizeof(k), k.stride, stream);
+}
+
+bool fwd_diff_asm_applies(const FwdArgs &a) {
+    return a.nmaps == 2 && a.d == 64 && a.dv == 128 && a.stride == 0 && a.dilation == 1 &&
+           a.n_global == 0;
+}
+
+int64_t fwd_diff_asm_items(const FwdArgs &a) {
+    // one item per (batch, query head, block of 128 query rows)
+    return static_cast<int64_t>(a.B) * a.Hq * ((a.N + 127) / 128);
+}
+
+hipError_t launch_fwd_diff_asm(const FwdArgs &a, hipStream_t stream) {
+    hipFunction_t fn = nullptr;
+    int cus = 0;
+    hipError_t e = asm_function(kDiff, &fn, &cus);
+    if (e != hipSuccess)
+        return e;
+    DiffArgs k{};
+    k.q1 = a.q[0];
+    k.k1 = a.k[0];
+    k.q2 = a.q[1];
+    k.k2 = a.k[1];
+    k.v = a.v;
+    k.out = a.out;
+    k.N = a.N;
+    k.window = a.window < a.N ? a.window : a.N;
+    k.G = a.Hq / a.Hkv;
+    k.c = a.scale * 1.4426950408889634f;
+    k.lambda = a.lambda;
+    const int64_t items = fwd_diff_asm_items(a);
+    if (items <= 0 || items > INT32_MAX)
+        return hipErrorInvalidValue;
+    k.items = static_cast<int32_t>(items);
+    k.stride = persistent_grid(items, cus);
+    k.row_blocks = (a.N + 127) / 128;
+    return launch(fn, &k, sizeof(k), k.stride, stream);
+}
+
+}  // namespace swa

@@ -691,6 +691,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
     if (fwd_gqa_applies(a))
         return launch_fwd_gqa(a, stream);
+    if (fwd_diff_asm_applies(a))
+        return launch_fwd_diff_asm(a, stream);
     if (a.nmaps == 1) {
         switch (a.d) {
         case 32: return launch<32, 32, 1>(a, stream);

@@ -153,6 +153,10 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 bool fwd_gqa_applies(const FwdArgs &a);
 int64_t fwd_gqa_items(const FwdArgs &a);
 hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream);
+// The differential kernel for bf16, d = 64, dv = 128, window only.
+bool fwd_diff_asm_applies(const FwdArgs &a);
+int64_t fwd_diff_asm_items(const FwdArgs &a);
+hipError_t launch_fwd_diff_asm(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t stream);
