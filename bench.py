@@ -155,10 +155,12 @@ def dev(x, torch, dtype):
 
 
 def kernel_build_sha(kernel_src):
-    """Hash of a kernel's source together with the build script (its compiler
-    flags), the key under which its measured traffic is stored."""
+    """Hash of a kernel's source (one path, or a list of the files it is
+    generated from) together with the build script (its compiler flags),
+    the key under which its measured traffic is stored."""
     h = hashlib.sha256()
-    for f in (kernel_src, os.path.join(ROOT, "sparse_masked_transformer_amd", "build.py")):
+    srcs = [kernel_src] if isinstance(kernel_src, str) else list(kernel_src)
+    for f in srcs + [os.path.join(ROOT, "sparse_masked_transformer_amd", "build.py")]:
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -565,10 +567,12 @@ def main():
                          "roofline_frac": round(x["tflops"] / PEAK_BF16_TFLOPS, 4)}
     if "diff" in res:
         f = res["diff"]
-        line["diff"] = {"workload": "diff_bf16", "tflops": round(f["tflops"], 2),
+        line["diff"] = {"workload": "diff_bf16", "kernel": "diff_fwd_d64_dv128", "tflops": round(f["tflops"], 2),
                         "tflops_512_per_cell": round(f["tflops_formula"], 2),
                         "us": round(f["event_ms"] * 1e3, 2),
                         "roofline_frac": round(f["tflops"] / PEAK_BF16_TFLOPS, 4)}
+        if peaks:
+            line["diff"]["frac_measured"] = round(f["tflops"] / peaks["mfma_bf16_tflops"], 4)
     if "tiny_f32" in res:
         line["tiny_f32_us"] = round(res["tiny_f32"]["event_ms"] * 1e3, 2)
     print(json.dumps(line), flush=True)
