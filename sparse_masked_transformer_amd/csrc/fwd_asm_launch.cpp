@@ -1,10 +1,12 @@
 // Launch of the generated gfx950 assembly kernels: swa_fwd_gqa_d128
-// (grouped-query sliding-window forward, bf16, d = 128; gen_fwd_gqa.py) and
-// diff_fwd_d64_dv128 (differential sliding-window forward, bf16, d = 64,
-// dv = 128; gen_fwd_diff.py).  Their code objects are embedded in this
-// library (fwd_gqa_blob.cpp, fwd_diff_blob.cpp, made by the build from the
-// generated .s files) and loaded once per device.  Both run a persistent
-// grid of one 512-lane workgroup per compute unit.
+// (grouped-query sliding-window forward, bf16, d = 128; gen_fwd_gqa.py), its
+// dilated variant swa_fwd_gqa_d128_dil (each residue class of the rows mod
+// the dilation walked as a plain window), and diff_fwd_d64_dv128
+// (differential sliding-window forward, bf16, d = 64, dv = 128;
+// gen_fwd_diff.py).  Their code objects are embedded in this library
+// (fwd_gqa_blob.cpp, fwd_gqa_dil_blob.cpp, fwd_diff_blob.cpp, made by the
+// build from the generated .s files) and loaded once per device.  All run a
+// persistent grid of one 512-lane workgroup per compute unit.
 #include <mutex>
 
 #include "swa_internal.h"
@@ -13,6 +15,8 @@ namespace swa {
 
 extern const unsigned char kFwdGqaCodeObject[];
 extern const size_t kFwdGqaCodeObjectSize;
+extern const unsigned char kFwdGqaDilCodeObject[];
+extern const size_t kFwdGqaDilCodeObjectSize;
 extern const unsigned char kFwdDiffCodeObject[];
 extern const size_t kFwdDiffCodeObjectSize;
 
@@ -25,7 +29,9 @@ struct GqaArgs {
     float *lse;
     int32_t N, window, G, head_blocks, row_blocks;
     float c;
-    int32_t items, stride, Hkv, Hq;
+    int32_t items, stride;
+    int32_t dilation;   // dilated variant: the dilation r and the number of
+    int32_t classes;    // residue classes min(r, N) (unused by the plain kernel)
 };
 static_assert(sizeof(GqaArgs) == 80, "kernel argument block is 80 bytes");
 
@@ -41,7 +47,7 @@ static_assert(sizeof(DiffArgs) == 80, "kernel argument block is 80 bytes");
 
 constexpr int kMaxDevices = 64;
 
-enum AsmKernel { kGqa = 0, kDiff = 1, kNumAsm = 2 };
+enum AsmKernel { kGqa = 0, kGqaDil = 1, kDiff = 2, kNumAsm = 3 };
 
 // The kernel function `which` on the current device and that device's
 // compute unit count.
@@ -49,8 +55,10 @@ hipError_t asm_function(AsmKernel which, hipFunction_t *fn, int *cus) {
     static std::mutex mu;
     static hipFunction_t fns[kMaxDevices][kNumAsm] = {};
     static int cu_count[kMaxDevices] = {};
-    static const unsigned char *const images[kNumAsm] = {kFwdGqaCodeObject, kFwdDiffCodeObject};
-    static const char *const names[kNumAsm] = {"swa_fwd_gqa_d128", "diff_fwd_d64_dv128"};
+    static const unsigned char *const images[kNumAsm] = {kFwdGqaCodeObject, kFwdGqaDilCodeObject,
+                                                         kFwdDiffCodeObject};
+    static const char *const names[kNumAsm] = {"swa_fwd_gqa_d128", "swa_fwd_gqa_d128_dil",
+                                               "diff_fwd_d64_dv128"};
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -102,20 +110,29 @@ hipError_t launch(hipFunction_t fn, void *args, size_t size, int32_t grid, hipSt
 }  // namespace
 
 bool fwd_gqa_applies(const FwdArgs &a) {
-    return a.nmaps == 1 && a.d == 128 && a.dv == 128 && a.stride == 0 && a.dilation == 1 &&
-           a.n_global == 0 && (a.Hq / a.Hkv) % 4 == 0;
+    return a.nmaps == 1 && a.d == 128 && a.dv == 128 && a.stride == 0 && a.n_global == 0 &&
+           (a.Hq / a.Hkv) % 4 == 0;
 }
 
+namespace {
+// rows of the longest residue class, the number of classes with rows, and
+// 64-row blocks per class (dilation 1: one class of N rows)
+int64_t class_rows(const FwdArgs &a) { return (static_cast<int64_t>(a.N) + a.dilation - 1) / a.dilation; }
+int64_t class_count(const FwdArgs &a) { return a.dilation < a.N ? a.dilation : a.N; }
+int64_t class_blocks(const FwdArgs &a) { return (class_rows(a) + 63) / 64; }
+}  // namespace
+
 int64_t fwd_gqa_items(const FwdArgs &a) {
-    // one item per (batch, key/value head, block of 4 query heads, block of
-    // 64 query rows)
-    return static_cast<int64_t>(a.B) * a.Hkv * ((a.Hq / a.Hkv) / 4) * ((a.N + 63) / 64);
+    // one item per (batch, key/value head, block of 4 query heads, residue
+    // class of the rows mod the dilation, block of 64 rows of the class)
+    return static_cast<int64_t>(a.B) * a.Hkv * ((a.Hq / a.Hkv) / 4) * class_count(a) * class_blocks(a);
 }
 
 hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
     hipFunction_t fn = nullptr;
     int cus = 0;
-    hipError_t e = asm_function(kGqa, &fn, &cus);
+    const bool dilated = a.dilation > 1;
+    hipError_t e = asm_function(dilated ? kGqaDil : kGqa, &fn, &cus);
     if (e != hipSuccess)
         return e;
     GqaArgs k{};
@@ -125,19 +142,21 @@ hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
     k.out = a.out;
     k.lse = a.lse;
     k.N = a.N;
-    // distances are < N, so a window of N or more is the full causal mask
-    k.window = a.window < a.N ? a.window : a.N;
+    // distances within a class are below its length, so a window of that
+    // length or more is the full causal mask of the class
+    const int64_t rows = class_rows(a);
+    k.window = static_cast<int32_t>(a.window < rows ? a.window : rows);
     k.G = a.Hq / a.Hkv;
     k.head_blocks = k.G / 4;
-    k.row_blocks = (a.N + 63) / 64;
+    k.row_blocks = static_cast<int32_t>(class_blocks(a));
     k.c = a.scale * 1.4426950408889634f;
     const int64_t items = fwd_gqa_items(a);
     if (items <= 0 || items > INT32_MAX)
         return hipErrorInvalidValue;
     k.items = static_cast<int32_t>(items);
     k.stride = persistent_grid(items, cus);
-    k.Hkv = a.Hkv;
-    k.Hq = a.Hq;
+    k.dilation = a.dilation;
+    k.classes = static_cast<int32_t>(class_count(a));
     return launch(fn, &k, sizeof(k), k.stride, stream);
 }
 

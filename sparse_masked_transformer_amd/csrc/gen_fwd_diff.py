@@ -699,9 +699,10 @@ amdhsa.kernels:
 
 
 def main(out_path):
+    """Write the kernel to out_path; returns its name."""
     with open(out_path, "w") as f:
         f.write(render())
-    return out_path
+    return NAME
 
 
 if __name__ == "__main__":

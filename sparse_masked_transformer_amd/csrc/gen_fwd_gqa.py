@@ -497,6 +497,15 @@ S_X = [s(78 + i) for i in range(14)]  # scalar temporaries s78..s91
 # only within 2^-8, which on peaky rows costs up to ~0.02 of output error)
 OPT = {"fp32_sums": False}
 
+# the dilated variant (dilation r > 1, window only): the rows i with
+# i % r == c form residue class c, on which the dilated window is a plain
+# window of W keys; the kernel runs each class as its own sequence of
+# N_c = ceil((N - c) / r) rows, reading every r-th row (a row pitch of
+# 256 r bytes from byte 256 c).  Off in the plain kernel, whose code is
+# unchanged by the option.
+DIL = {"on": False}
+S_DIL, S_PITCH, S_TILEB, S_CLS, S_NC, S_NCLS = s(66), s(67), s(92), s(93), s(94), s(95)
+
 
 # ---------------------------------------------------------------------------
 # optional register dumps (a development aid: off in the library build)
@@ -582,6 +591,21 @@ def rsrc(P, dst, base, idx, bytes_per_idx_sgpr, num_sgpr):
     P.salu("s_and_b32", dst.sub(1), dst.sub(1), "0xffff")
     P.salu("s_mov_b32", dst.sub(2), num_sgpr, writes_scc=False)
     P.salu("s_mov_b32", dst.sub(3), "0x00020000", writes_scc=False)
+
+
+def rsrc_add(P, dst, off):
+    """Move a raw buffer descriptor's base up by `off` bytes (SGPR)."""
+    P.salu("s_add_u32", dst.sub(0), dst.sub(0), off)
+    P.salu("s_addc_u32", dst.sub(1), dst.sub(1), "0", reads_scc=True)
+    P.salu("s_and_b32", dst.sub(1), dst.sub(1), "0xffff")
+
+
+def class_rows(P, dst, pitch, row_bytes):
+    """dst = (N_c - 1) * pitch + row_bytes: the bytes from a class's first
+    row to the end of its last (the descriptor range of the class)."""
+    P.salu("s_sub_u32", dst, S_NC, "1")
+    P.salu("s_mul_i32", dst, dst, pitch)
+    P.salu("s_add_u32", dst, dst, str(row_bytes))
 
 
 def dma_ops():
@@ -900,7 +924,10 @@ def setup_ops(pn):
         P.salu("s_add_u32", S_X[9], S_J, "1")                  # i
         P.salu("s_add_u32", S_X[4], S_X[9], "2")               # tile i + 2
         P.salu("s_add_u32", S_X[5], S_TLO, S_X[4])
-        P.salu("s_lshl_b32", S_X[5], S_X[5], "14")
+        if DIL["on"]:
+            P.salu("s_mul_i32", S_X[5], S_X[5], S_TILEB)
+        else:
+            P.salu("s_lshl_b32", S_X[5], S_X[5], "14")
 
     # past the band (i + 2 >= T) the offset is N rows, out of the
     # descriptor's range: the loads read zeros without touching memory,
@@ -1065,7 +1092,11 @@ def epilogue(P, phase):
         for kk in range(4):
             P.ds_read("ds_read_b128", v(ob + 4 * kk, 4), V_ORD, kk * 8 * OROW)
         for kk in range(4):
-            P.salu("s_mov_b32", S_X[3 + kk], str(kk * 8 * 256 + half * 128), writes_scc=False)
+            if DIL["on"]:
+                P.salu("s_mul_i32", S_X[3 + kk], S_PITCH, str(8 * kk))
+                P.salu("s_add_u32", S_X[3 + kk], S_X[3 + kk], str(half * 128))
+            else:
+                P.salu("s_mov_b32", S_X[3 + kk], str(kk * 8 * 256 + half * 128), writes_scc=False)
             P.add(I(f"  buffer_store_dwordx4 {v(ob + 4 * kk, 4)}, {V_OST}, {S_RSO}, {S_X[3 + kk]} offen",
                     "vstore", regs_of(v(ob + 4 * kk, 4), V_OST, S_RSO, S_X[3 + kk]), EMPTY))
     P.scmp("s_cmp_lt_u32", S_VID, S_TOTAL)
@@ -1074,7 +1105,8 @@ def epilogue(P, phase):
 
 
 def query_head(P, dst):
-    """dst = bg * G + 4 hb + (wave & 3): this wave's query head."""
+    """dst = bg * G + 4 hb + (wave & 3): this wave's query head (S_X[8] is
+    its temporary)."""
     P.salu("s_mul_i32", dst, S_BG, S_G)
     P.salu("s_lshl_b32", S_X[8], S_HB, "2")
     P.salu("s_add_u32", dst, dst, S_X[8])
@@ -1110,7 +1142,16 @@ def item_loads(P, first):
     P.salu("s_cselect_b32", S_LID, S_X[1], S_VID, reads_scc=True, writes_scc=False)
     # lid -> (head block, row block, batch * kv head), row blocks ascending
     udiv(P, S_LID, S_NHB, S_X[4], S_HB, V_T[1], V_T[2])        # S_X[4] = rest
-    udiv(P, S_X[4], S_NRB, S_BG, S_RB, V_T[1], V_T[2])         # row block
+    if DIL["on"]:
+        # rest -> (batch * kv head, residue class, row block of the class)
+        udiv(P, S_X[4], S_NRB, S_X[5], S_RB, V_T[1], V_T[2])
+        udiv(P, S_X[5], S_NCLS, S_BG, S_CLS, V_T[1], V_T[2])
+        P.salu("s_sub_u32", S_X[6], S_N, S_CLS)                # rows of the class: ceil((N - c) / r)
+        P.salu("s_add_u32", S_X[6], S_X[6], S_DIL)
+        P.salu("s_sub_u32", S_X[6], S_X[6], "1")
+        udiv(P, S_X[6], S_DIL, S_NC, S_X[7], V_T[1], V_T[2])
+    else:
+        udiv(P, S_X[4], S_NRB, S_BG, S_RB, V_T[1], V_T[2])     # row block
     P.salu("s_lshl_b32", S_R0, S_RB, "6")
     P.salu("s_lshl_b32", S_R0W, S_WR, "5")
     P.salu("s_add_u32", S_R0W, S_R0W, S_R0)                    # this wave's first row
@@ -1120,28 +1161,49 @@ def item_loads(P, first):
     P.salu("s_max_i32", S_X[0], S_X[0], "0")
     P.salu("s_lshr_b32", S_TLO, S_X[0], "6")
     P.salu("s_add_u32", S_X[1], S_R0, "63")
-    P.salu("s_sub_u32", S_X[2], S_N, "1")
+    P.salu("s_sub_u32", S_X[2], S_NC if DIL["on"] else S_N, "1")
     P.salu("s_min_u32", S_X[1], S_X[1], S_X[2])
+    if DIL["on"]:
+        # (a last row block past its class's rows walks one tile of zeros)
+        P.salu("s_max_u32", S_X[1], S_X[1], S_R0)
     P.salu("s_lshr_b32", S_X[1], S_X[1], "6")
     P.salu("s_sub_u32", S_T, S_X[1], S_TLO)
     P.salu("s_add_u32", S_T, S_T, "1")
     # descriptors
     P.salu("s_lshl_b32", S_X[6], S_N, "8")                     # bytes per head (N rows of 256 B)
-    rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[6])
-    rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
-    query_head(P, S_X[7])
-    rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
+    if DIL["on"]:
+        query_head(P, S_X[7])                                  # (uses S_X[8] as a temporary)
+        class_rows(P, S_X[8], S_PITCH, 256)                    # the class's rows: (N_c - 1) pitch + 256
+        P.salu("s_lshl_b32", S_X[9], S_CLS, "8")
+        P.salu("s_mul_i32", S_NB, S_NC, S_PITCH)               # past the class's rows
+        rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[8])
+        rsrc_add(P, S_RSK, S_X[9])
+        rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[8])
+        rsrc_add(P, S_RSV, S_X[9])
+        rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[8])
+        rsrc_add(P, S_RSQ, S_X[9])
+    else:
+        rsrc(P, S_RSK, S_K, S_BG, S_X[6], S_X[6])
+        rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
+        query_head(P, S_X[7])
+        rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
     # Q fragments
-    P.salu("s_lshl_b32", S_X[9], S_R0W, "8")
+    if DIL["on"]:
+        P.salu("s_mul_i32", S_X[9], S_R0W, S_PITCH)
+    else:
+        P.salu("s_lshl_b32", S_X[9], S_R0W, "8")
     P.valu("v_add_u32", V_QOFF, S_X[9], V_QLANE)
     for ks in range(8):
         P.buf_load(A_Q.sub(4 * ks, 4), V_QOFF, S_RSQ, "0", 32 * ks, track=False)
     # tiles 0 and 1 (tile 1 also when the band has one tile: its rows are
     # read, or are past N and read as zeros, and never used)
-    P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
+    if DIL["on"]:
+        P.salu("s_mul_i32", S_SOFF, S_TLO, S_TILEB)
+    else:
+        P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
     P.salu("s_mul_i32", S_SB, S_BASE, str(STAGE))
     dma_tile(P)
-    P.salu("s_add_u32", S_SOFF, S_SOFF, str(1 << 14))
+    P.salu("s_add_u32", S_SOFF, S_SOFF, S_TILEB if DIL["on"] else str(1 << 14))
     P.salu("s_add_u32", S_X[0], S_BASE, "1")
     P.salu("s_and_b32", S_X[0], S_X[0], "3")
     P.salu("s_mul_i32", S_SB, S_X[0], str(STAGE))
@@ -1160,19 +1222,37 @@ def item_start(P):
     P.label(".Litem")
     P.salu("s_lshl_b32", S_X[6], S_N, "8")
     query_head(P, S_X[7])
-    rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[6])
-    P.salu("s_lshl_b32", S_X[9], S_N, "2")
-    rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[9])
+    if DIL["on"]:
+        P.salu("s_lshl_b32", S_X[9], S_N, "2")
+        class_rows(P, S_X[8], S_PITCH, 256)
+        P.salu("s_lshl_b32", S_X[10], S_CLS, "8")
+        rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[8])
+        rsrc_add(P, S_RSO, S_X[10])
+        P.salu("s_lshl_b32", S_X[11], S_DIL, "2")              # log-sum-exp pitch 4 r
+        class_rows(P, S_X[8], S_X[11], 4)
+        P.salu("s_lshl_b32", S_X[10], S_CLS, "2")
+        rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[8])
+        rsrc_add(P, S_RSL, S_X[10])
+    else:
+        rsrc(P, S_RSO, S_OUT, S_X[7], S_X[6], S_X[6])
+        P.salu("s_lshl_b32", S_X[9], S_N, "2")
+        rsrc(P, S_RSL, S_LSE, S_X[7], S_X[9], S_X[9])
     P.salu("s_add_u32", S_R0W32, S_R0W, "32")
     t = V_T
     P.valu("v_add_u32", t[5], S_R0W, V_COL)                    # row
-    P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
+    if DIL["on"]:
+        P.valu("v_mul_u32_u24", V_LOFF, S_X[11], t[5])
+    else:
+        P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
     P.valu("v_lshlrev_b32", t[7], "2", V_HL)
     P.valu("v_sub_u32", V_IBASE, t[5], t[7])
     # output store offset: row r0w + lane / 8, bytes 16 (lane % 8) of a half row
     P.valu("v_lshrrev_b32", t[0], "3", V_LANE)
     P.valu("v_add_u32", t[0], S_R0W, t[0])
-    P.valu("v_lshlrev_b32", t[0], "8", t[0])
+    if DIL["on"]:
+        P.valu("v_mul_u32_u24", t[0], S_PITCH, t[0])
+    else:
+        P.valu("v_lshlrev_b32", t[0], "8", t[0])
     P.valu("v_and_b32", t[1], "7", V_LANE)
     P.valu("v_lshlrev_b32", t[1], "4", t[1])
     P.valu("v_add_u32", V_OST, t[0], t[1])
@@ -1218,6 +1298,13 @@ def prologue(P):
         P.smem("s_load_dwordx2", s(92, 2), S_KARG, "0x50")
         P.smem("s_load_dword", s(94), S_KARG, "0x58")
     P.waitcnt(lgkm=0)
+    if DIL["on"]:
+        # (the dilation and the class count share the argument dwords of
+        # the item and workgroup registers set below)
+        P.salu("s_mov_b32", S_DIL, s(22), writes_scc=False)
+        P.salu("s_mov_b32", S_NCLS, s(23), writes_scc=False)
+        P.salu("s_lshl_b32", S_PITCH, S_DIL, "8")
+        P.salu("s_lshl_b32", S_TILEB, S_PITCH, "6")
     P.salu("s_and_b32", S_WH, S_WAVE, "3")
     P.salu("s_lshr_b32", S_WR, S_WAVE, "2")
     if DEBUG["on"]:
@@ -1254,7 +1341,10 @@ def prologue(P):
     P.valu("v_add_u32", t[2], t[2], t[4])
     P.valu("v_add_u32", V_VLANE, str(KTILE), t[2])
     # Q rows: row col of the wave's 32, bytes 16 hl of each 32-byte group
-    P.valu("v_lshlrev_b32", t[0], "8", V_COL)
+    if DIL["on"]:
+        P.valu("v_mul_u32_u24", t[0], S_PITCH, V_COL)
+    else:
+        P.valu("v_lshlrev_b32", t[0], "8", V_COL)
     P.valu("v_lshlrev_b32", t[1], "4", V_HL)
     P.valu("v_add_u32", V_QLANE, t[0], t[1])
     # output staging: LDS write base (row col, values 4 hl: col * 144 +
@@ -1303,7 +1393,10 @@ def _chunk_src(P, dst, pos, magic, rowb, t):
     P.valu("v_sub_u32", t[12], pos, t[12])                     # column byte
     P.add(I(f"  v_cmp_gt_u32 vcc, {2 * D}, {t[12]}", "vcmp", t[12].regs(), VCC))
     P.valu("v_cndmask_b32", t[12], "0", t[12], "vcc")
-    P.valu("v_lshlrev_b32", t[11], "8", t[11])
+    if DIL["on"]:
+        P.valu("v_mul_u32_u24", t[11], S_PITCH, t[11])
+    else:
+        P.valu("v_lshlrev_b32", t[11], "8", t[11])
     P.valu("v_add_u32", dst, t[11], t[12])
 
 
@@ -1340,23 +1433,28 @@ def kernel_text():
     return "\n".join(lines)
 
 
+def kernel_name():
+    return NAME + ("_dil" if DIL["on"] else "")
+
+
 def render():
+    name = kernel_name()
     body = kernel_text()
     karg = KARG_BYTES + (16 if DEBUG["on"] else 0)
     head = f""".amdgcn_target "amdgcn-amd-amdhsa--gfx950"
 .text
-.globl {NAME}
+.globl {name}
 .p2align 8
-.type {NAME},@function
-{NAME}:
+.type {name},@function
+{name}:
 """
     tail = f"""
 .Lfunc_end:
-.size {NAME}, .Lfunc_end-{NAME}
+.size {name}, .Lfunc_end-{name}
 
 .rodata
 .p2align 6
-.amdhsa_kernel {NAME}
+.amdhsa_kernel {name}
   .amdhsa_group_segment_fixed_size {LDS_BYTES}
   .amdhsa_private_segment_fixed_size 0
   .amdhsa_kernarg_size {karg}
@@ -1378,8 +1476,8 @@ def render():
 ---
 amdhsa.version: [ 1, 2 ]
 amdhsa.kernels:
-  - .name: {NAME}
-    .symbol: {NAME}.kd
+  - .name: {name}
+    .symbol: {name}.kd
     .kernarg_segment_size: {karg}
     .group_segment_fixed_size: {LDS_BYTES}
     .private_segment_fixed_size: 0
@@ -1397,11 +1495,18 @@ amdhsa.kernels:
     return head + body + tail
 
 
-def main(out_path):
-    text = render()
+def main(out_path, dilated=False):
+    """Write the kernel (the dilated variant if `dilated`) to out_path;
+    returns its name."""
+    DIL["on"] = dilated
+    try:
+        text = render()
+        name = kernel_name()
+    finally:
+        DIL["on"] = False
     with open(out_path, "w") as f:
         f.write(text)
-    return out_path
+    return name
 
 
 if __name__ == "__main__":

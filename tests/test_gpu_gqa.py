@@ -4,7 +4,9 @@ multiple of 4 query heads per key/value head) against the fp64 oracle.
 
 The kernel works on items of 64 query rows of 4 query heads of a key/value
 head, a workgroup per compute unit taking items in turn; the cases cover
-one-tile bands, chains of several items per workgroup, ragged
+one-tile bands, chains of several items per workgroup, dilated windows
+(the variant that walks each residue class of the rows as a plain window),
+ragged
 sequence ends (rows and keys past N), windows at and around the 64-key tile
 size, windows beyond N, several head blocks per key/value head, batches,
 peaky scores that move the running maximum late, the log-sum-exp output, and
@@ -95,6 +97,40 @@ def test_gqa_parity(swa, B, Hq, Hkv, N, W):
     lerr = float(np.max(np.abs(lse - want_lse)))
     assert err <= TOL, err
     assert lerr <= LSE_TOL, lerr
+
+
+DILATED_CASES = [
+    # B, Hq, Hkv, N, W, dilation: each residue class of the rows mod the
+    # dilation runs as a plain window over every dilation-th row
+    (1, 4, 1, 200, 16, 2),
+    (1, 4, 1, 333, 40, 3),
+    (1, 8, 2, 1000, 100, 2),
+    (1, 4, 1, 130, 1, 5),
+    (1, 4, 1, 385, 9, 3),          # classes of 129, 128, 128 rows: empty last blocks
+    (1, 4, 1, 7, 3, 8),            # N < dilation: one row per class
+    (1, 4, 1, 40, 3, 64),          # the largest dilation
+    (1, 4, 1, 500, 2 ** 30, 2),    # every earlier key of the class attends
+    (1, 4, 1, 4097, 700, 2),
+    (2, 8, 2, 2000, 300, 4),
+    (4, 16, 4, 2100, 300, 3),      # 528 items
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,W,dil", DILATED_CASES)
+def test_gqa_dilated_parity(swa, B, Hq, Hkv, N, W, dil):
+    print(f"[case] gqa dilated B={B} Hq={Hq} Hkv={Hkv} N={N} W={W} dilation={dil}", flush=True)
+    cfg = dict(dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, N=N, d=128, dv=128, window=W, stride=0, dilation=dil,
+               scale=1.0 / math.sqrt(128), seed=3000 + N + W % 9973 + dil)
+    q, k, v = synth.prefill_inputs(cfg)
+    mask = swa.swa_block_mask_build(N, W, 0, d=128, dilation=dil)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    out = swa.swa_attn_fwd(bf(q), bf(k), bf(v), W, 0, cfg["scale"], mask, lse=lse)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want, want_lse = oracle.attn_full(q, k, v, W, 0, cfg["scale"], with_lse=True, dilation=dil)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - want))) <= TOL
+    assert float(np.max(np.abs(lse.cpu().numpy() - want_lse))) <= LSE_TOL
 
 
 @pytest.mark.parametrize("q_scale,W", [(8.0, 300), (16.0, 1024)])
