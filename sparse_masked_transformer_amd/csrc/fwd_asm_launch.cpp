@@ -1,10 +1,13 @@
 // Launch of the generated gfx950 assembly kernels: swa_fwd_gqa_d128
 // (grouped-query sliding-window forward, bf16, d = 128; gen_fwd_gqa.py), its
 // dilated variant swa_fwd_gqa_d128_dil (each residue class of the rows mod
-// the dilation walked as a plain window), and diff_fwd_d64_dv128
+// the dilation walked as a plain window) and global-token variant
+// swa_fwd_gqa_d128_glb (the global columns' tiles walked ahead of the band),
+// and diff_fwd_d64_dv128
 // (differential sliding-window forward, bf16, d = 64, dv = 128;
 // gen_fwd_diff.py).  Their code objects are embedded in this library
-// (fwd_gqa_blob.cpp, fwd_gqa_dil_blob.cpp, fwd_diff_blob.cpp, made by the
+// (fwd_gqa_blob.cpp, fwd_gqa_dil_blob.cpp, fwd_gqa_glb_blob.cpp,
+// fwd_diff_blob.cpp, made by the
 // build from the generated .s files) and loaded once per device.  All run a
 // persistent grid of one 512-lane workgroup per compute unit.
 #include <mutex>
@@ -17,6 +20,8 @@ extern const unsigned char kFwdGqaCodeObject[];
 extern const size_t kFwdGqaCodeObjectSize;
 extern const unsigned char kFwdGqaDilCodeObject[];
 extern const size_t kFwdGqaDilCodeObjectSize;
+extern const unsigned char kFwdGqaGlbCodeObject[];
+extern const size_t kFwdGqaGlbCodeObjectSize;
 extern const unsigned char kFwdDiffCodeObject[];
 extern const size_t kFwdDiffCodeObjectSize;
 
@@ -30,8 +35,8 @@ struct GqaArgs {
     int32_t N, window, G, head_blocks, row_blocks;
     float c;
     int32_t items, stride;
-    int32_t dilation;   // dilated variant: the dilation r and the number of
-    int32_t classes;    // residue classes min(r, N) (unused by the plain kernel)
+    int32_t aux;        // dilated variant: the dilation r; global-token variant: n_global
+    int32_t classes;    // dilated variant: the residue classes min(r, N)
 };
 static_assert(sizeof(GqaArgs) == 80, "kernel argument block is 80 bytes");
 
@@ -47,7 +52,7 @@ static_assert(sizeof(DiffArgs) == 80, "kernel argument block is 80 bytes");
 
 constexpr int kMaxDevices = 64;
 
-enum AsmKernel { kGqa = 0, kGqaDil = 1, kDiff = 2, kNumAsm = 3 };
+enum AsmKernel { kGqa = 0, kGqaDil = 1, kGqaGlb = 2, kDiff = 3, kNumAsm = 4 };
 
 // The kernel function `which` on the current device and that device's
 // compute unit count.
@@ -56,9 +61,9 @@ hipError_t asm_function(AsmKernel which, hipFunction_t *fn, int *cus) {
     static hipFunction_t fns[kMaxDevices][kNumAsm] = {};
     static int cu_count[kMaxDevices] = {};
     static const unsigned char *const images[kNumAsm] = {kFwdGqaCodeObject, kFwdGqaDilCodeObject,
-                                                         kFwdDiffCodeObject};
+                                                         kFwdGqaGlbCodeObject, kFwdDiffCodeObject};
     static const char *const names[kNumAsm] = {"swa_fwd_gqa_d128", "swa_fwd_gqa_d128_dil",
-                                               "diff_fwd_d64_dv128"};
+                                               "swa_fwd_gqa_d128_glb", "diff_fwd_d64_dv128"};
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -110,8 +115,9 @@ hipError_t launch(hipFunction_t fn, void *args, size_t size, int32_t grid, hipSt
 }  // namespace
 
 bool fwd_gqa_applies(const FwdArgs &a) {
-    return a.nmaps == 1 && a.d == 128 && a.dv == 128 && a.stride == 0 && a.n_global == 0 &&
-           (a.Hq / a.Hkv) % 4 == 0;
+    // a window, dilated or with global tokens (not both)
+    return a.nmaps == 1 && a.d == 128 && a.dv == 128 && a.stride == 0 &&
+           (a.dilation == 1 || a.n_global == 0) && (a.Hq / a.Hkv) % 4 == 0;
 }
 
 namespace {
@@ -131,8 +137,8 @@ int64_t fwd_gqa_items(const FwdArgs &a) {
 hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
     hipFunction_t fn = nullptr;
     int cus = 0;
-    const bool dilated = a.dilation > 1;
-    hipError_t e = asm_function(dilated ? kGqaDil : kGqa, &fn, &cus);
+    const AsmKernel which = a.dilation > 1 ? kGqaDil : (a.n_global > 0 ? kGqaGlb : kGqa);
+    hipError_t e = asm_function(which, &fn, &cus);
     if (e != hipSuccess)
         return e;
     GqaArgs k{};
@@ -155,7 +161,7 @@ hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream) {
         return hipErrorInvalidValue;
     k.items = static_cast<int32_t>(items);
     k.stride = persistent_grid(items, cus);
-    k.dilation = a.dilation;
+    k.aux = which == kGqaGlb ? (a.n_global < a.N ? a.n_global : a.N) : a.dilation;
     k.classes = static_cast<int32_t>(class_count(a));
     return launch(fn, &k, sizeof(k), k.stride, stream);
 }

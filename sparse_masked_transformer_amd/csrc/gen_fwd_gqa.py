@@ -506,6 +506,17 @@ OPT = {"fp32_sums": False}
 DIL = {"on": False}
 S_DIL, S_PITCH, S_TILEB, S_CLS, S_NC, S_NCLS = s(66), s(67), s(92), s(93), s(94), s(95)
 
+# the global-token variant (n_global G > 0, dilation 1, window only): keys
+# j < G attend every row i >= j, and rows i < G attend every key j <= i.
+# An item whose band starts past the global columns walks their tiles
+# first (the prefix tiles 0 .. NP-1), then its band; an item holding
+# global rows starts its band at key 0.  Step s of an item is tile s while
+# s < NP, else tile t_lo + s - NP.  Off in the plain kernel.
+GLB = {"on": False}
+S_NGLB, S_PB = s(66), s(67)          # G; NP + the item's stage base (the first band step)
+V_GB = v(126)                        # G - 4 (lane / 32): the global columns of the lane's keys
+V_WM1L = v(80)                       # W - 1, or 2^30 on a global row (every earlier key attends)
+
 
 # ---------------------------------------------------------------------------
 # optional register dumps (a development aid: off in the library build)
@@ -786,7 +797,10 @@ def mask_block(P, sbuf, k0):
     for kb in range(2):
         P.salu("s_add_u32", S_X[3], k0, str(32 * kb))
         P.valu("v_subrev_u32", tb, S_X[3], V_IBASE)                      # base = i - 4 hl - key0
-        P.valu("v_subrev_u32", tlo, S_WM1, tb)                            # base - (W - 1)
+        if GLB["on"]:
+            P.valu("v_sub_u32", tlo, tb, V_WM1L)                          # base - (W - 1)
+        else:
+            P.valu("v_subrev_u32", tlo, S_WM1, tb)                        # base - (W - 1)
         P.valu("v_max_i32", tlo, "0", tlo)
         P.valu("v_min_i32", thi, "31", tb)
         P.valu("v_lshlrev_b32_e64", tm1, thi, "2")
@@ -795,6 +809,22 @@ def mask_block(P, sbuf, k0):
         P.valu("v_and_b32", tm1, tm1, tm2)
         P.add(I(f"  v_cmp_le_i32 vcc, {tlo}, {thi}", "vcmp", regs_of(tlo, thi), VCC))
         P.valu("v_cndmask_b32", tm1, "0", tm1, "vcc")
+        if GLB["on"]:
+            # or the global columns kc < G - 4 hl - key0, within kc <= hi
+            tg, tg2 = V_T[6], V_T[7]
+            P.valu("v_subrev_u32", tg, S_X[3], V_GB)
+            P.valu("v_min_i32", tg, "32", tg)
+            P.valu("v_add_u32", tg2, "-1", tg)
+            P.valu("v_lshlrev_b32_e64", tg2, tg2, "2")
+            P.valu("v_add_u32", tg2, "-1", tg2)                            # (1 << g) - 1, g = 1..32
+            P.add(I(f"  v_cmp_lt_i32 vcc, 0, {tg}", "vcmp", regs_of(tg), VCC))
+            P.valu("v_cndmask_b32", tg2, "0", tg2, "vcc")
+            P.valu("v_lshlrev_b32_e64", tm2, thi, "2")
+            P.valu("v_add_u32", tm2, "-1", tm2)                            # (2 << hi) - 1
+            P.valu("v_and_b32", tg2, tg2, tm2)
+            P.add(I(f"  v_cmp_le_i32 vcc, 0, {thi}", "vcmp", regs_of(thi), VCC))
+            P.valu("v_cndmask_b32", tg2, "0", tg2, "vcc")
+            P.valu("v_or_b32", tm1, tm1, tg2)
         for r in range(16):
             kc = (r % 4) + 8 * (r // 4)
             sr = v(sbuf + 16 * kb + r)
@@ -924,6 +954,10 @@ def setup_ops(pn):
         P.salu("s_add_u32", S_X[9], S_J, "1")                  # i
         P.salu("s_add_u32", S_X[4], S_X[9], "2")               # tile i + 2
         P.salu("s_add_u32", S_X[5], S_TLO, S_X[4])
+        if GLB["on"]:
+            P.salu("s_sub_u32", S_X[6], S_X[4], S_BASE)        # a prefix step: tile = step
+            P.scmp("s_cmp_lt_u32", S_X[4], S_PB)
+            P.salu("s_cselect_b32", S_X[5], S_X[6], S_X[5], reads_scc=True, writes_scc=False)
         if DIL["on"]:
             P.salu("s_mul_i32", S_X[5], S_X[5], S_TILEB)
         else:
@@ -944,6 +978,10 @@ def setup_ops(pn):
 
     def o4(P):
         P.salu("s_add_u32", S_X[6], S_TLO, S_X[9])
+        if GLB["on"]:
+            P.salu("s_sub_u32", S_X[7], S_X[9], S_BASE)
+            P.scmp("s_cmp_lt_u32", S_X[9], S_PB)
+            P.salu("s_cselect_b32", S_X[6], S_X[7], S_X[6], reads_scc=True, writes_scc=False)
         P.salu("s_lshl_b32", S_K0P[pn], S_X[6], "6")           # key0 of tile i
         P.salu("s_add_u32", S_X[7], S_K0P[pn], "63")
         P.salu("s_add_u32", S_X[8], S_K0P[pn], S_W)
@@ -1160,6 +1198,9 @@ def item_loads(P, first):
     P.salu("s_add_i32", S_X[0], S_X[0], "1")
     P.salu("s_max_i32", S_X[0], S_X[0], "0")
     P.salu("s_lshr_b32", S_TLO, S_X[0], "6")
+    if GLB["on"]:
+        P.scmp("s_cmp_lt_u32", S_R0, S_NGLB)                   # global rows: the band starts at key 0
+        P.salu("s_cselect_b32", S_TLO, "0", S_TLO, reads_scc=True, writes_scc=False)
     P.salu("s_add_u32", S_X[1], S_R0, "63")
     P.salu("s_sub_u32", S_X[2], S_NC if DIL["on"] else S_N, "1")
     P.salu("s_min_u32", S_X[1], S_X[1], S_X[2])
@@ -1197,18 +1238,38 @@ def item_loads(P, first):
         P.buf_load(A_Q.sub(4 * ks, 4), V_QOFF, S_RSQ, "0", 32 * ks, track=False)
     # tiles 0 and 1 (tile 1 also when the band has one tile: its rows are
     # read, or are past N and read as zeros, and never used)
-    if DIL["on"]:
+    if GLB["on"]:
+        # prefix tiles NP = min(ceil(G / 64), t_lo); tiles of steps 0 and 1
+        P.salu("s_add_u32", S_X[0], S_NGLB, "63")
+        P.salu("s_lshr_b32", S_X[0], S_X[0], "6")
+        P.salu("s_min_u32", S_X[10], S_X[0], S_TLO)            # NP
+        P.scmp("s_cmp_gt_u32", S_X[10], "0")
+        P.salu("s_cselect_b32", S_X[0], "0", S_TLO, reads_scc=True, writes_scc=False)
+        P.salu("s_sub_u32", S_X[1], S_TLO, S_X[10])
+        P.salu("s_add_u32", S_X[1], S_X[1], "1")
+        P.scmp("s_cmp_gt_u32", S_X[10], "1")
+        P.salu("s_cselect_b32", S_X[1], "1", S_X[1], reads_scc=True, writes_scc=False)
+        P.salu("s_lshl_b32", S_SOFF, S_X[0], "14")
+        P.salu("s_lshl_b32", S_X[1], S_X[1], "14")
+    elif DIL["on"]:
         P.salu("s_mul_i32", S_SOFF, S_TLO, S_TILEB)
     else:
         P.salu("s_lshl_b32", S_SOFF, S_TLO, "14")
     P.salu("s_mul_i32", S_SB, S_BASE, str(STAGE))
     dma_tile(P)
-    P.salu("s_add_u32", S_SOFF, S_SOFF, S_TILEB if DIL["on"] else str(1 << 14))
+    if GLB["on"]:
+        P.salu("s_mov_b32", S_SOFF, S_X[1], writes_scc=False)
+    else:
+        P.salu("s_add_u32", S_SOFF, S_SOFF, S_TILEB if DIL["on"] else str(1 << 14))
     P.salu("s_add_u32", S_X[0], S_BASE, "1")
     P.salu("s_and_b32", S_X[0], S_X[0], "3")
     P.salu("s_mul_i32", S_SB, S_X[0], str(STAGE))
     dma_tile(P)
     # step counter from S_BASE: first tile and band end shifted to match
+    if GLB["on"]:
+        P.salu("s_add_u32", S_T, S_T, S_X[10])                 # prefix steps first
+        P.salu("s_sub_u32", S_TLO, S_TLO, S_X[10])
+        P.salu("s_add_u32", S_PB, S_X[10], S_BASE)
     P.salu("s_sub_u32", S_TLO, S_TLO, S_BASE)
     P.salu("s_add_u32", S_T, S_T, S_BASE)
     if skip:
@@ -1246,6 +1307,11 @@ def item_start(P):
         P.valu("v_lshlrev_b32", V_LOFF, "2", t[5])
     P.valu("v_lshlrev_b32", t[7], "2", V_HL)
     P.valu("v_sub_u32", V_IBASE, t[5], t[7])
+    if GLB["on"]:
+        P.add(I(f"  v_cmp_gt_u32 vcc, {S_NGLB}, {t[5]}", "vcmp", regs_of(S_NGLB, t[5]), VCC))
+        P.valu("v_mov_b32", t[6], "0x40000000")
+        P.valu("v_mov_b32", t[8], S_WM1)
+        P.valu("v_cndmask_b32", V_WM1L, t[8], t[6], "vcc")
     # output store offset: row r0w + lane / 8, bytes 16 (lane % 8) of a half row
     P.valu("v_lshrrev_b32", t[0], "3", V_LANE)
     P.valu("v_add_u32", t[0], S_R0W, t[0])
@@ -1298,6 +1364,8 @@ def prologue(P):
         P.smem("s_load_dwordx2", s(92, 2), S_KARG, "0x50")
         P.smem("s_load_dword", s(94), S_KARG, "0x58")
     P.waitcnt(lgkm=0)
+    if GLB["on"]:
+        P.salu("s_mov_b32", S_NGLB, s(22), writes_scc=False)   # (shares an argument dword, as below)
     if DIL["on"]:
         # (the dilation and the class count share the argument dwords of
         # the item and workgroup registers set below)
@@ -1347,6 +1415,9 @@ def prologue(P):
         P.valu("v_lshlrev_b32", t[0], "8", V_COL)
     P.valu("v_lshlrev_b32", t[1], "4", V_HL)
     P.valu("v_add_u32", V_QLANE, t[0], t[1])
+    if GLB["on"]:
+        P.valu("v_lshlrev_b32", t[0], "2", V_HL)
+        P.valu("v_sub_u32", V_GB, S_NGLB, t[0])
     # output staging: LDS write base (row col, values 4 hl: col * 144 +
     # 8 hl), LDS read base (row lane / 8, bytes 16 (lane % 8))
     P.valu("v_mul_u32_u24", V_OWL, str(OROW), V_COL)
@@ -1434,7 +1505,7 @@ def kernel_text():
 
 
 def kernel_name():
-    return NAME + ("_dil" if DIL["on"] else "")
+    return NAME + ("_dil" if DIL["on"] else "") + ("_glb" if GLB["on"] else "")
 
 
 def render():
@@ -1495,15 +1566,16 @@ amdhsa.kernels:
     return head + body + tail
 
 
-def main(out_path, dilated=False):
-    """Write the kernel (the dilated variant if `dilated`) to out_path;
-    returns its name."""
-    DIL["on"] = dilated
+def main(out_path, dilated=False, global_tokens=False):
+    """Write the kernel (the dilated or the global-token variant) to
+    out_path; returns its name."""
+    assert not (dilated and global_tokens)
+    DIL["on"], GLB["on"] = dilated, global_tokens
     try:
         text = render()
         name = kernel_name()
     finally:
-        DIL["on"] = False
+        DIL["on"] = GLB["on"] = False
     with open(out_path, "w") as f:
         f.write(text)
     return name

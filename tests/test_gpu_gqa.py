@@ -6,7 +6,8 @@ The kernel works on items of 64 query rows of 4 query heads of a key/value
 head, a workgroup per compute unit taking items in turn; the cases cover
 one-tile bands, chains of several items per workgroup, dilated windows
 (the variant that walks each residue class of the rows as a plain window),
-ragged
+global tokens (the variant that walks the global columns' tiles ahead of
+the band), ragged
 sequence ends (rows and keys past N), windows at and around the 64-key tile
 size, windows beyond N, several head blocks per key/value head, batches,
 peaky scores that move the running maximum late, the log-sum-exp output, and
@@ -128,6 +129,42 @@ def test_gqa_dilated_parity(swa, B, Hq, Hkv, N, W, dil):
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     want, want_lse = oracle.attn_full(q, k, v, W, 0, cfg["scale"], with_lse=True, dilation=dil)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - want))) <= TOL
+    assert float(np.max(np.abs(lse.cpu().numpy() - want_lse))) <= LSE_TOL
+
+
+GLOBAL_CASES = [
+    # B, Hq, Hkv, N, W, n_global: keys below n_global attend every later row
+    # and rows below it attend every earlier key; the variant walks the
+    # global columns' tiles ahead of each item's band
+    (1, 4, 1, 200, 16, 64),
+    (1, 4, 1, 333, 40, 1),
+    (1, 4, 1, 333, 40, 65),
+    (1, 8, 2, 1000, 100, 130),     # global rows beyond the first item
+    (1, 4, 1, 130, 1, 5),
+    (1, 4, 1, 64, 64, 64),
+    (1, 4, 1, 500, 1000, 64),      # window longer than the sequence
+    (1, 4, 1, 700, 50, 300),       # five tiles of global columns
+    (2, 8, 2, 1100, 200, 64),
+    (1, 4, 1, 257, 3, 200),
+    (1, 4, 1, 90, 90, 1000),       # every token global
+    (4, 16, 4, 2100, 300, 64),     # 528 items
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,W,g", GLOBAL_CASES)
+def test_gqa_global_tokens_parity(swa, B, Hq, Hkv, N, W, g):
+    print(f"[case] gqa global tokens B={B} Hq={Hq} Hkv={Hkv} N={N} W={W} n_global={g}", flush=True)
+    cfg = dict(dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, N=N, d=128, dv=128, window=W, stride=0, n_global=g,
+               scale=1.0 / math.sqrt(128), seed=5000 + N + W % 9973 + g)
+    q, k, v = synth.prefill_inputs(cfg)
+    mask = swa.swa_block_mask_build(N, W, 0, d=128, n_global=g)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    out = swa.swa_attn_fwd(bf(q), bf(k), bf(v), W, 0, cfg["scale"], mask, lse=lse)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want, want_lse = oracle.attn_full(q, k, v, W, 0, cfg["scale"], with_lse=True, n_global=g)
     assert np.all(np.isfinite(got))
     assert float(np.max(np.abs(got - want))) <= TOL
     assert float(np.max(np.abs(lse.cpu().numpy() - want_lse))) <= LSE_TOL
