@@ -50,6 +50,15 @@ The running maximum moves only when a tile's maximum exceeds it by more than
 8 (log2 units); O is then rescaled at the start of the next iteration, after
 the products of the old maximum have been accumulated.
 
+Variants (build options, the plain kernel's code unchanged by them) for
+the dilated window and the global tokens of Learn: Sparse & Sliding-Window
+Attention, §3b
+  dilated (DIL): with dilation r, each residue class of the rows mod r is
+  walked as a plain window over every r-th row (row pitch 256 r bytes);
+  global tokens (GLB): the tiles of the global columns left of an item's
+  band are walked ahead of it and the global columns ORed into the cell
+  mask.
+
 Hazards: every instruction records the registers it reads and writes; a
 final pass inserts the wait states gfx950 requires between producers and
 consumers (MFMA results, VALU -> MFMA operands, transcendental results,
