@@ -3,7 +3,10 @@
 The hand-picked parity cases pin the edges one at a time; this sweep draws
 combinations of them (sequence length, window, stride, dilation, global
 tokens, head sizes, grouped heads, batch, dtype, decode lengths and sink
-slots) from a fixed seed, so every run checks the same configurations.
+slots) from a fixed seed, so every run checks the same configurations; two
+more sweeps draw only shapes the generated kernels serve (grouped-query
+prefill with a plain, dilated or global-token window; differential
+attention at d = 64, dv = 128).
 Tolerances are the parity bar: max-abs 2e-2 for bf16 inputs, 1e-5 for fp32.
 SWA_RANDOM_SCALE=k multiplies the number of drawn configurations by k (the
 default run draws 48; k = 150 draws about 7,000, about a minute on one GPU).
@@ -143,6 +146,38 @@ def long_configs(n, seed):
     return out
 
 
+def asm_prefill_configs(n, seed):
+    """Shapes of the generated prefill kernel (bf16, d = 128, 4 or 8 query
+    heads per key/value head, no stride): a plain, dilated or global-token
+    window, with the log-sum-exp."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 1501))
+        kind = int(rng.integers(0, 3))
+        Hkv = int(rng.integers(1, 3))
+        out.append(dict(dtype="bf16", B=int(rng.integers(1, 3)), Hq=Hkv * int(rng.choice([4, 8])), Hkv=Hkv,
+                        N=N, d=128, dv=128, window=int(rng.integers(1, N + 41)), stride=0,
+                        dilation=int(rng.integers(2, 9)) if kind == 1 else 1,
+                        n_global=int(rng.integers(1, N + 4)) if kind == 2 else 0,
+                        scale=1.0 / math.sqrt(128), seed=5000 + i))
+    return out
+
+
+def asm_diff_configs(n, seed):
+    """Shapes of the generated differential kernel (bf16, d = 64, dv = 128,
+    a window only), lambda from -1 to 2."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 1201))
+        Hkv = int(rng.integers(1, 3))
+        out.append(dict(dtype="bf16", B=int(rng.integers(1, 3)), Hq=Hkv * int(rng.choice([1, 2, 4])), Hkv=Hkv,
+                        N=N, d=64, dv=128, window=int(rng.integers(1, N + 41)), stride=0, dilation=1,
+                        n_global=0, scale=0.125, lam=float(rng.uniform(-1.0, 2.0)), seed=6000 + i))
+    return out
+
+
 def label(c):
     keys = ("dtype", "B", "Hq", "Hkv", "N", "d", "dv", "window", "stride", "dilation", "n_global",
             "n_sink", "two")
@@ -165,6 +200,31 @@ def test_random_prefill(swa, cfg):
     want = oracle.attn_full(q, k, v, cfg["window"], cfg["stride"], cfg["scale"],
                             dilation=cfg["dilation"], n_global=cfg["n_global"])
     assert max_err(host(out), want) <= TOL[dt]
+
+
+@pytest.mark.parametrize("cfg", asm_prefill_configs(12 * SCALE, 17), ids=label)
+def test_random_asm_prefill(swa, cfg):
+    banner(cfg)
+    q, k, v = synth.prefill_inputs(cfg)
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], 0, d=128, dilation=cfg["dilation"],
+                                    n_global=cfg["n_global"])
+    lse = torch.empty((cfg["B"], cfg["Hq"], cfg["N"]), dtype=torch.float32, device="cuda")
+    out = swa.swa_attn_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), cfg["window"], 0, cfg["scale"],
+                           mask, lse=lse)
+    want, want_lse = oracle.attn_full(q, k, v, cfg["window"], 0, cfg["scale"], with_lse=True,
+                                      dilation=cfg["dilation"], n_global=cfg["n_global"])
+    assert max_err(host(out), want) <= TOL["bf16"]
+    assert max_err(host(lse), want_lse) <= 4e-3
+
+
+@pytest.mark.parametrize("cfg", asm_diff_configs(8 * SCALE, 18), ids=label)
+def test_random_asm_diff(swa, cfg):
+    banner(cfg)
+    ins = synth.diff_inputs(cfg)
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], 0, d=64, dv=128, op=swa.SWA_OP_DIFF)
+    out = swa.diff_attn_fwd(*(dev(x, "bf16") for x in ins), cfg["window"], 0, cfg["scale"], cfg["lam"], mask)
+    want = oracle.diff_full(*ins, cfg["window"], 0, cfg["scale"], cfg["lam"])
+    assert max_err(host(out), want) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("cfg", diff_configs(10 * SCALE, 12), ids=label)
