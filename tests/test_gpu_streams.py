@@ -33,13 +33,22 @@ def host(t):
 
 
 def problems(swa):
-    """Three independent problems, inputs on the device, each with its oracle."""
+    """Four independent problems, inputs on the device, each with its oracle:
+    a strided prefill (the HIP kernel), a grouped-query window prefill and a
+    differential prefill (the generated persistent kernels), a decode."""
     pcfg = dict(dtype="bf16", B=1, Hq=8, Hkv=2, N=1500, d=128, dv=128, window=200, stride=37,
                 scale=1.0 / math.sqrt(128), seed=301)
     q, k, v = synth.prefill_inputs(pcfg)
     pmask = swa.swa_block_mask_build(pcfg["N"], pcfg["window"], pcfg["stride"], d=128)
     pin = (dev(q), dev(k), dev(v))
     pwant = oracle.attn_full(q, k, v, pcfg["window"], pcfg["stride"], pcfg["scale"])
+
+    gcfg = dict(dtype="bf16", B=2, Hq=16, Hkv=4, N=2100, d=128, dv=128, window=300, stride=0,
+                scale=1.0 / math.sqrt(128), seed=304)
+    gq, gk, gv = synth.prefill_inputs(gcfg)
+    gmask = swa.swa_block_mask_build(gcfg["N"], gcfg["window"], 0, d=128)
+    gin = (dev(gq), dev(gk), dev(gv))
+    gwant = oracle.attn_full(gq, gk, gv, gcfg["window"], 0, gcfg["scale"])
 
     fcfg = dict(dtype="bf16", B=1, Hq=4, Hkv=4, N=900, d=64, dv=128, window=150, stride=0,
                 scale=0.125, lam=0.5, seed=302)
@@ -58,6 +67,7 @@ def problems(swa):
     calls = {
         "prefill": (lambda: swa.swa_attn_fwd(*pin, pcfg["window"], pcfg["stride"], pcfg["scale"], pmask),
                     pwant),
+        "gqa": (lambda: swa.swa_attn_fwd(*gin, gcfg["window"], 0, gcfg["scale"], gmask), gwant),
         "diff": (lambda: swa.diff_attn_fwd(*fin, fcfg["window"], 0, fcfg["scale"], fcfg["lam"], fmask),
                  fwant),
         "decode": (lambda: swa.swa_attn_decode(*din, dcfg["scale"]), dwant),
@@ -72,7 +82,7 @@ def check(outs, calls):
 
 
 def test_two_streams_interleaved(swa):
-    print("[case] prefill, diff, decode on two streams, interleaved", flush=True)
+    print("[case] prefill, grouped-query prefill, diff, decode on two streams, interleaved", flush=True)
     calls = problems(swa)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
@@ -84,12 +94,14 @@ def test_two_streams_interleaved(swa):
             outs["decode"] = calls["decode"][0]()
         with torch.cuda.stream(s1):
             outs["diff"] = calls["diff"][0]()
+        with torch.cuda.stream(s2):
+            outs["gqa"] = calls["gqa"][0]()
     torch.cuda.synchronize()
     check(outs, calls)
 
 
 def test_two_host_threads(swa):
-    print("[case] prefill and decode from two host threads", flush=True)
+    print("[case] prefill, grouped-query prefill, diff and decode from four host threads", flush=True)
     calls = problems(swa)
     torch.cuda.synchronize()
     outs, errors = {}, []
@@ -104,7 +116,7 @@ def test_two_host_threads(swa):
         except Exception as e:   # reported below, on the main thread
             errors.append(f"{name}: {e!r}")
 
-    threads = [threading.Thread(target=run, args=(n,)) for n in ("prefill", "decode", "diff")]
+    threads = [threading.Thread(target=run, args=(n,)) for n in ("prefill", "decode", "diff", "gqa")]
     for t in threads:
         t.start()
     for t in threads:
