@@ -123,6 +123,20 @@ def test_diff_asm_rows_past_n_read_as_zeros(swa):
     assert float(np.max(np.abs(got - want))) <= TOL
 
 
+def test_diff_asm_longest_sequence(swa):
+    """N at its maximum (2^22), checked on sampled rows, ends included."""
+    N = swa.SWA_MAX_N
+    print(f"[case] diff asm at N={N} (sampled rows)", flush=True)
+    cfg = config(1, 2, 1, N, 200, seed=93)
+    ins = synth.diff_inputs(cfg)
+    got = run(swa, cfg, *ins).reshape(-1, 128)
+    must = [h * N + i for h in range(2) for i in (0, 127, 128, N // 2, N - 129, N - 128, N - 1)]
+    rows = synth.sample_rows(2 * N, 160, seed=94, must=must)
+    want = oracle.diff_rows(*ins, cfg["window"], 0, cfg["scale"], cfg["lam"], rows)
+    assert float(np.max(np.abs(got[rows] - want))) <= TOL
+    assert np.all(np.isfinite(got[-4096:]))
+
+
 def test_diff_asm_deterministic(swa):
     print("[case] diff asm determinism (chained items)", flush=True)
     cfg = config(2, 16, 8, 2100, 500, seed=91)

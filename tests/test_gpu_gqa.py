@@ -229,6 +229,25 @@ def test_gqa_workload_all_rows(swa):
     assert float(np.max(np.abs(got - want))) <= TOL
 
 
+def test_gqa_longest_sequence(swa):
+    """N at its maximum (2^22): the largest byte offsets the generated kernel
+    forms (row offsets, tile offsets and descriptor ranges up to 1 GiB per
+    head), checked on sampled rows of every head, ends included."""
+    N = swa.SWA_MAX_N
+    print(f"[case] gqa at N={N} (sampled rows)", flush=True)
+    cfg = dict(dtype="bf16", B=1, Hq=4, Hkv=1, N=N, d=128, dv=128, window=128, stride=0,
+               scale=1.0 / math.sqrt(128), seed=24)
+    q, k, v = synth.prefill_inputs(cfg)
+    got, lse = run(swa, q, k, v, cfg["window"], cfg["scale"])
+    got = got.reshape(-1, 128)
+    must = [h * N + i for h in range(4) for i in (0, 63, 64, N // 2, N - 65, N - 64, N - 1)]
+    rows = synth.sample_rows(4 * N, 192, seed=25, must=must)
+    want, want_lse = oracle.attn_rows(q, k, v, cfg["window"], 0, cfg["scale"], rows, with_lse=True)
+    assert float(np.max(np.abs(got[rows] - want))) <= TOL
+    assert float(np.max(np.abs(lse.reshape(-1)[rows] - want_lse))) <= LSE_TOL
+    assert np.all(np.isfinite(got[-4096:]))
+
+
 def test_gqa_deterministic(swa):
     cfg = dict(dtype="bf16", B=1, Hq=8, Hkv=2, N=1500, d=128, dv=128, window=300, stride=0,
                scale=1.0 / math.sqrt(128), seed=5)
