@@ -103,7 +103,7 @@ def dma_ops():
     / S_SOFFV (V) into the stage at S_SB: K1 and K2 chunks w and 8 (every
     wave writes the same bytes of chunk 8), V chunks w, w + 8 and
     16 + (w & 3)."""
-    def k_op(P, rs, base, jk):
+    def k_op(rs, base, jk):
         def op(P):
             if jk == 0:
                 P.salu("s_add_u32", "m0", S_SBW, str(base))
@@ -111,8 +111,7 @@ def dma_ops():
                 P.salu("s_add_u32", "m0", S_SB, str(base + 8192))
             P.dma(V_DK[jk], rs, S_SOFFK)
         return op
-    ops = [k_op(None, S_RSK1, 0, 0), k_op(None, S_RSK1, 0, 1), k_op(None, S_RSK2, KTILE, 0),
-           k_op(None, S_RSK2, KTILE, 1)]
+    ops = [k_op(S_RSK1, 0, 0), k_op(S_RSK1, 0, 1), k_op(S_RSK2, KTILE, 0), k_op(S_RSK2, KTILE, 1)]
     for jv in range(3):
         def op(P, jv=jv):
             if jv < 2:
