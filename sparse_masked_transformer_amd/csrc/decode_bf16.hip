@@ -24,8 +24,8 @@
 // nontemporal hint instead.)
 //   * A wave streams its slots 32 at a time: coalesced 16-byte loads into
 //     registers two steps ahead (two register stages; one for two maps with
-//     2 d + dv > 256), then into its own LDS area, rows padded (K +16 bytes,
-//     V +64 bytes) against bank conflicts.
+//     2 d + dv > 256), then into its own LDS area, rows padded by 32 bytes
+//     against bank conflicts.
 //   * The G query heads sharing the key/value head form the 16 columns of a
 //     v_mfma_f32_16x16x32_bf16 (unused columns are zero): S^T = K Q^T with K
 //     from LDS as the A operand; lane l holds head l%16 and keys 4(l/16)+i.
@@ -117,8 +117,12 @@ constexpr float kNegBig = -1e30f;
 
 template <int D, int DV, int NMAPS>
 struct Lay {
-    static constexpr int kRow = 2 * D + 16;    // K row stride in LDS, bytes
-    static constexpr int vRow = 2 * DV + 64;   // V row stride in LDS, bytes
+    // Row strides in LDS, bytes.  Both pad by 32 bytes: measured with the
+    // LDS bank-conflict counter, the 16-byte K reads and the transposed
+    // 8-byte V reads are then conflict-free (K +16 and V +64, the earlier
+    // paddings, left conflicts on 15% and 25% of the LDS cycles).
+    static constexpr int kRow = 2 * D + 32;
+    static constexpr int vRow = 2 * DV + 32;
     static constexpr int kTile = kDecodeStep * kRow;
     static constexpr int vTile = kDecodeStep * vRow;
     static constexpr int wave_bytes = NMAPS * kTile + vTile;
@@ -140,11 +144,17 @@ constexpr int reg_stages() { return NMAPS * D + DV > 256 ? 1 : 2; }
 template <int D, int DV, int NMAPS>
 constexpr int occupancy() { return NMAPS == 2 && (2 * D + DV > 192 || DV == 128) ? 1 : 2; }
 
+// Row stride (floats) of the waves' outputs in the merge area: 16 floats of
+// padding put the rows of four query heads, which one 16-byte store per
+// lane writes, on different banks.
+template <int DV>
+constexpr int kMergeRow = DV + 16;
+
 // LDS bytes of a workgroup: the waves' tiles, or the merge area if larger.
 template <int D, int DV, int NMAPS>
 size_t lds_bytes(int waves, int G) {
     size_t tiles = static_cast<size_t>(waves) * Lay<D, DV, NMAPS>::wave_bytes;
-    size_t merge = static_cast<size_t>(waves) * NMAPS * (2 * 16 + G * DV) * sizeof(float);
+    size_t merge = static_cast<size_t>(waves) * NMAPS * (2 * 16 + G * kMergeRow<DV>) * sizeof(float);
     return tiles > merge ? tiles : merge;
 }
 
@@ -429,7 +439,7 @@ void decode_kernel(Params p) {
     __syncthreads();  // every wave is done with its tiles
     float *mw = reinterpret_cast<float *>(dsm);   // [waves][NMAPS][16]
     float *lw = mw + waves * NMAPS * 16;          // [waves][NMAPS][16]
-    float *ow = lw + waves * NMAPS * 16;          // [waves][NMAPS][Gb][DV]
+    float *ow = lw + waves * NMAPS * 16;          // [waves][NMAPS][Gb][kMergeRow]
     if (grp == 0) {
 #pragma unroll
         for (int m = 0; m < NMAPS; ++m) {
@@ -442,7 +452,8 @@ void decode_kernel(Params p) {
         for (int m = 0; m < NMAPS; ++m)
 #pragma unroll
             for (int db = 0; db < DV / 16; ++db)
-                *reinterpret_cast<f32x4 *>(ow + ((wave * NMAPS + m) * Gb + colq) * DV + db * 16 + grp * 4) =
+                *reinterpret_cast<f32x4 *>(ow + ((wave * NMAPS + m) * Gb + colq) * kMergeRow<DV> + db * 16 +
+                                           grp * 4) =
                     o[m][db];
     }
     __syncthreads();
@@ -459,7 +470,7 @@ void decode_kernel(Params p) {
             for (int w = 0; w < waves; ++w) {
                 const float wgt = __builtin_amdgcn_exp2f(mw[(w * NMAPS + m) * 16 + col] - mstar);
                 l += wgt * lw[(w * NMAPS + m) * 16 + col];
-                acc += wgt * ow[((w * NMAPS + m) * Gb + col) * DV + dd];
+                acc += wgt * ow[((w * NMAPS + m) * Gb + col) * kMergeRow<DV> + dd];
             }
             if (p.splits == 1) {
                 const float r = l > 0.f ? acc / l : 0.f;
