@@ -451,8 +451,9 @@ NW = 8                               # waves per workgroup
 S_BUF = [0, 32]                      # two score buffers of 32 VGPRs: tile j, tile j + 1
 P_BUF = 64                           # probabilities of one tile, bf16 pairs: 16 VGPRs
 V_TID, V_KLANE, V_VLANE, V_KADDR, V_VADDR = v(80), v(81), v(82), v(83), v(84)
-V_DK = [v(85 + i) for i in range(3)]  # LDS-DMA source offsets per lane (K chunks)
-V_DV = [v(88 + i) for i in range(3)]  # (V chunks)
+V_DK = [v(85), v(86)]                # LDS-DMA source offsets per lane: K chunks wave, wave + 8
+V_DV = [v(88), v(89)]                # V chunks wave, wave + 8
+V_DX = v(87)                         # the wave's fifth chunk (V 16 + wave, or K 16)
 V_M = v(91)                          # running maximum (scaled, log2 units)
 V_MTHR = v(92)                       # running maximum + slack
 V_ALPHA = v(93)
@@ -490,7 +491,8 @@ S_K0P = [s(61), s(76)]               # key0 of the tile, by iteration phase
 S_FULL = [s(77), s(60)]              # 1 if every cell of the tile attends this wave's rows, by phase
 S_WM1, S_NINF, S_ONES = s(63), s(64), s(65)
 S_SBW = s(62)                        # DMA stage base + 1024 * wave
-S_WAVE1K3, S_SBW3 = s(72), s(73)     # 1024 * (wave & 3), stage base + that
+S_XOFF = s(72)                       # LDS offset of the wave's fifth chunk within a stage
+S_RSE = s(96, 4)                     # its descriptor: V on waves 0-3, K on waves 4-7
 S_NB = s(33)                         # N * 256: bytes per head, first offset past the rows
 S_FLAG = s(68, 2)
 S_CMP = s(70, 2)
@@ -631,32 +633,32 @@ def class_rows(P, dst, pitch, row_bytes):
 def dma_ops():
     """This wave's LDS-DMA loads of the tile whose key offset (bytes) is
     S_SOFF into the stage at LDS byte S_SB, as a list of emitters (each sets
-    M0 and issues one 1 KiB load).  K chunks wave, wave + 8 and 16 (every
-    wave writes the same bytes of chunk 16); V chunks wave, wave + 8 and
-    16 + (wave & 3)."""
+    M0 and issues one 1 KiB load).  The padded K tile is 17 chunks of 1 KiB
+    and the V tile 20: K chunks wave and wave + 8, V chunks wave and
+    wave + 8, and a fifth chunk through the wave's own descriptor, V chunk
+    16 + wave on waves 0-3 and K chunk 16 on waves 4-7 (the four of them
+    write the same bytes)."""
     ops = []
-    for jk in range(3):
+    for jk in range(2):
         def op(P, jk=jk):
-            if jk < 2:
-                P.salu("s_add_u32", "m0", S_SBW, str(jk * 8192))
-            else:
-                P.salu("s_add_u32", "m0", S_SB, str(16 * 1024))
+            P.salu("s_add_u32", "m0", S_SBW, str(jk * 8192))
             P.dma(V_DK[jk], S_RSK, S_SOFF)
         ops.append(op)
-    for jv in range(3):
+    for jv in range(2):
         def op(P, jv=jv):
-            if jv < 2:
-                P.salu("s_add_u32", "m0", S_SBW, str(KTILE + jv * 8192))
-            else:
-                P.salu("s_add_u32", "m0", S_SBW3, str(KTILE + 16 * 1024))
+            P.salu("s_add_u32", "m0", S_SBW, str(KTILE + jv * 8192))
             P.dma(V_DV[jv], S_RSV, S_SOFF)
         ops.append(op)
+
+    def op(P):
+        P.salu("s_add_u32", "m0", S_SB, S_XOFF)
+        P.dma(V_DX, S_RSE, S_SOFF)
+    ops.append(op)
     return ops
 
 
 def dma_bases(P):
     P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
-    P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
 
 
 def dma_tile(P):
@@ -983,7 +985,6 @@ def setup_ops(pn):
         P.salu("s_and_b32", S_SB, S_X[4], "3")
         P.salu("s_mul_i32", S_SB, S_SB, str(STAGE))
         P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
-        P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
 
     def o4(P):
         P.salu("s_add_u32", S_X[6], S_TLO, S_X[9])
@@ -1237,6 +1238,11 @@ def item_loads(P, first):
         rsrc(P, S_RSV, S_V, S_BG, S_X[6], S_X[6])
         query_head(P, S_X[7])
         rsrc(P, S_RSQ, S_Q, S_X[7], S_X[6], S_X[6])
+    # the fifth DMA chunk's descriptor: V on waves 0-3, K on waves 4-7
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    for h in (0, 2):
+        P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSV.sub(h, 2), S_RSK.sub(h, 2), reads_scc=True,
+               writes_scc=False)
     # Q fragments
     if DIL["on"]:
         P.salu("s_mul_i32", S_X[9], S_R0W, S_PITCH)
@@ -1393,7 +1399,12 @@ def prologue(P):
         P.valu("v_lshlrev_b32", V_DBGL, "2", V_LANE)
     P.salu("s_mov_b32", S_VID, S_WG, writes_scc=False)
     P.salu("s_lshl_b32", S_WAVE1K, S_WAVE, "10")
-    P.salu("s_lshl_b32", S_WAVE1K3, S_WH, "10")
+    # the fifth chunk's LDS offset: KTILE + 1024 (16 + wave) on waves 0-3,
+    # 1024 * 16 on waves 4-7
+    P.salu("s_lshl_b32", S_XOFF, S_WH, "10")
+    P.salu("s_add_u32", S_XOFF, S_XOFF, str(KTILE + 16 * 1024))
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    P.salu("s_cselect_b32", S_XOFF, S_XOFF, str(16 * 1024), reads_scc=True, writes_scc=False)
     P.salu("s_lshl_b32", S_NB, S_N, "8")
     P.salu("s_sub_u32", S_WM1, S_W, "1")
     P.salu("s_mov_b32", S_NINF, "0xff800000", writes_scc=False)
@@ -1441,22 +1452,24 @@ def prologue(P):
     # wave + 8 jv (jv < 2) and 16 + (wave & 3)
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
     P.valu("v_mov_b32", t[9], S_WAVE1K)
-    P.valu("v_mov_b32", t[13], S_WAVE1K3)
-    for jk in range(3):
-        if jk < 2:
-            P.valu("v_add_u32", t[10], t[9], t[8])
-            P.valu("v_add_u32", t[10], str(jk * 8192), t[10])
-        else:
-            P.valu("v_add_u32", t[10], str(16 * 1024), t[8])
+    for jk in range(2):
+        P.valu("v_add_u32", t[10], t[9], t[8])
+        P.valu("v_add_u32", t[10], str(jk * 8192), t[10])
         _chunk_src(P, V_DK[jk], t[10], M272, KROW, t)
-    for jv in range(3):
-        if jv < 2:
-            P.valu("v_add_u32", t[10], t[9], t[8])
-            P.valu("v_add_u32", t[10], str(jv * 8192), t[10])
-        else:
-            P.valu("v_add_u32", t[10], t[13], t[8])
-            P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
+    for jv in range(2):
+        P.valu("v_add_u32", t[10], t[9], t[8])
+        P.valu("v_add_u32", t[10], str(jv * 8192), t[10])
         _chunk_src(P, V_DV[jv], t[10], M320, VROW, t)
+    # the fifth chunk: K chunk 16 on waves 4-7, V chunk 16 + wave on waves 0-3
+    P.valu("v_add_u32", t[10], str(16 * 1024), t[8])
+    _chunk_src(P, t[14], t[10], M272, KROW, t)
+    P.salu("s_lshl_b32", S_X[10], S_WH, "10")
+    P.valu("v_add_u32", t[10], S_X[10], t[8])
+    P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
+    _chunk_src(P, V_DX, t[10], M320, VROW, t)
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    P.salu("s_cselect_b64", "vcc", "-1", "0", reads_scc=True, writes_scc=False)
+    P.valu("v_cndmask_b32", V_DX, t[14], V_DX, "vcc")
     # the first item's loads (stage base 0), all of them in before its set-up
     P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
     item_loads(P, first=True)
@@ -1543,7 +1556,7 @@ def render():
   .amdhsa_system_sgpr_workgroup_id_x 1
   .amdhsa_system_vgpr_workitem_id 0
   .amdhsa_next_free_vgpr 256
-  .amdhsa_next_free_sgpr 96
+  .amdhsa_next_free_sgpr 100
   .amdhsa_accum_offset 128
   .amdhsa_reserve_vcc 1
   .amdhsa_float_denorm_mode_32 3
@@ -1563,7 +1576,7 @@ amdhsa.kernels:
     .private_segment_fixed_size: 0
     .kernarg_segment_align: 8
     .wavefront_size: 64
-    .sgpr_count: 96
+    .sgpr_count: 100
     .vgpr_count: 256
     .agpr_count: 128
     .max_flat_workgroup_size: {64 * NW}

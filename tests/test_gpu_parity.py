@@ -194,6 +194,57 @@ def test_prefill_peaky_scores(swa, dtype):
     assert max_err(got, want) <= TOL[dtype]
 
 
+# every HIP kernel the boundary can pick for these shapes (the generated
+# kernels have their own case): bf16 window and local+strided prefill at
+# d = 32, 64 and 128 with fewer than 4 query heads per key/value head, the
+# bf16 two-map kernel (with a stride, and at d = 32, dv = 64), and the fp32
+# paths
+NAN_TAIL_CASES = [
+    # kind, B, Hq, Hkv, N, d, dv, W, stride
+    ("prefill", 1, 2, 2, 333, 64, 64, 40, 7),
+    ("prefill", 2, 4, 2, 200, 128, 128, 64, 0),
+    ("prefill", 1, 2, 1, 130, 32, 32, 17, 0),
+    ("diff", 1, 2, 2, 300, 64, 128, 70, 9),
+    ("diff", 1, 4, 2, 190, 32, 64, 40, 0),
+]
+
+
+def nan_tail(x, dtype, extra=64):
+    """x on the device as a view at the start of a larger buffer whose rows
+    past it hold NaN (a cache allocated longer than the sequence)."""
+    B, H, N, w = x.shape
+    buf = torch.full((B * H * N + extra, w), float("nan"), device="cuda",
+                     dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    buf[:B * H * N] = dev(x, dtype).reshape(-1, w)
+    return buf[:B * H * N].view(B, H, N, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind,B,Hq,Hkv,N,d,dv,W,s", NAN_TAIL_CASES)
+def test_rows_past_n_read_as_zeros(swa, dtype, kind, B, Hq, Hkv, N, d, dv, W, s):
+    """Queries, keys and values past row N of the last head hold NaN inside
+    the same allocation: the kernels must not let them into any output."""
+    banner(f"NaN past N {kind} {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} dv={dv} W={W} s={s}")
+    cfg = dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dv=dv, window=W, stride=s,
+               scale=1.0 / math.sqrt(d), lam=0.5, seed=900 + N + d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if kind == "prefill":
+        q, k, v = synth.prefill_inputs(cfg)
+        mask = swa.swa_block_mask_build(N, W, s, dtype=tdt, d=d)
+        out = swa.swa_attn_fwd(nan_tail(q, dtype), nan_tail(k, dtype), nan_tail(v, dtype), W, s, cfg["scale"],
+                               mask)
+        want = oracle.attn_full(q, k, v, W, s, cfg["scale"])
+    else:
+        ins = synth.diff_inputs(cfg)
+        mask = swa.swa_block_mask_build(N, W, s, dtype=tdt, d=d, dv=dv, op=swa.SWA_OP_DIFF)
+        out = swa.diff_attn_fwd(*(nan_tail(x, dtype) for x in ins), W, s, cfg["scale"], cfg["lam"], mask)
+        want = oracle.diff_full(*ins, W, s, cfg["scale"], cfg["lam"])
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= TOL[dtype]
+
+
 def test_tiny_fp32_workload_full(swa):
     cfg = synth.workload("tiny_swa_f32")
     banner("workload tiny_swa_f32 (all rows)")
