@@ -71,8 +71,9 @@ for _x in range(KTILE):
 # numbers: score and P buffers, softmax state, temporaries, O, the fragment
 # rings, S_C, S_NINF, S_ONES, S_WM1, S_FLAG and the flag temporaries, S_X)
 V_KLANE, V_VLANE = v(81), v(82)
-V_DK = [v(85), v(86)]                # LDS-DMA source offsets per lane: K chunk w, K chunk 8
-V_DV = [v(87), v(88), v(89)]         # V chunks w, w + 8, 16 + (w & 3)
+V_DK = [v(85)]                       # LDS-DMA source offsets per lane: K chunk w (K1 and K2)
+V_DV = [v(87), v(88)]                # V chunks w, w + 8
+V_DX = v(86)                         # the wave's fifth chunk (V 16 + w, or K 8)
 V_OWL, V_ORDL, V_OST, V_XCH = v(120), v(121), v(122), v(123)
 V_QLANE = v(127)                     # (lane % 32) * 128 + 16 (lane / 32)
 
@@ -92,7 +93,8 @@ S_K0P = [s(61), s(76)]
 S_FULL = [s(77), s(60)]
 S_SBW = s(62)
 S_NBV, S_SOFFV = s(66), s(67)
-S_WAVE1K3, S_SBW3 = s(72), s(73)
+S_XOFF, S_SOFFX, S_NBX, S_SHX = s(73), s(72), s(94), s(95)   # the fifth chunk: LDS offset in a stage,
+S_RSE = s(96, 4)                     # key offset, offset past the rows, row shift, descriptor
 S_VID, S_RGRP = s(92), s(93)
 
 
@@ -100,32 +102,33 @@ S_VID, S_RGRP = s(92), s(93)
 # building blocks of this kernel
 def dma_ops():
     """This wave's LDS-DMA loads of the tile at key offset S_SOFFK (K1, K2)
-    / S_SOFFV (V) into the stage at S_SB: K1 and K2 chunks w and 8 (every
-    wave writes the same bytes of chunk 8), V chunks w, w + 8 and
-    16 + (w & 3)."""
-    def k_op(rs, base, jk):
-        def op(P):
-            if jk == 0:
-                P.salu("s_add_u32", "m0", S_SBW, str(base))
-            else:
-                P.salu("s_add_u32", "m0", S_SB, str(base + 8192))
-            P.dma(V_DK[jk], rs, S_SOFFK)
-        return op
-    ops = [k_op(S_RSK1, 0, 0), k_op(S_RSK1, 0, 1), k_op(S_RSK2, KTILE, 0), k_op(S_RSK2, KTILE, 1)]
-    for jv in range(3):
+    / S_SOFFV (V) into the stage at S_SB.  The padded K1 and K2 tiles are 9
+    chunks of 1 KiB each and the V tile 20: K1 chunk w, K2 chunk w, V chunks
+    w and w + 8, and a fifth chunk through the wave's own descriptor and
+    offset (S_RSE, S_SOFFX): V chunk 16 + w on waves 0-3, K1 chunk 8 on
+    waves 4 and 6, K2 chunk 8 on waves 5 and 7 (two waves write the same
+    bytes)."""
+    ops = []
+    for rs, base in ((S_RSK1, 0), (S_RSK2, KTILE)):
+        def op(P, rs=rs, base=base):
+            P.salu("s_add_u32", "m0", S_SBW, str(base))
+            P.dma(V_DK[0], rs, S_SOFFK)
+        ops.append(op)
+    for jv in range(2):
         def op(P, jv=jv):
-            if jv < 2:
-                P.salu("s_add_u32", "m0", S_SBW, str(2 * KTILE + jv * 8192))
-            else:
-                P.salu("s_add_u32", "m0", S_SBW3, str(2 * KTILE + 16 * 1024))
+            P.salu("s_add_u32", "m0", S_SBW, str(2 * KTILE + jv * 8192))
             P.dma(V_DV[jv], S_RSV, S_SOFFV)
         ops.append(op)
+
+    def op(P):
+        P.salu("s_add_u32", "m0", S_SB, S_XOFF)
+        P.dma(V_DX, S_RSE, S_SOFFX)
+    ops.append(op)
     return ops
 
 
 def dma_tile(P):
     P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
-    P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
     for op in dma_ops():
         op(P)
 
@@ -216,6 +219,7 @@ def setup_ops(pn):
         P.salu("s_add_u32", S_X[4], S_X[9], "2")               # tile i + 2
         P.salu("s_add_u32", S_X[5], S_TLO, S_X[4])
         P.salu("s_lshl_b32", S_X[2], S_X[5], "14")             # V offset (256-byte rows)
+        P.salu("s_lshl_b32", S_X[3], S_X[5], S_SHX)            # the fifth chunk's tensor
         P.salu("s_lshl_b32", S_X[5], S_X[5], "13")             # K offset (128-byte rows)
 
     # past the band the offsets are N rows, out of the descriptors' range:
@@ -224,12 +228,12 @@ def setup_ops(pn):
         P.scmp("s_cmp_lt_u32", S_X[4], S_T)
         P.salu("s_cselect_b32", S_SOFFK, S_X[5], S_NBK, reads_scc=True, writes_scc=False)
         P.salu("s_cselect_b32", S_SOFFV, S_X[2], S_NBV, reads_scc=True, writes_scc=False)
+        P.salu("s_cselect_b32", S_SOFFX, S_X[3], S_NBX, reads_scc=True, writes_scc=False)
 
     def o3(P):
         P.salu("s_and_b32", S_SB, S_X[4], "3")
         P.salu("s_mul_i32", S_SB, S_SB, str(STAGE))
         P.salu("s_add_u32", S_SBW, S_SB, S_WAVE1K)
-        P.salu("s_add_u32", S_SBW3, S_SB, S_WAVE1K3)
 
     def o4(P):
         P.salu("s_add_u32", S_X[6], S_TLO, S_X[9])
@@ -452,6 +456,16 @@ def item_loads(P, first):
     rsrc(P, S_RSK2, S_K2, S_KV, S_X[6], S_X[6])
     P.salu("s_lshl_b32", S_X[7], S_N, "8")
     rsrc(P, S_RSV, S_V, S_KV, S_X[7], S_X[7])
+    # the fifth DMA chunk's descriptor: V on waves 0-3, K1 on waves 4 and
+    # 6, K2 on waves 5 and 7
+    P.scmp("s_bitcmp1_b32", S_WAVE, "0")
+    for h in (0, 2):
+        P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSK2.sub(h, 2), S_RSK1.sub(h, 2), reads_scc=True,
+               writes_scc=False)
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    for h in (0, 2):
+        P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSV.sub(h, 2), S_RSE.sub(h, 2), reads_scc=True,
+               writes_scc=False)
     qsrc = s(S_X[8].i, 2)
     P.scmp("s_cmp_eq_u32", S_MAP, "0")
     P.salu("s_cselect_b64", qsrc, S_Q1, S_Q2, reads_scc=True, writes_scc=False)
@@ -465,10 +479,13 @@ def item_loads(P, first):
     # zeros, never used)
     P.salu("s_lshl_b32", S_SOFFK, S_TLO, "13")
     P.salu("s_lshl_b32", S_SOFFV, S_TLO, "14")
+    P.salu("s_lshl_b32", S_SOFFX, S_TLO, S_SHX)
     P.salu("s_mul_i32", S_SB, S_BASE, str(STAGE))
     dma_tile(P)
     P.salu("s_add_u32", S_SOFFK, S_SOFFK, str(1 << 13))
     P.salu("s_add_u32", S_SOFFV, S_SOFFV, str(1 << 14))
+    P.salu("s_add_u32", S_X[0], S_TLO, "1")
+    P.salu("s_lshl_b32", S_SOFFX, S_X[0], S_SHX)
     P.salu("s_add_u32", S_X[0], S_BASE, "1")
     P.salu("s_and_b32", S_X[0], S_X[0], "3")
     P.salu("s_mul_i32", S_SB, S_X[0], str(STAGE))
@@ -546,9 +563,20 @@ def prologue(P):
     P.salu("s_lshr_b32", S_MAP, S_WAVE, "2")
     P.salu("s_mov_b32", S_VID, S_WG, writes_scc=False)
     P.salu("s_lshl_b32", S_WAVE1K, S_WAVE, "10")
-    P.salu("s_lshl_b32", S_WAVE1K3, S_RGRP, "10")
     P.salu("s_lshl_b32", S_NBK, S_N, "7")
     P.salu("s_lshl_b32", S_NBV, S_N, "8")
+    # the fifth DMA chunk: V chunk 16 + w on waves 0-3 (LDS offset
+    # 2 KTILE + 1024 (16 + w), rows of 256 bytes), K1 / K2 chunk 8 on even /
+    # odd waves 4-7 (8 KiB into the K1 or K2 tile, rows of 128 bytes)
+    P.salu("s_mov_b32", S_X[0], str(8 * 1024), writes_scc=False)
+    P.scmp("s_bitcmp1_b32", S_WAVE, "0")
+    P.salu("s_cselect_b32", S_X[0], str(KTILE + 8 * 1024), S_X[0], reads_scc=True, writes_scc=False)
+    P.salu("s_lshl_b32", S_XOFF, S_RGRP, "10")
+    P.salu("s_add_u32", S_XOFF, S_XOFF, str(2 * KTILE + 16 * 1024))
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    P.salu("s_cselect_b32", S_XOFF, S_XOFF, S_X[0], reads_scc=True, writes_scc=False)
+    P.salu("s_cselect_b32", S_SHX, "14", "13", reads_scc=True, writes_scc=False)
+    P.salu("s_cselect_b32", S_NBX, S_NBV, S_NBK, reads_scc=True, writes_scc=False)
     P.salu("s_sub_u32", S_WM1, S_W, "1")
     P.salu("s_mov_b32", S_NINF, "0xff800000", writes_scc=False)
     P.salu("s_mov_b32", S_ONES, "0x3f803f80", writes_scc=False)
@@ -595,16 +623,20 @@ def prologue(P):
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
     P.valu("v_add_u32", t[10], S_WAVE1K, t[8])
     _chunk_src(P, V_DK[0], t[10], M144, KROW, 7, 2 * D, t)
-    P.valu("v_add_u32", t[10], str(8 * 1024), t[8])
-    _chunk_src(P, V_DK[1], t[10], M144, KROW, 7, 2 * D, t)
-    for jv in range(3):
-        if jv < 2:
-            P.valu("v_add_u32", t[10], S_WAVE1K, t[8])
-            P.valu("v_add_u32", t[10], str(jv * 8192), t[10])
-        else:
-            P.valu("v_add_u32", t[10], S_WAVE1K3, t[8])
-            P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
+    for jv in range(2):
+        P.valu("v_add_u32", t[10], S_WAVE1K, t[8])
+        P.valu("v_add_u32", t[10], str(jv * 8192), t[10])
         _chunk_src(P, V_DV[jv], t[10], M320, VROW, 8, 2 * DV, t)
+    # the fifth chunk: K chunk 8 on waves 4-7, V chunk 16 + w on waves 0-3
+    P.valu("v_add_u32", t[10], str(8 * 1024), t[8])
+    _chunk_src(P, t[14], t[10], M144, KROW, 7, 2 * D, t)
+    P.salu("s_lshl_b32", S_X[0], S_RGRP, "10")
+    P.valu("v_add_u32", t[10], S_X[0], t[8])
+    P.valu("v_add_u32", t[10], str(16 * 1024), t[10])
+    _chunk_src(P, V_DX, t[10], M320, VROW, 8, 2 * DV, t)
+    P.scmp("s_cmp_lt_u32", S_WAVE, "4")
+    P.salu("s_cselect_b64", "vcc", "-1", "0", reads_scc=True, writes_scc=False)
+    P.valu("v_cndmask_b32", V_DX, t[14], V_DX, "vcc")
     P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
     item_loads(P, first=True)
     P.waitcnt(vm=0)
@@ -665,7 +697,7 @@ def render():
   .amdhsa_system_sgpr_workgroup_id_x 1
   .amdhsa_system_vgpr_workitem_id 0
   .amdhsa_next_free_vgpr 256
-  .amdhsa_next_free_sgpr 96
+  .amdhsa_next_free_sgpr 100
   .amdhsa_accum_offset 128
   .amdhsa_reserve_vcc 1
   .amdhsa_float_denorm_mode_32 3
@@ -685,7 +717,7 @@ amdhsa.kernels:
     .private_segment_fixed_size: 0
     .kernarg_segment_align: 8
     .wavefront_size: 64
-    .sgpr_count: 96
+    .sgpr_count: 100
     .vgpr_count: 256
     .agpr_count: 128
     .max_flat_workgroup_size: 512
