@@ -282,7 +282,9 @@ def by_map(P, first_map, second_map):
     P.label(done)
 
 
-def iteration(P, phase, has_qk, has_pv, first):
+def iteration(P, phase, has_qk, has_pv, first, exact=True):
+    """One tile j of the pipeline, as in gen_fwd_gqa (exact=False: no row
+    maximum unless a row's sum of p exceeds 2^SLACK)."""
     sb_cur, sb_next = S_BUF[phase], S_BUF[1 - phase]
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
     if first:
@@ -302,10 +304,12 @@ def iteration(P, phase, has_qk, has_pv, first):
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
         item_loads(P, first=False)
-    valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
-            + v_prefetch_ops() + pack_ops(sb_cur, 1))
+    valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
+            + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
     extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
     interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
+    if not exact:
+        g.max_redo(P, phase, qk=lambda P, sb: interleave(P, mfma_order(True, False), sb, []), stage=STAGE)
     if has_qk:
         k_addr_next(P)
     if not has_pv:
@@ -654,9 +658,17 @@ def kernel_text():
     P.salu("s_add_u32", S_X[0], S_J, "1")
     P.scmp("s_cmp_ge_u32", S_X[0], S_T)
     P.branch("s_cbranch_scc1", ".Llast1")
-    P.label(".Lmid1")
+    # j = 1 and 2 with the row maximum too: every row of the 128 attends a
+    # key of tiles 0 .. 2, so from j = 3 on the running maximum is finite
     for ph in (1, 0):
         iteration(P, ph, True, True, False)
+        P.salu("s_add_u32", S_J, S_J, "1")
+        P.salu("s_add_u32", S_X[0], S_J, "1")
+        P.scmp("s_cmp_ge_u32", S_X[0], S_T)
+        P.branch("s_cbranch_scc1", f".Llast{1 - ph}")
+    P.label(".Lmid1")
+    for ph in (1, 0):
+        iteration(P, ph, True, True, False, exact=False)
         P.salu("s_add_u32", S_J, S_J, "1")
         P.salu("s_add_u32", S_X[0], S_J, "1")
         P.scmp("s_cmp_ge_u32", S_X[0], S_T)

@@ -38,7 +38,8 @@ Software pipeline (one iteration per 64-key tile j)
   matrix cores: O += V(j-1)^T P(j-1) (16 MFMAs: four, then two per QK MFMA)
                 and S(j+1) = K(j+1) Q^T (16 MFMAs, the last ten after the
                 P V product)
-  vector ALU:   row maxima of S(j), then p = exp2(s * c - m), the bf16
+  vector ALU:   (first two tiles of an item, and its last: row maxima of
+                S(j)), then p = exp2(s * c - m), the bf16
                 packing of P(j) into the P buffer (once the P V product has
                 read it) and the row sums, spread evenly between the MFMAs
   LDS:          the fragments of both products, three ahead of their MFMA;
@@ -47,8 +48,12 @@ Software pipeline (one iteration per 64-key tile j)
   DMA:          tile j+2 into the fourth stage (buffer_load ... lds), and
                 the scalar set-up of the next step, spread between the MFMAs
 The running maximum moves only when a tile's maximum exceeds it by more than
-8 (log2 units); O is then rescaled at the start of the next iteration, after
-the products of the old maximum have been accumulated.
+SLACK = 32 (log2 units); O is then rescaled at the start of the next
+iteration, after the products of the old maximum have been accumulated.
+Every row of an item attends a key of its first two tiles, so from the
+third tile on the step takes no row maximum: it checks instead that no
+row's sum of p exceeds 2^SLACK and, only if one does, computes the tile
+again with its maximum (outputs are those of the step with maxima).
 
 Variants (build options, the plain kernel's code unchanged by them) for
 the dilated window and the global tokens of Learn: Sparse & Sliding-Window
@@ -66,6 +71,7 @@ SGPRs written by the VALU, M0 before LDS-DMA) and the s_waitcnt each load's
 consumer needs.
 """
 import os
+import struct
 import sys
 
 # ---------------------------------------------------------------------------
@@ -79,7 +85,12 @@ STAGE = KTILE + VTILE         # 37888
 NSTAGE = 4
 LDS_BYTES = NSTAGE * STAGE    # 151552
 KCH, VCH = KTILE // 1024, VTILE // 1024   # 17, 20 chunks of 1 KiB
-SLACK = 8.0
+# the running maximum m moves only when a tile's maximum exceeds it by more
+# than SLACK (log2 units), so every p = exp2(s c - m) is at most 2^SLACK:
+# bf16 P keeps its relative precision at any magnitude, and the fp32 sums
+# of p and of p v stay finite for |v| up to 2^(128 - SLACK - 10) over 2^10
+# keys.  With 32 a move is rare even on sharply peaked rows.
+SLACK = 32.0
 OROW = 144                    # LDS row of the output staging (half a row of values + 16)
 EPI_STORES = 8                # output stores of an item's epilogue (the log-sum-exp store aside)
 assert 8 * 32 * OROW <= STAGE
@@ -1028,10 +1039,14 @@ def k_addr_next(P):
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
 
 
-def iteration(P, phase, has_qk, has_pv, first):
+def iteration(P, phase, has_qk, has_pv, first, exact=True):
     """One tile j (S_J) of the pipeline; score buffers by phase = j % 2.  The
     last step of an item (no QK product) also starts the loads of the
-    workgroup's next item."""
+    workgroup's next item.  With exact=False the step takes no row maximum:
+    p = exp2(s c - m) with the running maximum m as it stands, and only if
+    some row's sum of this tile's p exceeds 2^SLACK (then a p may exceed
+    it: the tile's maximum may lie more than SLACK above m) is the tile
+    redone with its maximum (max_redo)."""
     sb_cur, sb_next = S_BUF[phase], S_BUF[1 - phase]
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
     # the first step waits for tile 1 of its item, not for the previous
@@ -1050,10 +1065,12 @@ def iteration(P, phase, has_qk, has_pv, first):
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
         item_loads(P, first=False)
-    valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
-            + v_prefetch_ops() + pack_ops(sb_cur, 1))
+    valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
+            + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
     extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
     interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
+    if not exact:
+        max_redo(P, phase)
     if has_qk:
         k_addr_next(P)
     dump(P, f"soft{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32), v(P_BUF, 16), V_M, V_L[0], V_L[1],
@@ -1064,6 +1081,45 @@ def iteration(P, phase, has_qk, has_pv, first):
         # the start of the next step
         P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+
+
+def max_redo(P, phase, qk=None, stage=None):
+    """After a step without the row maximum: if any lane's sum of the tile's
+    p exceeds 2^SLACK, recompute S(j) = K(j) Q^T (tile j is still in its
+    stage, the Q fragments in place), mask it, and take the step's softmax
+    again with the row maximum.  Every wave of the branch starts and ends
+    with no LDS read in flight (the next step's first V^T fragments, read
+    during this step, are waited for here), so both paths join in the same
+    state.  qk(P, sbuf) emits the kernel's QK product into sbuf and stage
+    is its LDS stage size (this kernel's by default)."""
+    sb_cur = S_BUF[phase]
+    if qk is None:
+        def qk(P, sbuf):
+            interleave(P, mfma_order(True, False), sbuf, [])
+    stage = STAGE if stage is None else stage
+    t = V_T[15]
+    P.valu("v_add_f32", t, V_LT[0], V_LT[1])
+    two_slack = struct.unpack("<I", struct.pack("<f", 2.0 ** SLACK))[0]
+    P.salu("s_mov_b32", S_X[13], hex(two_slack), writes_scc=False)   # 2^SLACK
+    P.add(I(f"  v_cmp_lt_f32 {S_CMP}, {S_X[13]}, {t}", "vcmp", regs_of(S_X[13], t), S_CMP.regs()))
+    P.waitcnt(lgkm=0)
+    P.scmp("s_cmp_eq_u64", S_CMP, "0")
+    skip = P.new_label("nomax")
+    P.branch("s_cbranch_scc1", skip)
+    P.salu("s_and_b32", S_X[12], S_J, "3")
+    P.salu("s_mul_i32", S_X[12], S_X[12], str(stage))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    qk(P, sb_cur)
+    P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
+    full = P.new_label("full")
+    P.branch("s_cbranch_scc1", full)
+    mask_block(P, sb_cur, S_K0P[phase])
+    P.label(full)
+    for op in (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
+               + pack_ops(sb_cur, 1)):
+        op(P)
+    P.waitcnt(lgkm=0)
+    P.label(skip)
 
 
 def settle_previous(P):
@@ -1506,14 +1562,21 @@ def kernel_text():
     P.salu("s_add_u32", S_X[0], S_J, "1")
     P.scmp("s_cmp_ge_u32", S_X[0], S_T)
     P.branch("s_cbranch_scc1", ".Llast1")
-    P.label(".Lmid1")
-    for ph in (1, 0):
-        iteration(P, ph, True, True, False)
+    # j = 1 with the row maximum too: every row of the item attends a key of
+    # tiles 0 and 1, so from j = 2 on the running maximum is finite
+    iteration(P, 1, True, True, False)
+    P.salu("s_add_u32", S_J, S_J, "1")
+    P.salu("s_add_u32", S_X[0], S_J, "1")
+    P.scmp("s_cmp_ge_u32", S_X[0], S_T)
+    P.branch("s_cbranch_scc1", ".Llast0")
+    P.label(".Lmid0")
+    for ph in (0, 1):
+        iteration(P, ph, True, True, False, exact=False)
         P.salu("s_add_u32", S_J, S_J, "1")
         P.salu("s_add_u32", S_X[0], S_J, "1")
         P.scmp("s_cmp_ge_u32", S_X[0], S_T)                   # j == T - 1 (>=: a bound)
         P.branch("s_cbranch_scc1", f".Llast{1 - ph}")
-    P.branch("s_branch", ".Lmid1")
+    P.branch("s_branch", ".Lmid0")
     for ph in range(2):
         P.label(f".Llast{ph}")
         iteration(P, ph, False, True, False)
