@@ -105,6 +105,27 @@ def test_diff_asm_peaky_map(swa, which):
     assert float(np.max(np.abs(got - want))) <= TOL
 
 
+@pytest.mark.parametrize("which", [0, 1])
+def test_diff_asm_score_jump_redoes_tile(swa, which):
+    """One map's keys at two positions score about 100 and 150 (log2 units)
+    above every other score, in tiles past the first three of the items that
+    attend them: the steps there take no row maximum, their row-sum check
+    fails, and the tile is computed again with its maximum.  Without that,
+    p = 2^(score - maximum) of the second key would overflow fp32."""
+    print(f"[case] diff asm score jump in map {which + 1}", flush=True)
+    N, W = 1300, 600
+    cfg = config(1, 4, 2, N, W, seed=5151 + which)
+    q1, k1, q2, k2, v = synth.diff_inputs(cfg)
+    q1, q2, k1, k2 = np.abs(q1), np.abs(q2), k1.copy(), k2.copy()
+    kk = k1 if which == 0 else k2
+    for j, val in ((500, 16.0), (901, 24.0)):
+        kk[:, :, j, :] = val
+    got = run(swa, cfg, q1, k1, q2, k2, v)
+    want = oracle.diff_full(q1, k1, q2, k2, v, W, 0, cfg["scale"], cfg["lam"])
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - want))) <= TOL
+
+
 def test_diff_asm_rows_past_n_read_as_zeros(swa):
     """K1, K2 and V are views at the start of larger buffers whose rows past
     N hold NaN: rows past N must read as zeros."""

@@ -189,6 +189,36 @@ def test_gqa_peaky_scores(swa, q_scale, W):
     assert float(np.max(np.abs(lse - want_lse) / np.maximum(1.0, np.abs(want_lse)))) <= LSE_TOL
 
 
+@pytest.mark.parametrize("variant", ["plain", "dilated", "global"])
+def test_gqa_score_jump_redoes_tile(swa, variant):
+    """Keys whose scores lie 80-130 and 160-270 (log2 units) above every
+    other score, in tiles past the first two of the items that attend them:
+    the steps there take no row maximum, their row-sum check fails, and the
+    tile is computed again with its maximum (the running maximum moves
+    twice).  Without that, p = 2^(score - maximum) of the second key would
+    overflow fp32."""
+    print(f"[case] gqa score jump ({variant})", flush=True)
+    N, W = 1300, 600 if variant == "plain" else 300
+    dil, g = (2, 0) if variant == "dilated" else ((1, 64) if variant == "global" else (1, 0))
+    cfg = dict(dtype="bf16", B=1, Hq=8, Hkv=2, N=N, d=128, dv=128, window=W, stride=0,
+               scale=1.0 / math.sqrt(128), seed=4343)
+    q, k, v = synth.prefill_inputs(cfg)
+    q = np.abs(q)                        # q . k > 0 for the positive rows below
+    k = k.copy()
+    for j, val in ((400, 8.0), (901, 16.0)):
+        k[:, :, j, :] = val
+    mask = swa.swa_block_mask_build(N, W, 0, d=128, dilation=dil, n_global=g)
+    lse = torch.empty((1, 8, N), dtype=torch.float32, device="cuda")
+    out = swa.swa_attn_fwd(bf(q), bf(k), bf(v), W, 0, cfg["scale"], mask, lse=lse)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want, want_lse = oracle.attn_full(q, k, v, W, 0, cfg["scale"], with_lse=True, dilation=dil, n_global=g)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - want))) <= TOL
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert float(np.max(np.abs(got_lse - want_lse) / np.maximum(1.0, np.abs(want_lse)))) <= LSE_TOL
+
+
 def test_gqa_rows_past_n_read_as_zeros(swa):
     """K and V are views at the start of larger buffers whose rows past N hold
     NaN: the kernel must read rows past N as zeros (masked keys of the last,
