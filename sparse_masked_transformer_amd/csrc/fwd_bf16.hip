@@ -50,13 +50,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 8.0f;       // log2 units the running maximum may lag
+// log2 units the running maximum may lag: p = exp2(s c - m) stays below
+// 2^kSlack, so bf16 P keeps its relative precision, the fp32 sums of p and
+// p v stay finite for |v| up to 2^(128 - kSlack - 10) over 2^10 keys, and
+// sharply peaked rows seldom move the maximum (and rescale O)
+constexpr float kSlack = 32.0f;
 constexpr float kNegBig = -1e30f;    // running maximum before any key
 constexpr int kThreads = kFwdThreads;
 constexpr int kDiffThreads = kDiffFwdThreads;
@@ -459,20 +464,26 @@ __device__ __forceinline__ void fwd_bf16_body(const Params &p) {
                     o[rg][db] *= alpha[rg];
             };
             bf16x8 pf[RG][2][2];
+            // Row sums over the bf16-rounded p, the values the P V product
+            // accumulates (v_dot2 of a packed pair with ones): the weights of
+            // a row then sum to one exactly after the division, whatever the
+            // running maximum's lag.
             auto softmax_exp = [&](int rg, int kb) {
                 const f32x16 &sv = sh[rg][kb];
                 const float nm = -m_run[rg];
+                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
                 float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     bf16x8 v8;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[hf * 8 + e], p.c, nm));
-                        lsum[e & 3] += pv;
-                        v8[e] = (__bf16)pv;
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        v8[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[hf * 8 + e], p.c, nm));
                     pf[rg][kb][hf] = v8;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v8[2 * e], v8[2 * e + 1]}, ones, lsum[e],
+                                                                  false);
                 }
                 l_run[rg] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
             };
