@@ -3,11 +3,13 @@
 // dilated variant swa_fwd_gqa_d128_dil (each residue class of the rows mod
 // the dilation walked as a plain window) and global-token variant
 // swa_fwd_gqa_d128_glb (the global columns' tiles walked ahead of the band),
-// and diff_fwd_d64_dv128
+// diff_fwd_d64_dv128
 // (differential sliding-window forward, bf16, d = 64, dv = 128;
-// gen_fwd_diff.py).  Their code objects are embedded in this library
+// gen_fwd_diff.py) and swa_fwd_mha_d64_str (multi-head window with an
+// optional power-of-two stride pattern, bf16, d = 64; gen_fwd_str.py).
+// Their code objects are embedded in this library
 // (fwd_gqa_blob.cpp, fwd_gqa_dil_blob.cpp, fwd_gqa_glb_blob.cpp,
-// fwd_diff_blob.cpp, made by the
+// fwd_diff_blob.cpp, fwd_str_blob.cpp, made by the
 // build from the generated .s files) and loaded once per device.  All run a
 // persistent grid of one 512-lane workgroup per compute unit.
 #include <mutex>
@@ -24,6 +26,8 @@ extern const unsigned char kFwdGqaGlbCodeObject[];
 extern const size_t kFwdGqaGlbCodeObjectSize;
 extern const unsigned char kFwdDiffCodeObject[];
 extern const size_t kFwdDiffCodeObjectSize;
+extern const unsigned char kFwdStrCodeObject[];
+extern const size_t kFwdStrCodeObjectSize;
 
 namespace {
 
@@ -50,9 +54,21 @@ struct DiffArgs {
 };
 static_assert(sizeof(DiffArgs) == 80, "kernel argument block is 80 bytes");
 
+struct StrArgs {
+    const void *q, *k, *v;
+    void *out;
+    float *lse;
+    int32_t N, window, items, stride, row_blocks;
+    float c;
+    int32_t key_stride;   // stride pattern s (a power of two), or 0
+    int32_t log2_stride;  // log2 s (0 without a stride)
+    int32_t pad[2];
+};
+static_assert(sizeof(StrArgs) == 80, "kernel argument block is 80 bytes");
+
 constexpr int kMaxDevices = 64;
 
-enum AsmKernel { kGqa = 0, kGqaDil = 1, kGqaGlb = 2, kDiff = 3, kNumAsm = 4 };
+enum AsmKernel { kGqa = 0, kGqaDil = 1, kGqaGlb = 2, kDiff = 3, kStr = 4, kNumAsm = 5 };
 
 // The kernel function `which` on the current device and that device's
 // compute unit count.
@@ -61,9 +77,11 @@ hipError_t asm_function(AsmKernel which, hipFunction_t *fn, int *cus) {
     static hipFunction_t fns[kMaxDevices][kNumAsm] = {};
     static int cu_count[kMaxDevices] = {};
     static const unsigned char *const images[kNumAsm] = {kFwdGqaCodeObject, kFwdGqaDilCodeObject,
-                                                         kFwdGqaGlbCodeObject, kFwdDiffCodeObject};
+                                                         kFwdGqaGlbCodeObject, kFwdDiffCodeObject,
+                                                         kFwdStrCodeObject};
     static const char *const names[kNumAsm] = {"swa_fwd_gqa_d128", "swa_fwd_gqa_d128_dil",
-                                               "swa_fwd_gqa_d128_glb", "diff_fwd_d64_dv128"};
+                                               "swa_fwd_gqa_d128_glb", "diff_fwd_d64_dv128",
+                                               "swa_fwd_mha_d64_str"};
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -200,6 +218,56 @@ hipError_t launch_fwd_diff_asm(const FwdArgs &a, hipStream_t stream) {
     k.items = static_cast<int32_t>(items);
     k.stride = persistent_grid(items, cus);
     k.row_blocks = (a.N + 127) / 128;
+    return launch(fn, &k, sizeof(k), k.stride, stream);
+}
+
+namespace {
+// log2 of a stride the multi-head kernel takes (a power of two from 64 to
+// 2^18: a 64-key tile then holds at most one stride key, and gathered key
+// offsets stay below 2^32 bytes for N up to 2^22), else -1
+int str_log2(int stride) {
+    for (int k = 6; k <= 18; ++k)
+        if (stride == (1 << k))
+            return k;
+    return -1;
+}
+}  // namespace
+
+bool fwd_str_applies(const FwdArgs &a) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.Hq;
+    return a.nmaps == 1 && a.d == 64 && a.dv == 64 && a.Hq == a.Hkv && heads % 2 == 0 &&
+           a.dilation == 1 && a.n_global == 0 && (a.stride == 0 || str_log2(a.stride) > 0);
+}
+
+int64_t fwd_str_items(const FwdArgs &a) {
+    // one item per (pair of consecutive (batch, head) indices, block of 128
+    // query rows)
+    return static_cast<int64_t>(a.B) * a.Hq / 2 * ((a.N + 127) / 128);
+}
+
+hipError_t launch_fwd_str(const FwdArgs &a, hipStream_t stream) {
+    hipFunction_t fn = nullptr;
+    int cus = 0;
+    hipError_t e = asm_function(kStr, &fn, &cus);
+    if (e != hipSuccess)
+        return e;
+    StrArgs k{};
+    k.q = a.q[0];
+    k.k = a.k[0];
+    k.v = a.v;
+    k.out = a.out;
+    k.lse = a.lse;
+    k.N = a.N;
+    k.window = a.window < a.N ? a.window : a.N;
+    k.c = a.scale * 1.4426950408889634f;
+    const int64_t items = fwd_str_items(a);
+    if (items <= 0 || items > INT32_MAX)
+        return hipErrorInvalidValue;
+    k.items = static_cast<int32_t>(items);
+    k.stride = persistent_grid(items, cus);
+    k.row_blocks = (a.N + 127) / 128;
+    k.key_stride = a.stride;
+    k.log2_stride = a.stride > 0 ? str_log2(a.stride) : 0;
     return launch(fn, &k, sizeof(k), k.stride, stream);
 }
 

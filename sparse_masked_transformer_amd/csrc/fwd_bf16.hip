@@ -704,6 +704,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
         return launch_fwd_gqa(a, stream);
     if (fwd_diff_asm_applies(a))
         return launch_fwd_diff_asm(a, stream);
+    if (fwd_str_applies(a))
+        return launch_fwd_str(a, stream);
     if (a.nmaps == 1) {
         switch (a.d) {
         case 32: return launch<32, 32, 1>(a, stream);

@@ -358,8 +358,27 @@ def _nops(n):
     return out
 
 
+def check_scc(ins):
+    """Every reader of SCC reads the flag its producer of that kind set: a
+    select or a conditional branch the last compare, an add with carry the
+    last add (no other SCC writer between them, no label or branch)."""
+    last = None
+    for x in ins:
+        if x.kind in ("label", "branch") and not (x.kind == "branch" and "scc" in x.text):
+            last = None
+            continue
+        op = x.text.split()[0] if x.text.strip() else ""
+        if SCC <= x.reads:
+            want = ("s_add_u32", "s_addc_u32") if op == "s_addc_u32" else ("s_cmp", "s_bitcmp")
+            if last is None or not last.startswith(want):
+                raise ValueError(f"{x.text.strip()} reads SCC set by {last}")
+        if SCC <= x.writes:
+            last = op
+
+
 def resolve(ins):
     """Insert s_nop for hazards and s_waitcnt for load consumers."""
+    check_scc(ins)
     out = []
     hist = []           # (wait-state index, instruction)
     ws = 0
@@ -777,10 +796,11 @@ def exp_ops(sbuf, kb):
     return ops
 
 
-def pack_ops(sbuf, kb):
+def pack_ops(sbuf, kb, vlast=None):
     """The probabilities of key half kb packed to bf16 pairs into the P
     buffer (the B operand of the P V product), and the row sums of the
-    packed values."""
+    packed values.  vlast: the last V^T fragment of the current P V product
+    that reads key half kb (8 kb + 7 at value head size 128)."""
     sv = [v(sbuf + 16 * kb + k) for k in range(16)]
     pv = [v(P_BUF + 8 * kb + i) for i in range(8)]
     lt = V_LT
@@ -789,7 +809,7 @@ def pack_ops(sbuf, kb):
     # of the current P V product)
     for i in range(8):
         ops.append(after(lambda P, i=i: P.valu("v_cvt_pk_bf16_f32", pv[i], sv[2 * i], sv[2 * i + 1]),
-                         "v", 8 * kb + 7))
+                         "v", 8 * kb + 7 if vlast is None else vlast))
     if not OPT["fp32_sums"]:
         for i in range(8):
             a_ = i % 2            # (key half 0 initializes both partials)
@@ -854,11 +874,12 @@ def mask_block(P, sbuf, k0):
             P.valu("v_bitop3_b32", sr, sr, S_NINF, tk, extra="bitop3:0xe4")
 
 
-def rescale_block(P, with_o=True):
+def rescale_block(P, with_o=True, o=None):
     """The running maximum moved (rare): alpha = exp2(m_old - m_new), the
     threshold follows the maximum, the running sum and (once a P V product
     has been accumulated) O are rescaled, after every product of the old
-    maximum."""
+    maximum.  o: the O accumulators (A_O by default)."""
+    o = A_O if o is None else o
     tmp = V_T
     P.valu("v_sub_f32", tmp[0], V_MOLD, V_M)
     P.valu("v_exp_f32", V_ALPHA, tmp[0], kind="trans")
@@ -867,15 +888,15 @@ def rescale_block(P, with_o=True):
     P.valu("v_mul_f32", V_L[1], V_L[1], V_ALPHA)
     if not with_o:
         return
-    for k0 in range(0, 64, 8):
+    for k0 in range(0, o.n, 8):
         for k in range(8):
-            P.add(I(f"  v_accvgpr_read_b32 {tmp[k]}, {A_O.sub(k0 + k)}", "valu",
-                    A_O.sub(k0 + k).regs(), tmp[k].regs()))
+            P.add(I(f"  v_accvgpr_read_b32 {tmp[k]}, {o.sub(k0 + k)}", "valu",
+                    o.sub(k0 + k).regs(), tmp[k].regs()))
         for k in range(8):
             P.valu("v_mul_f32", tmp[k], tmp[k], V_ALPHA)
         for k in range(8):
-            P.add(I(f"  v_accvgpr_write_b32 {A_O.sub(k0 + k)}, {tmp[k]}", "valu",
-                    tmp[k].regs(), A_O.sub(k0 + k).regs()))
+            P.add(I(f"  v_accvgpr_write_b32 {o.sub(k0 + k)}, {tmp[k]}", "valu",
+                    tmp[k].regs(), o.sub(k0 + k).regs()))
 
 
 # ---------------------------------------------------------------------------
@@ -1083,7 +1104,7 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
 
 
-def max_redo(P, phase, qk=None, stage=None):
+def max_redo(P, phase, qk=None, stage=None, mask=None):
     """After a step without the row maximum: if any lane's sum of the tile's
     p exceeds 2^SLACK, recompute S(j) = K(j) Q^T (tile j is still in its
     stage, the Q fragments in place), mask it, and take the step's softmax
@@ -1091,7 +1112,8 @@ def max_redo(P, phase, qk=None, stage=None):
     with no LDS read in flight (the next step's first V^T fragments, read
     during this step, are waited for here), so both paths join in the same
     state.  qk(P, sbuf) emits the kernel's QK product into sbuf and stage
-    is its LDS stage size (this kernel's by default)."""
+    is its LDS stage size (this kernel's by default); mask(P, phase), when
+    given, masks the recomputed tile in place of this kernel's mask."""
     sb_cur = S_BUF[phase]
     if qk is None:
         def qk(P, sbuf):
@@ -1110,11 +1132,14 @@ def max_redo(P, phase, qk=None, stage=None):
     P.salu("s_mul_i32", S_X[12], S_X[12], str(stage))
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
     qk(P, sb_cur)
-    P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
-    full = P.new_label("full")
-    P.branch("s_cbranch_scc1", full)
-    mask_block(P, sb_cur, S_K0P[phase])
-    P.label(full)
+    if mask is not None:
+        mask(P, phase)
+    else:
+        P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
+        full = P.new_label("full")
+        P.branch("s_cbranch_scc1", full)
+        mask_block(P, sb_cur, S_K0P[phase])
+        P.label(full)
     for op in (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
                + pack_ops(sb_cur, 1)):
         op(P)
@@ -1122,14 +1147,15 @@ def max_redo(P, phase, qk=None, stage=None):
     P.label(skip)
 
 
-def settle_previous(P):
+def settle_previous(P, o=None):
     """Between the P V products of the previous tile and of this one: if the
     previous tile moved the running maximum, rescale l and O (rare), then add
-    the previous tile's row sums to l."""
+    the previous tile's row sums to l.  o: the O accumulators (A_O by
+    default)."""
     skip = P.new_label("norescale")
     P.scmp("s_cmp_eq_u64", S_FLAG, "0")
     P.branch("s_cbranch_scc1", skip)
-    rescale_block(P, with_o=True)
+    rescale_block(P, with_o=True, o=o)
     P.label(skip)
     P.valu("v_add_f32", V_L[0], V_L[0], V_LT[0])
     P.valu("v_add_f32", V_L[1], V_L[1], V_LT[1])

@@ -157,6 +157,11 @@ hipError_t launch_fwd_gqa(const FwdArgs &a, hipStream_t stream);
 bool fwd_diff_asm_applies(const FwdArgs &a);
 int64_t fwd_diff_asm_items(const FwdArgs &a);
 hipError_t launch_fwd_diff_asm(const FwdArgs &a, hipStream_t stream);
+// The multi-head kernel for bf16, d = dv = 64, a window with an optional
+// power-of-two stride pattern (64 .. 2^18), B * Hq even.
+bool fwd_str_applies(const FwdArgs &a);
+int64_t fwd_str_items(const FwdArgs &a);
+hipError_t launch_fwd_str(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t stream);
