@@ -555,10 +555,15 @@ def main():
         s = res["strided"]
         t_hbm = s["alg_bytes"] / (PEAK_HBM_GBS * 1e9)
         t_mfma = s["alg_flops"] / (PEAK_BF16_TFLOPS * 1e12)
-        line["strided"] = {"workload": "local_strided_bf16", "tflops": round(s["tflops"], 2),
+        ssrc = os.path.join(ROOT, "sparse_masked_transformer_amd", "csrc", "gen_fwd_str.py")
+        line["strided"] = {"workload": "local_strided_bf16", "kernel": "swa_fwd_mha_d64_str",
+                           "tflops": round(s["tflops"], 2),
                            "gbs": round(s["gbs"], 1), "us": round(s["event_ms"] * 1e3, 2),
+                           "isolated_median_us": round(s["median_ms"] * 1e3, 2),
                            "roofline_frac": round(max(t_hbm, t_mfma) / (s["event_ms"] * 1e-3), 4),
-                           "bound": "hbm" if t_hbm > t_mfma else "mfma"}
+                           "bound": "hbm" if t_hbm > t_mfma else "mfma",
+                           "traffic": traffic_record([ssrc, os.path.join(os.path.dirname(ssrc), "gen_fwd_gqa.py")],
+                                                     "fwd_str_local_strided")}
     for key in ("global", "dilated"):
         if key in res:
             x = res[key]
@@ -570,7 +575,9 @@ def main():
         line["diff"] = {"workload": "diff_bf16", "kernel": "diff_fwd_d64_dv128", "tflops": round(f["tflops"], 2),
                         "tflops_512_per_cell": round(f["tflops_formula"], 2),
                         "us": round(f["event_ms"] * 1e3, 2),
-                        "roofline_frac": round(f["tflops"] / PEAK_BF16_TFLOPS, 4)}
+                        "roofline_frac": round(f["tflops"] / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_record([os.path.join(ROOT, "sparse_masked_transformer_amd", "csrc", x)
+                                                   for x in ("gen_fwd_diff.py", "gen_fwd_gqa.py")], "diff_bf16")}
         if peaks:
             line["diff"]["frac_measured"] = round(f["tflops"] / peaks["mfma_bf16_tflops"], 4)
     if "tiny_f32" in res:

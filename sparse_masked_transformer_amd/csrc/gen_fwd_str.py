@@ -14,9 +14,11 @@ Work decomposition
   (B * H even; the key/value head of a query head is itself).  Wave w takes
   head bh0 + (w >> 2) and rows 32 (w & 3) .. +31, so waves w and w + 4 share
   a SIMD, the rows and the key tiles they walk.  LDS stages (four) hold per
-  64-key tile the K and V tiles of both heads (64 rows of 128 bytes, padded
-  to 144; 36,864 bytes per stage, 147,456 in all): one workgroup per CU,
-  two waves per SIMD.  Per tile a wave issues 8 MFMAs of S^T = K Q^T and 8
+  64-key tile the K and V tiles of both heads (K: 64 rows of 128 bytes,
+  padded to 144; V: 32 pairs of rows at a pitch of 320 bytes, so that any
+  four consecutive rows fall on disjoint LDS banks for the transposed
+  reads; 38,912 bytes per stage, 155,648 in all): one workgroup per CU, two
+  waves per SIMD.  Per tile a wave issues 8 MFMAs of S^T = K Q^T and 8
   of O^T += V^T P^T.
   An item walks first its prefix, the stride keys below its band (keys
   0, s, 2 s, ... below the band's first key: every row of the item attends
@@ -34,6 +36,7 @@ gen_fwd_gqa.py (imported with their register assignments), as in
 gen_fwd_diff.py.
 """
 import os
+import struct
 import sys
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -43,35 +46,45 @@ from gen_fwd_gqa import (I, Prog, v, s, regs_of, EMPTY, resolve,  # noqa: E402
                          settle_previous, after, AHEAD, RING, SLACK,
                          S_BUF, P_BUF, V_KLANE, V_VLANE, V_KADDR, V_VADDR, V_M, V_MTHR, V_L, V_LT,
                          V_IBASE, V_COL, V_HL, V_T, V_LANE, A_KR, A_VR, S_C, S_NINF, S_ONES, S_WM1,
-                         S_FLAG, S_X)
+                         S_FLAG, S_CMP, S_X)
 
 # ---------------------------------------------------------------------------
 # sizes
 D = 64                        # head size (q, k, v)
-ROW = 2 * D + 16              # padded LDS row of a K or V tile, bytes
-TILE = 64 * ROW               # 9216: 9 chunks of 1 KiB
-STAGE = 4 * TILE              # K of both heads, then V of both heads
+ROW = 2 * D + 16              # padded LDS row of a K tile, bytes
+KTILE = 64 * ROW              # 9216: 9 chunks of 1 KiB
+VPAIR = 4 * D + 64            # LDS pitch of a pair of V rows (two rows of 128 bytes, 64 bytes of padding)
+VTILE = 32 * VPAIR            # 10240: 10 chunks
+STAGE = 2 * KTILE + 2 * VTILE  # K of both heads, then V of both heads
 NSTAGE = 4
-LDS_BYTES = NSTAGE * STAGE    # 147456
+LDS_BYTES = NSTAGE * STAGE    # 155648
+TILE_OFF = (0, KTILE, 2 * KTILE, 2 * KTILE + VTILE)   # K0, K1, V0, V1 within a stage
+# the chunks past 8 of each tile (K0 8, K1 8, V0 8, V0 9, V1 8, V1 9): the
+# fifth DMA load of waves 0..5; waves 6 and 7 repeat those of waves 0 and 1
+FIFTH = [(0, 8), (1, 8), (2, 8), (2, 9), (3, 8), (3, 9), (0, 8), (1, 8)]
 OROW = 2 * D + 16             # LDS row of the output staging
 EPI_STORES = 4                # output stores of a wave per item (the log-sum-exp store aside)
 KARG_BYTES = 80
 NAME = "swa_fwd_mha_d64_str"
-assert 8 * 32 * OROW <= STAGE
-assert TILE % 1024 == 0
+assert 8 * 32 * OROW <= STAGE and LDS_BYTES <= 160 * 1024
+assert KTILE % 1024 == 0 and VTILE % 1024 == 0
 
-# floor(x / 144) as (x * M144) >> 24 over a tile
+# floor(x / 144) and floor(x / 320) as (x * M) >> 24 over a tile
 M144 = -(-(1 << 24) // ROW)
-for _x in range(TILE):
-    assert (_x * M144) >> 24 == _x // ROW
+M320 = -(-(1 << 24) // VPAIR)
+for _x in range(VTILE):
+    assert (_x * M144) >> 24 == _x // ROW and (_x * M320) >> 24 == _x // VPAIR
 
 # ---------------------------------------------------------------------------
 # registers (the ones shared with the imported building blocks keep their
 # numbers: score and P buffers, softmax state, temporaries, the fragment
 # rings, S_C, S_NINF, S_ONES, S_WM1, S_FLAG and the flag temporaries, S_X)
-V_DB, V_DB8 = v(85), v(86)           # LDS-DMA source offsets per lane, band tile: chunk w, chunk 8
-V_DP, V_DP8 = v(87), v(88)           # the same for a prefix tile (row pitch s rows)
-V_DC, V_DC8 = v(89), v(90)           # the ones of the tile being loaded
+# LDS-DMA source offsets per lane: K chunk w, V chunk w and the wave's
+# fifth chunk, for the rows of a band tile (pitch 128 bytes), of a prefix
+# tile (pitch s rows) and of the tile being loaded
+V_DBK, V_DBV, V_DB5 = v(85), v(86), v(80)
+V_DPK, V_DPV, V_DP5 = v(87), v(88), v(124)
+V_DCK, V_DCV, V_DC5 = v(89), v(90), v(126)
 V_HL0 = v(100)                       # 1 on the lanes of the first key quad (lane < 32), else 0
 V_LOFF = v(101)                      # log-sum-exp store offset: row * 4
 V_OWL, V_ORDL, V_OST = v(120), v(121), v(122)
@@ -94,27 +107,27 @@ S_K0P = [s(61), s(76)]               # 2 partial prefix tile; key0 (prefix: 64 x
 S_SBW, S_SOFF, S_SB, S_XOFF = s(62), s(66), s(67), s(72)
 assert (S_WM1.i, S_NINF.i, S_ONES.i, S_FLAG.i) == (63, 64, 65, 68)
 S_RSL, S_RSE = s(92, 4), s(96, 4)    # log-sum-exp; the wave's fifth DMA chunk
+S_FIFTH = s(73)                      # the tile (0..3: K0, K1, V0, V1) of the wave's fifth chunk
 
 
 # ---------------------------------------------------------------------------
 # building blocks of this kernel
 def dma_ops():
     """This wave's LDS-DMA loads of the tile at key offset S_SOFF into the
-    stage at S_SB, with lane offsets V_DC / V_DC8 (band or prefix rows).
-    The stage holds 4 tiles of 9 chunks of 1 KiB (K of heads 0 and 1, V of
-    heads 0 and 1, identical layouts): wave w loads chunk w of each, and
-    chunk 8 of tile w & 3 through its own descriptor (waves w and w + 4
-    write the same bytes)."""
+    stage at S_SB, with lane offsets V_DCK / V_DCV / V_DC5 (band or prefix
+    rows).  The stage holds the K tiles of heads 0 and 1 (9 chunks of 1 KiB
+    each) and their V tiles (10 chunks each): wave w loads chunk w of each,
+    and a fifth chunk (FIFTH) through its own descriptor."""
     ops = []
     for k, rs in enumerate((S_RSK0, S_RSK1, S_RSV0, S_RSV1)):
         def op(P, k=k, rs=rs):
-            P.salu("s_add_u32", "m0", S_SBW, str(k * TILE))
-            P.dma(V_DC, rs, S_SOFF)
+            P.salu("s_add_u32", "m0", S_SBW, str(TILE_OFF[k]))
+            P.dma(V_DCK if k < 2 else V_DCV, rs, S_SOFF)
         ops.append(op)
 
     def op(P):
         P.salu("s_add_u32", "m0", S_SB, S_XOFF)
-        P.dma(V_DC8, S_RSE, S_SOFF)
+        P.dma(V_DC5, S_RSE, S_SOFF)
     ops.append(op)
     return ops
 
@@ -143,9 +156,9 @@ def pv_read(P, n):
     kstep, db = divmod(n, 2)
     kb, hf = divmod(kstep, 2)
     slot = A_VR.sub(4 * (n % RING), 4)
-    off = (kb * 32 + hf * 16) * ROW + db * 64
+    off = (kb * 32 + hf * 16) // 2 * VPAIR + db * 64
     P.ds_read("ds_read_b64_tr_b16", slot.sub(0, 2), V_VADDR, off)
-    P.ds_read("ds_read_b64_tr_b16", slot.sub(2, 2), V_VADDR, off + 8 * ROW)
+    P.ds_read("ds_read_b64_tr_b16", slot.sub(2, 2), V_VADDR, off + 4 * VPAIR)
 
 
 def pv_mfma(P, n):
@@ -302,7 +315,7 @@ def tile_src(P, q, off_band, off_pre):
     """For step q of the item (SGPR): the key offset of its tile into
     S_SOFF (past the item's tiles: N rows, outside the descriptors, so the
     loads read zeros into a stage nothing reads) and its lane offsets into
-    V_DC / V_DC8.  off_band / off_pre are scalar temporaries."""
+    V_DCK / V_DCV / V_DC5.  off_band / off_pre are scalar temporaries."""
     P.salu("s_add_u32", off_band, S_TLO, q)
     P.salu("s_lshl_b32", off_band, off_band, "13")                    # band tile: 64 rows of 128 bytes
     P.salu("s_sub_u32", off_pre, q, S_BASE)
@@ -311,8 +324,8 @@ def tile_src(P, q, off_band, off_pre):
     P.scmp("s_cmp_lt_u32", q, S_PEND)
     P.salu("s_cselect_b32", S_SOFF, off_pre, off_band, reads_scc=True, writes_scc=False)
     P.salu("s_cselect_b64", s(S_X[2].i, 2), "-1", "0", reads_scc=True, writes_scc=False)
-    P.valu("v_cndmask_b32", V_DC, V_DB, V_DP, s(S_X[2].i, 2))
-    P.valu("v_cndmask_b32", V_DC8, V_DB8, V_DP8, s(S_X[2].i, 2))
+    for dc, db, dp in ((V_DCK, V_DBK, V_DPK), (V_DCV, V_DBV, V_DPV), (V_DC5, V_DB5, V_DP5)):
+        P.valu("v_cndmask_b32", dc, db, dp, s(S_X[2].i, 2))
     P.scmp("s_cmp_lt_u32", q, S_T)
     P.salu("s_cselect_b32", S_SOFF, S_SOFF, S_NB, reads_scc=True, writes_scc=False)
 
@@ -391,9 +404,51 @@ def k_addr_next(P):
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
 
 
+def redo_previous(P, phase):
+    """At the start of step j + 1 (phase `phase`): if a row's sum of the p
+    of tile j, taken without the row maximum, exceeds 2^SLACK (flag S_CMP,
+    set at the end of step j), compute S(j) = K(j) Q^T again (tile j is
+    still in its stage, the Q fragments in place; its score buffer is free),
+    mask it, and take its softmax again with the row maximum, before the
+    running sum and O take in tile j.  Placed after the barrier, the check
+    waits for nothing the step does not wait for anyway."""
+    p = 1 - phase
+    sb = S_BUF[p]
+    skip = P.new_label("nomax")
+    P.scmp("s_cmp_eq_u64", S_CMP, "0")
+    P.branch("s_cbranch_scc1", skip)
+    P.salu("s_add_u32", S_X[12], S_J, "-1")
+    P.salu("s_and_b32", S_X[12], S_X[12], "3")
+    P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    interleave(P, mfma_order(True, False), sb, [])
+    mask(P, p)
+    for op in max_ops(sb) + merge_rr([exp_ops(sb, 0), exp_ops(sb, 1)]) + pack(sb, 0) + pack(sb, 1):
+        op(P)
+    P.salu("s_add_u32", S_X[12], S_J, "1")                     # the K fragments of this step's product
+    P.salu("s_and_b32", S_X[12], S_X[12], "3")
+    P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
+    P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    P.label(skip)
+
+
+def sum_check(P):
+    """S_CMP = the lanes whose sum of this tile's p exceeds 2^SLACK (a p
+    may then exceed it: the tile's maximum may lie more than SLACK above
+    the running maximum)."""
+    t = V_T[15]
+    P.valu("v_add_f32", t, V_LT[0], V_LT[1])
+    two_slack = struct.unpack("<I", struct.pack("<f", 2.0 ** SLACK))[0]
+    P.salu("s_mov_b32", S_X[13], hex(two_slack), writes_scc=False)
+    P.add(I(f"  v_cmp_lt_f32 {S_CMP}, {S_X[13]}, {t}", "vcmp", regs_of(S_X[13], t), S_CMP.regs()))
+
+
 def iteration(P, phase, has_qk, has_pv, first, exact=True):
-    """One tile j of the pipeline, as in gen_fwd_gqa (exact=False: no row
-    maximum unless a row's sum of p exceeds 2^SLACK)."""
+    """One tile j of the pipeline, as in gen_fwd_gqa.  exact=False: no row
+    maximum; the row sums are checked at the end of the step and, where
+    one exceeds 2^SLACK, the step is redone at the start of the next
+    (redo_previous).  Every step but an item's first starts with that
+    check of its predecessor (an exact step clears the flag)."""
     sb_cur, sb_next = S_BUF[phase], S_BUF[1 - phase]
     P.comment(f"iteration phase {phase} qk={has_qk} pv={has_pv}")
     # the first step waits for tile 1 of its item, not for the previous
@@ -401,6 +456,7 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     P.waitcnt(vm=EPI_STORES if first else 0)
     P.barrier()
     if has_pv:
+        redo_previous(P, phase)
         settle_previous(P, o=A_O)
     mask(P, phase)
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
@@ -410,10 +466,11 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
             + pack(sb_cur, 0) + v_prefetch_ops() + pack(sb_cur, 1))
     extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
     interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
-    if not exact:
-        g.max_redo(P, phase, qk=lambda P, sb: interleave(P, mfma_order(True, False), sb, []), stage=STAGE,
-                   mask=mask)
     if has_qk:
+        if exact:
+            P.salu("s_mov_b64", S_CMP, "0", writes_scc=False)
+        else:
+            sum_check(P)
         k_addr_next(P)
     if not has_pv:
         P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
@@ -552,16 +609,15 @@ def item_loads(P, first):
     P.salu("s_add_u32", S_X[8], S_X[8], "1")
     rsrc(P, S_RSK1, S_K, S_X[8], nb, nb)
     rsrc(P, S_RSV1, S_V, S_X[8], nb, nb)
-    # the fifth chunk's descriptor: that of tile w & 3
-    P.salu("s_and_b32", S_X[0], S_WAVE, "3")
+    # the fifth chunk's descriptor: that of its tile
     for h in (0, 2):
-        P.scmp("s_cmp_eq_u32", S_X[0], "0")
+        P.scmp("s_cmp_eq_u32", S_FIFTH, "0")
         P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSK0.sub(h, 2), S_RSK1.sub(h, 2), reads_scc=True,
                writes_scc=False)
-        P.scmp("s_cmp_eq_u32", S_X[0], "2")
+        P.scmp("s_cmp_eq_u32", S_FIFTH, "2")
         P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSV0.sub(h, 2), S_RSE.sub(h, 2), reads_scc=True,
                writes_scc=False)
-        P.scmp("s_cmp_eq_u32", S_X[0], "3")
+        P.scmp("s_cmp_eq_u32", S_FIFTH, "3")
         P.salu("s_cselect_b64", S_RSE.sub(h, 2), S_RSV1.sub(h, 2), S_RSE.sub(h, 2), reads_scc=True,
                writes_scc=False)
     rsrc(P, S_RSQ, S_Q, S_BH, nb, nb)
@@ -624,8 +680,25 @@ def item_start(P):
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
 
 
+def _chunk_src_v(P, dst, pos, shift, t):
+    """dst = source byte offset of V tile byte `pos` (a VGPR): pair p =
+    pos / 320 holds rows 2 p and 2 p + 1 in its first 256 bytes; a byte at
+    w = pos % 320 is row 2 p + (w >> 7) & 1, column w & 127 (the padding
+    bytes fetch row 2 p's first 64 bytes again, never read)."""
+    P.salu("s_mov_b32", S_X[11], str(M320), writes_scc=False)
+    P.valu("v_mul_lo_u32", t[11], pos, S_X[11])
+    P.valu("v_lshrrev_b32", t[11], "24", t[11])                # pair
+    P.valu("v_mul_u32_u24", t[12], str(VPAIR), t[11])
+    P.valu("v_sub_u32", t[12], pos, t[12])                     # byte within the pair
+    P.valu("v_bfe_u32", t[13], t[12], "7", "1")
+    P.valu("v_lshl_add_u32", t[11], t[11], "1", t[13])         # row
+    P.valu("v_and_b32", t[12], "127", t[12])                   # column byte
+    P.valu("v_lshlrev_b32", t[11], shift, t[11])
+    P.valu("v_add_u32", dst, t[11], t[12])
+
+
 def _chunk_src(P, dst, pos, shift, t):
-    """dst = source byte offset of tile byte `pos` (a VGPR): row << shift
+    """dst = source byte offset of K tile byte `pos` (a VGPR): row << shift
     plus the column byte, the columns of padding replaced by 0."""
     P.salu("s_mov_b32", S_X[11], str(M144), writes_scc=False)
     P.valu("v_mul_lo_u32", t[11], pos, S_X[11])
@@ -654,39 +727,47 @@ def prologue(P):
     P.salu("s_lshl_b32", S_NB, S_N, "7")
     P.scmp("s_cmp_eq_u32", S_SSTR, "0")
     P.salu("s_cselect_b32", S_SBIT, "0", "4", reads_scc=True, writes_scc=False)
-    # the fifth chunk: chunk 8 of tile w & 3
-    P.salu("s_and_b32", S_XOFF, S_WAVE, "3")
-    P.salu("s_mul_i32", S_XOFF, S_XOFF, str(TILE))
-    P.salu("s_add_u32", S_XOFF, S_XOFF, str(8 * 1024))
+    # the fifth chunk (FIFTH): its tile and LDS offset in a stage
+    for w, (k, c) in enumerate(FIFTH):
+        P.scmp("s_cmp_eq_u32", S_WAVE, str(w))
+        P.salu("s_cselect_b32", S_FIFTH, str(k), S_FIFTH if w else "0", reads_scc=True, writes_scc=False)
+        P.salu("s_cselect_b32", S_XOFF, str(TILE_OFF[k] + 1024 * c), S_XOFF if w else "0", reads_scc=True,
+               writes_scc=False)
     P.salu("s_sub_u32", S_WM1, S_W, "1")
     P.salu("s_mov_b32", S_NINF, "0xff800000", writes_scc=False)
     P.salu("s_mov_b32", S_ONES, "0x3f803f80", writes_scc=False)
     t = V_T
     # this wave's head: its K and V tiles
-    P.salu("s_lshr_b32", S_X[0], S_WAVE, "2")
-    P.salu("s_mul_i32", S_X[0], S_X[0], str(TILE))
+    P.salu("s_lshr_b32", S_X[1], S_WAVE, "2")
+    P.salu("s_mul_i32", S_X[0], S_X[1], str(KTILE))
     # K fragment reads: row col, bytes 16 hl
     P.valu("v_mul_u32_u24", V_KLANE, str(ROW), V_COL)
     P.valu("v_lshlrev_b32", t[0], "4", V_HL)
     P.valu("v_add_u32", V_KLANE, V_KLANE, t[0])
     P.valu("v_add_u32", V_KLANE, S_X[0], V_KLANE)
-    # V^T fragment reads: rows 4 (grp / 2) + sl / 4, bytes 32 (grp % 2) +
-    # 8 (sl % 4), grp = lane / 16, sl = lane % 16
+    # V^T fragment reads: row r = 4 (grp / 2) + sl / 4 at (r / 2) * 320 +
+    # (r % 2) * 128, bytes 32 (grp % 2) + 8 (sl % 4), grp = lane / 16,
+    # sl = lane % 16
+    P.salu("s_mul_i32", S_X[1], S_X[1], str(VTILE))
     P.valu("v_lshrrev_b32", t[0], "4", V_LANE)                 # grp
     P.valu("v_and_b32", t[1], "15", V_LANE)                    # sl
     P.valu("v_lshrrev_b32", t[2], "1", t[0])
     P.valu("v_lshlrev_b32", t[2], "2", t[2])
     P.valu("v_lshrrev_b32", t[3], "2", t[1])
-    P.valu("v_add_u32", t[2], t[2], t[3])
-    P.valu("v_mul_u32_u24", t[2], str(ROW), t[2])
+    P.valu("v_add_u32", t[2], t[2], t[3])                      # r
+    P.valu("v_lshrrev_b32", t[5], "1", t[2])
+    P.valu("v_mul_u32_u24", t[5], str(VPAIR), t[5])
+    P.valu("v_and_b32", t[2], "1", t[2])
+    P.valu("v_lshlrev_b32", t[2], "7", t[2])
+    P.valu("v_add_u32", t[2], t[2], t[5])
     P.valu("v_and_b32", t[3], "1", t[0])
     P.valu("v_lshlrev_b32", t[3], "5", t[3])
     P.valu("v_and_b32", t[4], "3", t[1])
     P.valu("v_lshlrev_b32", t[4], "3", t[4])
     P.valu("v_add_u32", t[2], t[2], t[3])
     P.valu("v_add_u32", t[2], t[2], t[4])
-    P.valu("v_add_u32", t[2], S_X[0], t[2])
-    P.valu("v_add_u32", V_VLANE, str(2 * TILE), t[2])
+    P.valu("v_add_u32", t[2], S_X[1], t[2])
+    P.valu("v_add_u32", V_VLANE, str(2 * KTILE), t[2])
     # Q rows of 128 bytes: row col, bytes 16 hl of each 32-byte group
     P.valu("v_lshlrev_b32", t[0], "7", V_COL)
     P.valu("v_lshlrev_b32", t[1], "4", V_HL)
@@ -701,15 +782,33 @@ def prologue(P):
     P.valu("v_lshlrev_b32", t[1], "4", t[1])
     P.valu("v_mul_u32_u24", V_ORDL, str(OROW), t[0])
     P.valu("v_add_u32", V_ORDL, V_ORDL, t[1])
-    # DMA lane offsets: chunk w and chunk 8 of a tile, rows of a band tile
-    # (pitch 128 bytes) and of a prefix tile (pitch s rows of 128 bytes)
+    # DMA lane offsets: K chunk w, V chunk w and the fifth chunk, rows of a
+    # band tile (pitch 128 bytes) and of a prefix tile (pitch s rows of 128
+    # bytes)
     P.valu("v_lshlrev_b32", t[8], "4", V_LANE)                 # 16 lane
     P.valu("v_add_u32", t[10], S_WAVE1K, t[8])
-    P.valu("v_add_u32", t[9], str(8 * 1024), t[8])
     P.salu("s_add_u32", S_X[1], S_LGS, "7")
-    for pos, db, dp in ((t[10], V_DB, V_DP), (t[9], V_DB8, V_DP8)):
-        _chunk_src(P, db, pos, "7", t)
-        _chunk_src(P, dp, pos, S_X[1], t)
+    _chunk_src(P, V_DBK, t[10], "7", t)
+    _chunk_src(P, V_DPK, t[10], S_X[1], t)
+    _chunk_src_v(P, V_DBV, t[10], "7", t)
+    _chunk_src_v(P, V_DPV, t[10], S_X[1], t)
+    # the fifth chunk: byte XOFF - TILE_OFF[FIFTH] + 16 lane of a K or V tile
+    P.salu("s_mov_b32", S_X[2], "0", writes_scc=False)
+    for k in (1, 2, 3):
+        P.scmp("s_cmp_eq_u32", S_FIFTH, str(k))
+        P.salu("s_cselect_b32", S_X[2], str(TILE_OFF[k]), S_X[2], reads_scc=True, writes_scc=False)
+    P.salu("s_sub_u32", S_X[2], S_XOFF, S_X[2])
+    P.valu("v_add_u32", t[9], S_X[2], t[8])
+    _chunk_src(P, t[14], t[9], "7", t)
+    _chunk_src_v(P, V_DB5, t[9], "7", t)
+    P.scmp("s_cmp_lt_u32", S_FIFTH, "2")
+    P.salu("s_cselect_b64", "vcc", "-1", "0", reads_scc=True, writes_scc=False)
+    P.valu("v_cndmask_b32", V_DB5, V_DB5, t[14], "vcc")
+    _chunk_src(P, t[14], t[9], S_X[1], t)
+    _chunk_src_v(P, V_DP5, t[9], S_X[1], t)
+    P.scmp("s_cmp_lt_u32", S_FIFTH, "2")
+    P.salu("s_cselect_b64", "vcc", "-1", "0", reads_scc=True, writes_scc=False)
+    P.valu("v_cndmask_b32", V_DP5, V_DP5, t[14], "vcc")
     P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
     item_loads(P, first=True)
     P.waitcnt(vm=0)
