@@ -37,12 +37,15 @@
  *     holds at most 2^32 - 1 work-items: a call that would need more returns
  *     SWA_ERR_UNSUPPORTED.  Forward calls have one workgroup per (batch,
  *     query head, query tile) of 256 lanes (512 for diff_attn_fwd in bf16),
- *     except two bf16 shapes that run a persistent grid of at most one
+ *     except three bf16 shapes that run a persistent grid of at most one
  *     512-lane workgroup per compute unit: swa_attn_fwd with d = dv = 128,
  *     no stride, a window that may be dilated or have global tokens (not
- *     both) and a multiple of 4 query heads per key/value head, and
- *     diff_attn_fwd with d = 64, dv = 128 and a window only.  The decode
- *     calls' launches are sized by their own work split.
+ *     both) and a multiple of 4 query heads per key/value head;
+ *     swa_attn_fwd with d = dv = 64, one query head per key/value head,
+ *     B * Hq even, no dilation or global tokens and a stride of 0 or a
+ *     power of two from 64 to 2^18; and diff_attn_fwd with d = 64,
+ *     dv = 128 and a window only.  The decode calls' launches are sized by
+ *     their own work split.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - No global mutable state, except the static scratch array of
  *     swa_attn_decode_noalloc: calls on different streams may overlap as
