@@ -13,8 +13,8 @@ no stride at all, pairs of heads that straddle two batch entries, chains of
 several items per workgroup (more items than compute units, also a count
 that is not a multiple of 8), peaky scores that move the running maximum
 late, a score jump past the first tiles that makes a step redo its tile, the
-log-sum-exp, and key/value rows past N that hold NaN (they must read as
-zeros).
+log-sum-exp, key/value rows past N that hold NaN (they must read as zeros),
+and the largest N with the largest and the smallest stride the kernel takes.
 """
 import numpy as np
 import pytest
@@ -170,3 +170,29 @@ def test_str_asm_deterministic(swa):
     a = run(swa, cfg, q, k, v)
     b = run(swa, cfg, q, k, v)
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def long_inputs(swa):
+    """One seeded input at N = 2^22 (the largest N the boundary accepts),
+    shared by the longest-sequence cases and released with the module."""
+    cfg = config(1, 2, swa.SWA_MAX_N, 200, 0, seed=97)
+    return synth.prefill_inputs(cfg)
+
+
+@pytest.mark.parametrize("W,s", [(200, 2 ** 18), (128, 64)])
+def test_str_asm_longest_sequence(swa, long_inputs, W, s):
+    """N at its maximum (2^22), checked on sampled rows, ends included: with
+    s = 2^18 the gathered rows of a prefix tile lie 2^25 bytes apart and
+    reach 2^31 bytes past the head's first row (past N: zeros); with s = 64
+    the items at the end gather 65,535 stride keys in 1,024 tiles."""
+    N = swa.SWA_MAX_N
+    print(f"[case] str asm at N={N} W={W} s={s} (sampled rows)", flush=True)
+    q, k, v = long_inputs
+    cfg = config(1, 2, N, W, s)
+    got = run(swa, cfg, q, k, v).reshape(-1, 64)
+    must = [h * N + i for h in range(2) for i in (0, 127, 128, 255, N // 2, N - 129, N - 128, N - 1)]
+    rows = synth.sample_rows(2 * N, 150, seed=98, must=must)
+    want = oracle.attn_rows(q, k, v, W, s, cfg["scale"], rows)
+    assert float(np.max(np.abs(got[rows] - want))) <= TOL
+    assert np.all(np.isfinite(got[-4096:]))
