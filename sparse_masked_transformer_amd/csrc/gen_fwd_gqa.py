@@ -522,6 +522,7 @@ S_FULL = [s(77), s(60)]              # 1 if every cell of the tile attends this 
 S_WM1, S_NINF, S_ONES = s(63), s(64), s(65)
 S_SBW = s(62)                        # DMA stage base + 1024 * wave
 S_XOFF = s(72)                       # LDS offset of the wave's fifth chunk within a stage
+S_HALF1 = s(73)                      # 1 if key half 1 of the item's last tile lies past the wave's rows
 S_RSE = s(96, 4)                     # its descriptor: V on waves 0-3, K on waves 4-7
 S_NB = s(33)                         # N * 256: bytes per head, first offset past the rows
 S_FLAG = s(68, 2)
@@ -712,6 +713,29 @@ def qk_mfma(P, n, sbuf):
     kb, ks = n % 2, n // 2
     dst = v(sbuf + 16 * kb, 16)
     P.mfma(dst, A_KR.sub(4 * (n % RING), 4), A_Q.sub(4 * ks, 4), None if ks == 0 else dst)
+
+
+def qk_half(P, sbuf, kb):
+    """S^T[kb] = K Q^T for key half kb alone (the 8 K fragments n with
+    n % 2 == kb, ring slots by position)."""
+    ns = [n for n in range(16) if n % 2 == kb]
+
+    def slot(i):
+        return A_KR.sub(4 * (i % RING), 4)
+
+    def rd(i):
+        P.ds_read("ds_read_b128", slot(i), V_KADDR, kb * 32 * KROW + (ns[i] // 2) * 32)
+
+    def mm(i):
+        ks = ns[i] // 2
+        dst = v(sbuf + 16 * kb, 16)
+        P.mfma(dst, slot(i), A_Q.sub(4 * ks, 4), None if ks == 0 else dst)
+    for i in range(AHEAD):
+        rd(i)
+    for i in range(len(ns)):
+        mm(i)
+        if i + AHEAD < len(ns):
+            rd(i + AHEAD)
 
 
 def pv_read(P, n):
@@ -1085,6 +1109,9 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32)])
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
+        # (before the next item's loads replace the row)
+        P.scmp("s_cmp_ge_u32", S_K0P[phase], S_R0W)
+        P.salu("s_cselect_b32", S_HALF1, "1", "0", reads_scc=True, writes_scc=False)
         item_loads(P, first=False)
     valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
             + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
@@ -1169,7 +1196,16 @@ def epilogue(P, phase):
     # this item's last reads of the stage the output is staged in)
     P.barrier()
     settle_previous(P)
+    # key half 1 of the last tile past the wave's last row: its p are 0, so
+    # its P V products are skipped
+    whole, done = P.new_label("pvlast"), P.new_label("pvdone")
+    P.scmp("s_cmp_eq_u32", S_HALF1, "0")
+    P.branch("s_cbranch_scc1", whole)
+    interleave(P, [("v", n) for n in range(8)], None, [], v_ready=AHEAD)
+    P.branch("s_branch", done)
+    P.label(whole)
     interleave(P, mfma_order(False, True), None, [], v_ready=AHEAD)
+    P.label(done)
     dump(P, f"O{phase}", [A_O])
     t = V_T
     l, l2, inv = t[0], t[1], t[2]
@@ -1440,7 +1476,22 @@ def item_start(P):
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
     dump_lds(P, "lds0", STAGE)
     dump(P, "q", [A_Q])
-    interleave(P, mfma_order(True, False), S_BUF[0], [])
+    if GLB["on"]:
+        interleave(P, mfma_order(True, False), S_BUF[0], [])
+    else:
+        # key half 0 of tile 0 before the window of the wave's first row
+        # (every key + W - 1 < the row): its scores are masked to -inf
+        # whatever they hold, so only key half 1 is computed
+        whole, done = P.new_label("qk0"), P.new_label("qk0done")
+        P.salu("s_add_u32", S_X[12], S_K0P[0], S_W)
+        P.salu("s_add_u32", S_X[12], S_X[12], "31")
+        P.scmp("s_cmp_gt_u32", S_X[12], S_R0W)
+        P.branch("s_cbranch_scc1", whole)
+        qk_half(P, S_BUF[0], 1)
+        P.branch("s_branch", done)
+        P.label(whole)
+        interleave(P, mfma_order(True, False), S_BUF[0], [])
+        P.label(done)
     P.salu("s_add_u32", S_X[12], S_BASE, "1")                  # QK(1) reads the next stage
     P.salu("s_and_b32", S_X[12], S_X[12], "3")
     P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
