@@ -3,10 +3,11 @@
 The hand-picked parity cases pin the edges one at a time; this sweep draws
 combinations of them (sequence length, window, stride, dilation, global
 tokens, head sizes, grouped heads, batch, dtype, decode lengths and sink
-slots) from a fixed seed, so every run checks the same configurations; two
+slots) from a fixed seed, so every run checks the same configurations; three
 more sweeps draw only shapes the generated kernels serve (grouped-query
 prefill with a plain, dilated or global-token window; differential
-attention at d = 64, dv = 128).
+attention at d = 64, dv = 128; multi-head prefill at d = 64 with a window
+and a power-of-two stride or none).
 Tolerances are the parity bar: max-abs 2e-2 for bf16 inputs, 1e-5 for fp32.
 SWA_RANDOM_SCALE=k multiplies the number of drawn configurations by k (the
 default run draws 48; k = 150 draws about 7,000, about a minute on one GPU).
@@ -178,6 +179,21 @@ def asm_diff_configs(n, seed):
     return out
 
 
+def asm_str_configs(n, seed):
+    """Shapes of the generated multi-head kernel (bf16, d = dv = 64, one query
+    head per key/value head, B * H even): a window with no stride or a
+    power-of-two stride from 64 to 2^18, with the log-sum-exp."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 3001))
+        B, H = [(1, 2), (2, 1), (1, 4), (2, 2), (3, 2)][int(rng.integers(0, 5))]
+        s = 0 if rng.random() < 0.25 else 1 << int(rng.integers(6, 19))
+        out.append(dict(dtype="bf16", B=B, Hq=H, Hkv=H, N=N, d=64, dv=64, window=int(rng.integers(1, N + 41)),
+                        stride=s, dilation=1, n_global=0, scale=0.125, seed=7000 + i))
+    return out
+
+
 def label(c):
     keys = ("dtype", "B", "Hq", "Hkv", "N", "d", "dv", "window", "stride", "dilation", "n_global",
             "n_sink", "two")
@@ -225,6 +241,19 @@ def test_random_asm_diff(swa, cfg):
     out = swa.diff_attn_fwd(*(dev(x, "bf16") for x in ins), cfg["window"], 0, cfg["scale"], cfg["lam"], mask)
     want = oracle.diff_full(*ins, cfg["window"], 0, cfg["scale"], cfg["lam"])
     assert max_err(host(out), want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg", asm_str_configs(8 * SCALE, 19), ids=label)
+def test_random_asm_str(swa, cfg):
+    banner(cfg)
+    q, k, v = synth.prefill_inputs(cfg)
+    mask = swa.swa_block_mask_build(cfg["N"], cfg["window"], cfg["stride"], d=64)
+    lse = torch.empty((cfg["B"], cfg["Hq"], cfg["N"]), dtype=torch.float32, device="cuda")
+    out = swa.swa_attn_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), cfg["window"], cfg["stride"],
+                           cfg["scale"], mask, lse=lse)
+    want, want_lse = oracle.attn_full(q, k, v, cfg["window"], cfg["stride"], cfg["scale"], with_lse=True)
+    assert max_err(host(out), want) <= TOL["bf16"]
+    assert max_err(host(lse), want_lse) <= 4e-3
 
 
 @pytest.mark.parametrize("cfg", diff_configs(10 * SCALE, 12), ids=label)
