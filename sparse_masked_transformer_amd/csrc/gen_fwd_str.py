@@ -12,8 +12,10 @@ stride s is 0 (a plain window) or a power of two from 64 to 2^18, so that a
 Work decomposition
   Item = 128 query rows of two consecutive (batch, head) pairs bh0, bh0 + 1
   (B * H even; the key/value head of a query head is itself).  Wave w takes
-  head bh0 + (w >> 2) and rows 32 (w & 3) .. +31, so waves w and w + 4 share
-  a SIMD, the rows and the key tiles they walk.  LDS stages (four) hold per
+  head bh0 + (w >> 2) and rows 32 g .. +31 with g = w & 3 for the first
+  head and 3 - (w & 3) for the second, so the two waves of a SIMD (w and
+  w + 4) hold rows from both ends of the block and every SIMD's pair does
+  about the same work in each step (masked tiles, dead tiles).  LDS stages (four) hold per
   64-key tile the K and V tiles of both heads (K: 64 rows of 128 bytes,
   padded to 144; V: 32 pairs of rows at a pitch of 320 bytes, so that any
   four consecutive rows fall on disjoint LDS banks for the transposed
@@ -458,13 +460,14 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     if has_pv:
         redo_previous(P, phase)
         settle_previous(P, o=A_O)
+    if not has_qk:
+        last_step(P, phase, has_pv)
+        return
     mask(P, phase)
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
-    if not has_qk:
-        item_loads(P, first=False)
     valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
             + pack(sb_cur, 0) + v_prefetch_ops() + pack(sb_cur, 1))
-    extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
+    extra = dma_ops() + setup_ops(1 - phase)
     interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
     if has_qk:
         if exact:
@@ -472,6 +475,49 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
         else:
             sum_check(P)
         k_addr_next(P)
+    if not has_pv:
+        P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+
+
+def last_step(P, phase, has_pv):
+    """The softmax of an item's last tile (with its row maximum), the P V
+    product of the one before (has_pv), and the loads of the next item.
+    Key halves of the tile that lie past every row of the wave (the tile is
+    the diagonal's or the one after it) take no softmax: every key past
+    the rows (2: the whole tile) gives p = 0, and the epilogue skips their
+    P V fragments too; only key half 1 past the rows (1) keeps half 0."""
+    sb_cur = S_BUF[phase]
+    order = mfma_order(False, has_pv)
+    dead, half, joined = P.new_label("lastdead"), P.new_label("lasthalf"), P.new_label("lastdone")
+    P.salu("s_add_u32", S_X[0], S_R0W, "32")
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[0])
+    P.branch("s_cbranch_scc1", dead)
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_R0W)
+    P.branch("s_cbranch_scc1", half)
+    for kind in ("full", "half", "dead"):
+        if kind == "half":
+            P.label(half)
+        elif kind == "dead":
+            P.label(dead)
+        if kind != "dead":
+            mask(P, phase)
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+        if kind == "dead":
+            for k in range(2):
+                P.valu("v_mov_b32", V_LT[k], "0")
+        item_loads(P, first=False)
+        if kind == "full":
+            valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack(sb_cur, 0)
+                    + v_prefetch_ops() + pack(sb_cur, 1))
+        elif kind == "half":
+            valu = max_ops(sb_cur) + exp_ops(sb_cur, 0) + pack(sb_cur, 0) + v_prefetch_ops()
+        else:
+            valu = []
+        interleave(P, order, None, valu, [], v_ready=AHEAD)
+        if kind != "dead":
+            P.branch("s_branch", joined)
+    P.label(joined)
     if not has_pv:
         P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
@@ -485,7 +531,22 @@ def epilogue(P, phase):
     item."""
     P.barrier()
     settle_previous(P, o=A_O)
+    # the key halves of the last tile past the wave's rows (as in last_step;
+    # the next item's loads have replaced S_R0W: lane 0's V_IBASE is the
+    # wave's first row)
+    dead, half, joined = P.new_label("pvdead"), P.new_label("pvhalf"), P.new_label("pvdone")
+    P.add(I(f"  v_readfirstlane_b32 {S_X[13]}, {V_IBASE}", "rfl", V_IBASE.regs(), S_X[13].regs()))
+    P.salu("s_add_u32", S_X[12], S_X[13], "32")
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[12])
+    P.branch("s_cbranch_scc1", dead)
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[13])
+    P.branch("s_cbranch_scc1", half)
     interleave(P, mfma_order(False, True), None, [], v_ready=AHEAD)
+    P.branch("s_branch", joined)
+    P.label(half)
+    interleave(P, [("v", n) for n in range(4)], None, [], v_ready=AHEAD)
+    P.label(dead)
+    P.label(joined)
     t = V_T
     l, l2, inv = t[0], t[1], t[2]
     P.valu("v_add_f32", l, V_L[0], V_L[1])
@@ -568,7 +629,12 @@ def item_loads(P, first):
     P.salu("s_lshr_b32", S_X[0], S_WAVE, "2")
     P.salu("s_add_u32", S_BH, S_X[8], S_X[0])                  # this wave's head
     P.salu("s_lshl_b32", S_X[5], rb, "7")                      # r0
+    # row group (w & 3) for the first head, 3 - (w & 3) for the second: the
+    # two waves of a SIMD take rows from both ends of the block
+    P.salu("s_lshr_b32", S_X[1], S_WAVE, "2")
+    P.salu("s_mul_i32", S_X[1], S_X[1], "3")
     P.salu("s_and_b32", S_X[0], S_WAVE, "3")
+    P.salu("s_xor_b32", S_X[0], S_X[0], S_X[1])
     P.salu("s_lshl_b32", S_X[0], S_X[0], "5")
     P.salu("s_add_u32", S_R0W, S_X[5], S_X[0])                 # this wave's first row
     # band of rows r0 .. r0+127: key tiles t_lo .. t_hi
