@@ -1109,14 +1109,29 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     dump(P, f"masked{phase}{int(has_qk)}{int(has_pv)}", [v(sb_cur, 32)])
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
-        # (before the next item's loads replace the row)
+        # the last tile: where its key half 1 lies past the wave's rows (before
+        # the next item's loads replace the row) that half takes no softmax
+        # (its p are 0; the epilogue skips its P V fragments)
         P.scmp("s_cmp_ge_u32", S_K0P[phase], S_R0W)
         P.salu("s_cselect_b32", S_HALF1, "1", "0", reads_scc=True, writes_scc=False)
+        half, joined = P.new_label("lasthalf"), P.new_label("lastdone")
+        P.scmp("s_cmp_eq_u32", S_HALF1, "1")
+        P.branch("s_cbranch_scc1", half)
         item_loads(P, first=False)
-    valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
-            + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
-    extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
-    interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
+        valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
+                + v_prefetch_ops() + pack_ops(sb_cur, 1))
+        interleave(P, mfma_order(False, has_pv), sb_next, valu, [], v_ready=AHEAD)
+        P.branch("s_branch", joined)
+        P.label(half)
+        item_loads(P, first=False)
+        valu = max_ops(sb_cur) + exp_ops(sb_cur, 0) + pack_ops(sb_cur, 0) + v_prefetch_ops()
+        interleave(P, mfma_order(False, has_pv), sb_next, valu, [], v_ready=AHEAD)
+        P.label(joined)
+    else:
+        valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
+                + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
+        extra = dma_ops() + setup_ops(1 - phase)
+        interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
     if not exact:
         max_redo(P, phase)
     if has_qk:
