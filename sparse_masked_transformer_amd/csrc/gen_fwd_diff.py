@@ -19,8 +19,10 @@ assignments).
 
 Work decomposition
   Item = 128 query rows of one query head.  Its 8 waves: wave w computes map
-  1 + (w >> 2) (query and key projection 1 or 2) for rows 32 (w & 3) .. +31;
-  waves w and w + 4 share a SIMD and the same rows.  LDS stages (four) hold,
+  1 + (w >> 2) (query and key projection 1 or 2) for rows 32 g .. +31, g =
+  w & 3 for the first map and 3 - (w & 3) for the second, so waves w and
+  w + 4 share a SIMD with rows from both ends of the item; the waves of the
+  two maps on the same rows exchange through LDS.  LDS stages (four) hold,
   per 64-key tile, the K1 and K2 tiles (64 keys x 64 channels, rows padded
   to 144 bytes) and the V tile (64 keys x 128 values, rows padded to 320
   bytes): every key tile is read from HBM once for both maps.  Per tile a
@@ -303,11 +305,12 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     P.label(skip)
     P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
-        item_loads(P, first=False)
-    valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
-            + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
-    extra = dma_ops() + setup_ops(1 - phase) if has_qk else []
-    interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
+        last_step(P, phase, has_pv)
+    else:
+        valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
+                + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
+        extra = dma_ops() + setup_ops(1 - phase)
+        interleave(P, mfma_order(has_qk, has_pv), sb_next, valu, extra, v_ready=AHEAD)
     if not exact:
         g.max_redo(P, phase, qk=lambda P, sb: interleave(P, mfma_order(True, False), sb, []), stage=STAGE)
     if has_qk:
@@ -317,16 +320,67 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
 
 
+def last_step(P, phase, has_pv):
+    """The softmax of an item's last tile (with its row maximum), the P V
+    product of the one before (has_pv), and the loads of the next item.
+    Key halves of the tile that lie past every row of the wave take no
+    softmax (their p are 0; the epilogue skips their P V fragments): the
+    whole tile for the row groups it lies past, key half 1 where only that
+    half does."""
+    sb_cur = S_BUF[phase]
+    order = mfma_order(False, has_pv)
+    dead, half, joined = P.new_label("lastdead"), P.new_label("lasthalf"), P.new_label("lastdone")
+    P.salu("s_add_u32", S_X[0], S_R0W, "32")
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[0])
+    P.branch("s_cbranch_scc1", dead)
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_R0W)
+    P.branch("s_cbranch_scc1", half)
+    for kind in ("full", "half", "dead"):
+        if kind == "half":
+            P.label(half)
+        elif kind == "dead":
+            P.label(dead)
+            for k in range(2):
+                P.valu("v_mov_b32", V_LT[k], "0")
+        item_loads(P, first=False)
+        if kind == "full":
+            valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
+                    + v_prefetch_ops() + pack_ops(sb_cur, 1))
+        elif kind == "half":
+            valu = max_ops(sb_cur) + exp_ops(sb_cur, 0) + pack_ops(sb_cur, 0) + v_prefetch_ops()
+        else:
+            valu = []
+        interleave(P, order, None, valu, [], v_ready=AHEAD)
+        if kind != "dead":
+            P.branch("s_branch", joined)
+    P.label(joined)
+
+
 def epilogue(P, phase):
     """O += V(T-1)^T P(T-1); then out = O1 / l1 - lambda O2 / l2 -> bf16.
     The second map's waves hand lambda O2 / l2 to their partner waves (same
-    rows, same SIMD) through LDS, half the values at a time, in the stage of
+    rows) through LDS, half the values at a time, in the stage of
     tile T-2 (free after the barrier; the stage of tile T-1 is still being
     read and the next two hold the next item's first tiles); the first
     map's waves stage the bf16 rows there for whole-row stores."""
     P.barrier()
     settle_previous(P)
+    # the key halves of the last tile past the wave's rows (as in last_step;
+    # the next item's loads have replaced S_R0W: lane 0's V_IBASE is the
+    # wave's first row)
+    dead, half, joined = P.new_label("pvdead"), P.new_label("pvhalf"), P.new_label("pvdone")
+    P.add(I(f"  v_readfirstlane_b32 {S_X[13]}, {V_IBASE}", "rfl", V_IBASE.regs(), S_X[13].regs()))
+    P.salu("s_add_u32", S_X[12], S_X[13], "32")
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[12])
+    P.branch("s_cbranch_scc1", dead)
+    P.scmp("s_cmp_ge_u32", S_K0P[phase], S_X[13])
+    P.branch("s_cbranch_scc1", half)
     interleave(P, mfma_order(False, True), None, [], v_ready=AHEAD)
+    P.branch("s_branch", joined)
+    P.label(half)
+    interleave(P, [("v", n) for n in range(8)], None, [], v_ready=AHEAD)
+    P.label(dead)
+    P.label(joined)
     t = V_T
     l, l2, inv = t[0], t[1], t[2]
     P.valu("v_add_f32", l, V_L[0], V_L[1])
@@ -641,6 +695,12 @@ def prologue(P):
     P.scmp("s_cmp_lt_u32", S_WAVE, "4")
     P.salu("s_cselect_b64", "vcc", "-1", "0", reads_scc=True, writes_scc=False)
     P.valu("v_cndmask_b32", V_DX, t[14], V_DX, "vcc")
+    # row groups: w & 3 for the first map's waves, 3 - (w & 3) for the
+    # second's, so the two waves of a SIMD hold rows from both ends of an
+    # item and meet about the same masked and dead tiles in each step (the
+    # fifth DMA chunk above is V chunk 16 + (w & 3) on the first map's waves)
+    P.salu("s_mul_i32", S_X[0], S_MAP, "3")
+    P.salu("s_xor_b32", S_RGRP, S_RGRP, S_X[0])
     P.salu("s_mov_b32", S_J, "-1", writes_scc=False)
     item_loads(P, first=True)
     P.waitcnt(vm=0)
