@@ -148,6 +148,42 @@ def qk_mfma(P, n, sbuf):
     P.mfma(dst, A_KR.sub(4 * (n % RING), 4), A_Q.sub(4 * ks, 4), None if ks == 0 else dst)
 
 
+def qk_half(P, sbuf, kb):
+    """S^T[kb] = K Q^T for key half kb alone (the 4 K fragments n with
+    n % 2 == kb, ring slots by position)."""
+    ns = [n for n in range(8) if n % 2 == kb]
+
+    def slot(i):
+        return A_KR.sub(4 * (i % RING), 4)
+
+    def rd(i):
+        P.ds_read("ds_read_b128", slot(i), V_KADDR, kb * 32 * KROW + (ns[i] // 2) * 32)
+
+    def mm(i):
+        ks = ns[i] // 2
+        dst = v(sbuf + 16 * kb, 16)
+        P.mfma(dst, slot(i), A_Q.sub(4 * ks, 4), None if ks == 0 else dst)
+    for i in range(min(AHEAD, len(ns))):
+        rd(i)
+    for i in range(len(ns)):
+        mm(i)
+        if i + AHEAD < len(ns):
+            rd(i + AHEAD)
+
+
+def first_tile_kind(P, dead, half):
+    """Branch to `dead` if the item's first tile lies before the window of
+    the wave's first row (every key + W - 1 < the row), to `half` if its key
+    half 0 does; fall through otherwise."""
+    P.salu("s_add_u32", S_X[12], S_K0P[0], S_W)
+    P.salu("s_add_u32", S_X[13], S_X[12], "63")
+    P.scmp("s_cmp_le_u32", S_X[13], S_R0W)
+    P.branch("s_cbranch_scc1", dead)
+    P.salu("s_add_u32", S_X[13], S_X[12], "31")
+    P.scmp("s_cmp_le_u32", S_X[13], S_R0W)
+    P.branch("s_cbranch_scc1", half)
+
+
 def interleave(P, order, sbuf_next, valu_ops, extra_ops=(), v_ready=0):
     """The MFMAs of `order` (("k", n): QK fragment n into sbuf_next; ("v",
     n): PV fragment n) with their fragment reads AHEAD ahead, the VALU ops
@@ -298,6 +334,9 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     P.barrier()
     if has_pv:
         settle_previous(P)
+    if first and has_qk:
+        first_step(P)
+        return
     P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
     skip = P.new_label("full")
     P.branch("s_cbranch_scc1", skip)
@@ -318,6 +357,47 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     if not has_pv:
         P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+
+
+def first_step(P):
+    """Step 0 of an item (S(1) = K(1) Q^T, the DMA of tile 2, the softmax of
+    tile 0).  Where tile 0 lies before the window of every row of the wave,
+    it takes no softmax (p = 0: the P buffer and the row sums are cleared
+    for the P V product of step 1); where only its key half 0 does, that
+    half takes none."""
+    sb = S_BUF[0]
+    dead, half, joined = P.new_label("firstdead"), P.new_label("firsthalf"), P.new_label("firstdone")
+    first_tile_kind(P, dead, half)
+    zero_lt = [lambda P, k=k: P.valu("v_mov_b32", V_LT[k], "0") for k in range(2)]
+
+    def zero_p(lo, hi):
+        return [lambda P, i=i: P.valu("v_mov_b32", v(P_BUF + i), "0") for i in range(lo, hi)]
+    for kind in ("full", "half", "dead"):
+        if kind == "half":
+            P.label(half)
+        elif kind == "dead":
+            P.label(dead)
+        if kind != "dead":
+            P.scmp("s_cmp_eq_u32", S_FULL[0], "1")
+            skip = P.new_label("full")
+            P.branch("s_cbranch_scc1", skip)
+            mask_block(P, sb, S_K0P[0])
+            P.label(skip)
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+        if kind == "full":
+            valu = (max_ops(sb) + merge_rr([exp_ops(sb, 0), exp_ops(sb, 1)]) + pack_ops(sb, 0)
+                    + v_prefetch_ops() + pack_ops(sb, 1))
+        elif kind == "half":
+            valu = zero_lt + max_ops(sb) + exp_ops(sb, 1) + pack_ops(sb, 1) + zero_p(0, 8) + v_prefetch_ops()
+        else:
+            valu = zero_lt + zero_p(0, 16) + v_prefetch_ops()
+        interleave(P, mfma_order(True, False), S_BUF[1], valu, dma_ops() + setup_ops(1), v_ready=AHEAD)
+        if kind != "dead":
+            P.branch("s_branch", joined)
+    P.label(joined)
+    k_addr_next(P)
+    P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
+    P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
 
 
 def last_step(P, phase, has_pv):
@@ -586,7 +666,15 @@ def item_start(P):
     P.salu("s_mov_b32", S_J, S_BASE, writes_scc=False)
     P.salu("s_mul_i32", S_X[12], S_BASE, str(STAGE))
     P.valu("v_add_u32", V_KADDR, S_X[12], V_KLANE)
+    # S(0), or of its key half 1 alone, or none (first_step)
+    dead, half, joined = P.new_label("qk0dead"), P.new_label("qk0half"), P.new_label("qk0done")
+    first_tile_kind(P, dead, half)
     interleave(P, mfma_order(True, False), S_BUF[0], [])
+    P.branch("s_branch", joined)
+    P.label(half)
+    qk_half(P, S_BUF[0], 1)
+    P.label(dead)
+    P.label(joined)
     P.salu("s_add_u32", S_X[12], S_BASE, "1")
     P.salu("s_and_b32", S_X[12], S_X[12], "3")
     P.salu("s_mul_i32", S_X[12], S_X[12], str(STAGE))
