@@ -1100,6 +1100,9 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     P.barrier()
     if has_pv:
         settle_previous(P)
+    if first and has_qk and not GLB["on"]:
+        first_step(P)
+        return
     # per-cell mask of tile j unless every cell of this wave's 32 rows attends
     P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
     skip = P.new_label("full")
@@ -1144,6 +1147,44 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
         # the start of the next step
         P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
         P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+
+
+def first_step(P):
+    """Step 0 of an item (S(1) = K(1) Q^T, the DMA of tile 2, the softmax of
+    tile 0, with its row maximum).  Where key half 0 of tile 0 lies before
+    the window of the wave's first row (item_start then computed key half 1
+    alone), that half takes no softmax: its P values and row sums are
+    cleared for the P V product of step 1."""
+    sb = S_BUF[0]
+    half, joined = P.new_label("firsthalf"), P.new_label("firstdone")
+    P.salu("s_add_u32", S_X[12], S_K0P[0], S_W)
+    P.salu("s_add_u32", S_X[12], S_X[12], "31")
+    P.scmp("s_cmp_le_u32", S_X[12], S_R0W)
+    P.branch("s_cbranch_scc1", half)
+    for kind in ("full", "half"):
+        if kind == "half":
+            P.label(half)
+        P.scmp("s_cmp_eq_u32", S_FULL[0], "1")
+        skip = P.new_label("full")
+        P.branch("s_cbranch_scc1", skip)
+        mask_block(P, sb, S_K0P[0])
+        P.label(skip)
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
+        if kind == "full":
+            valu = (max_ops(sb) + merge_rr([exp_ops(sb, 0), exp_ops(sb, 1)]) + pack_ops(sb, 0)
+                    + v_prefetch_ops() + pack_ops(sb, 1))
+        else:
+            valu = ([lambda P, k=k: P.valu("v_mov_b32", V_LT[k], "0") for k in range(2)]
+                    + max_ops(sb) + exp_ops(sb, 1) + pack_ops(sb, 1)
+                    + [lambda P, i=i: P.valu("v_mov_b32", v(P_BUF + i), "0") for i in range(8)]
+                    + v_prefetch_ops())
+        interleave(P, mfma_order(True, False), S_BUF[1], valu, dma_ops() + setup_ops(1), v_ready=AHEAD)
+        if kind == "full":
+            P.branch("s_branch", joined)
+    P.label(joined)
+    k_addr_next(P)
+    P.valu("v_add_f32", V_MTHR, str(SLACK), V_M)
+    P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
 
 
 def max_redo(P, phase, qk=None, stage=None, mask=None):
