@@ -337,15 +337,16 @@ def iteration(P, phase, has_qk, has_pv, first, exact=True):
     if first and has_qk:
         first_step(P)
         return
-    P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
-    skip = P.new_label("full")
-    P.branch("s_cbranch_scc1", skip)
-    mask_block(P, sb_cur, S_K0P[phase])
-    P.label(skip)
-    P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
     if not has_qk:
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
         last_step(P, phase, has_pv)
     else:
+        P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
+        skip = P.new_label("full")
+        P.branch("s_cbranch_scc1", skip)
+        mask_block(P, sb_cur, S_K0P[phase])
+        P.label(skip)
+        P.salu("s_mov_b64", S_FLAG, "0", writes_scc=False)
         valu = ((max_ops(sb_cur) if exact else []) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)])
                 + pack_ops(sb_cur, 0) + v_prefetch_ops() + pack_ops(sb_cur, 1))
         extra = dma_ops() + setup_ops(1 - phase)
@@ -422,6 +423,12 @@ def last_step(P, phase, has_pv):
             P.label(dead)
             for k in range(2):
                 P.valu("v_mov_b32", V_LT[k], "0")
+        if kind != "dead":
+            P.scmp("s_cmp_eq_u32", S_FULL[phase], "1")
+            skip = P.new_label("full")
+            P.branch("s_cbranch_scc1", skip)
+            mask_block(P, sb_cur, S_K0P[phase])
+            P.label(skip)
         item_loads(P, first=False)
         if kind == "full":
             valu = (max_ops(sb_cur) + merge_rr([exp_ops(sb_cur, 0), exp_ops(sb_cur, 1)]) + pack_ops(sb_cur, 0)
